@@ -1,0 +1,209 @@
+/*
+ * psd.h - page-selected sparse paged decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step over a paged KV cache in the vLLM block layout (EntmaxKV README,
+ * introduction: [2, num_blocks, page_size, H_kv, D] plus a block table; pages of 16
+ * tokens), in three calls:
+ *
+ *   1. psd_page_meta_update  - refresh the per-page key min/max of the pages an append
+ *                              touched (EntmaxKV README, package tree: per-page k_min /
+ *                              k_max refresh).
+ *   2. psd_select_pages      - score every page from those statistics with a
+ *                              Quest-style upper bound, take the max over each GQA
+ *                              group, and keep the top-b pages per (sequence, KV head)
+ *                              with the sink and the most recent page always kept
+ *                              (EntmaxKV README, "Two selection strategies", top-k;
+ *                              LOCKS README, introduction, "Configuration", "How it
+ *                              works").
+ *   3. psd_sparse_decode     - exact softmax attention over only the kept pages
+ *                              (EntmaxKV README, introduction; LOCKS README, "How it
+ *                              works", sparse decode).
+ *
+ * plus psd_dense_decode, the same attention over every page (the dense baseline the
+ * pages compare against: AMASS page, "Headline results"; LOCKS README, "Efficiency").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All data pointers are DEVICE pointers owned by the caller. The library allocates
+ *   nothing, keeps no state between calls and is reentrant. Workspaces are caller-owned
+ *   device buffers of at least the size the matching *_workspace_bytes query returns;
+ *   their contents need no initialisation and are scratch after the call.
+ * - Every call only enqueues work on `stream` (HIP stream, may be 0 / the null stream)
+ *   and returns without synchronising. A workspace or output may be reused only in
+ *   stream order.
+ * - Arguments are checked on the host before anything is launched; a failed check
+ *   returns a negative psd_status and launches nothing. Device-side preconditions are
+ *   documented per call and are not checked: seq_lens[s] in [1, 16 * max_pages_per_seq],
+ *   block ids in [0, num_blocks).
+ * - Element types: q, K, V and the page statistics share `dtype` (fp32 or bf16). The
+ *   attention output is fp32.
+ * - GQA grouping: query head h belongs to KV head h / (num_q_heads / num_kv_heads).
+ * - A sequence of length L has n = ceil(L / 16) logical pages; page p holds tokens
+ *   [16 p, min(16 p + 16, L)); slots past L in the last page are never read as data.
+ */
+#ifndef PSD_H
+#define PSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum psd_status {
+  PSD_OK = 0,
+  PSD_ERR_INVALID_ARG = -1, /* null pointer, inconsistent shape, stride or alignment */
+  PSD_ERR_UNSUPPORTED = -2, /* head dims / group size outside what the kernels build */
+  PSD_ERR_WORKSPACE = -3,   /* workspace null or smaller than the query returned */
+  PSD_ERR_CAPACITY = -4,    /* b_max (pages kept per unit) beyond the selection limit */
+  PSD_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch */
+} psd_status;
+
+typedef enum psd_dtype { PSD_F32 = 0, PSD_BF16 = 1 } psd_dtype;
+
+/*
+ * Shape of one layer's paged cache and decode batch.
+ *
+ * Supported: page_size == 16; (head_dim, head_dim_v) in {(64, 64), (128, 128),
+ * (576, 512)}; group G = num_q_heads / num_kv_heads either <= 16 or a multiple of 16
+ * up to 128. A latent (MLA-style) cache passes the same pointer as K and V with
+ * head_dim_v < head_dim: V is the first head_dim_v dims of each cached row.
+ *
+ * Strides are in elements; the last (dim) axis is contiguous. Every pointer and every
+ * stride times the element size must be a multiple of 16 bytes.
+ */
+typedef struct psd_shape {
+  int32_t batch;             /* B: sequences in the decode batch */
+  int32_t num_q_heads;       /* H_q: a multiple of num_kv_heads */
+  int32_t num_kv_heads;      /* H_kv */
+  int32_t head_dim;          /* D of q and K */
+  int32_t head_dim_v;        /* D_v of V and of the output, <= head_dim */
+  int32_t page_size;         /* tokens per page; must be 16 */
+  int32_t num_blocks;        /* physical blocks in the cache (and in the statistics) */
+  int32_t max_pages_per_seq; /* row length of the block table */
+  int32_t dtype;             /* psd_dtype of q, K, V and the page statistics */
+  int32_t reserved;          /* must be 0 */
+  int64_t k_block_stride, k_token_stride, k_head_stride;
+  int64_t v_block_stride, v_token_stride, v_head_stride;
+} psd_shape;
+
+/*
+ * Page statistics layout (`meta`): [num_blocks, num_kv_heads, 2, head_dim] in `dtype`,
+ * indexed by PHYSICAL block like the cache; plane 0 holds the per-dim minimum of the
+ * page's valid keys, plane 1 the maximum. Values are exact (copied key values).
+ */
+
+/*
+ * psd_page_meta_update - recompute page statistics from the cached keys.
+ *
+ * For every sequence s, refreshes the logical pages [first_page[s], n_s) (all pages from
+ * first_page on), or only the page holding token L_s - 1 when first_page is NULL (the
+ * decode-time refresh after the new token's K/V has been written into the cache).
+ * Passing first_page[s] = 0 rebuilds every page (prefill). first_page values < 0 are
+ * treated as 0. Writes meta[block_table[s][p], h, 0/1, :] for those pages only.
+ *
+ *   k_cache     [num_blocks, 16, H_kv, D] through the k_* strides (device, read)
+ *   meta        [num_blocks, H_kv, 2, D] (device, written)
+ *   block_table [B, max_pages_per_seq] int32 physical block ids (device, read)
+ *   seq_lens    [B] int32 tokens per sequence including the newest (device, read)
+ *   first_page  [B] int32 or NULL (device, read)
+ *
+ * Source: EntmaxKV README, package tree (per-page k_min / k_max refresh) and
+ * introduction (statistics kept beside the vLLM-layout cache).
+ */
+psd_status psd_page_meta_update(const psd_shape* shape, const void* k_cache, void* meta,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* first_page, hipStream_t stream);
+
+/* Workspace bytes psd_select_pages needs for this shape and b_max. 0 if unsupported. */
+size_t psd_select_workspace_bytes(const psd_shape* shape, int32_t b_max);
+
+/*
+ * psd_select_pages - pick the pages each (sequence, KV head) attends this step.
+ *
+ * For query head h and page p: UB_h(p) = sum_d max(q[h,d] kmin[p,d], q[h,d] kmax[p,d]),
+ * accumulated in fp64 over ascending d with exact products (bit-identical to a plain
+ * sequential fp64 loop). Group score(p) = max of UB_h(p) over the group's query heads.
+ * With n pages and b = min(n, max(budgets[s], 2)) (n when n <= 2): if n <= b all pages
+ * are kept; else pages 0 and n-1 plus the b-2 best of pages 1..n-2 by (score
+ * descending, page index ascending). No scale is applied before ranking.
+ *
+ *   q           [B, H_q, D] (device, read)
+ *   meta        statistics as above, current for every page scored (device, read)
+ *   budgets     [B] int32 pages kept per KV head, sink and tail included (device, read)
+ *   b_max       capacity of each selection row, >= 2; device precondition:
+ *               min(n_s, max(budgets[s], 2)) <= b_max. A row that would exceed it is
+ *               not truncated: its count is written as -1 and its pages as -1, and
+ *               psd_sparse_decode then writes NaN for that unit's heads.
+ *   sel_pages   [B, H_kv, b_max] int32 kept LOGICAL pages, ascending, -1 padded
+ *               (device, written)
+ *   sel_count   [B, H_kv] int32 number of kept pages (device, written)
+ *   workspace   >= psd_select_workspace_bytes(shape, b_max) bytes (device, scratch)
+ *
+ * Returns PSD_ERR_CAPACITY when b_max is beyond what the two-level selection holds.
+ * Source: EntmaxKV README, "Two selection strategies" (top-k from a Quest-style bound,
+ * budget counts pages and includes the tail page); LOCKS README, introduction and
+ * "Results" (sink + recent kept, inside b), "Configuration" (GQA combine `max`),
+ * "How it works" (static top-b, no second exact pass; MLA max-union over heads).
+ */
+psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* meta,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
+                            int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * Workspace bytes psd_sparse_decode (max_pages_attended = its b_max) or psd_dense_decode
+ * (max_pages_attended = max_pages_per_seq) needs. 0 if unsupported.
+ */
+size_t psd_decode_workspace_bytes(const psd_shape* shape, int32_t max_pages_attended);
+
+/*
+ * psd_sparse_decode - softmax attention over the kept pages only.
+ *
+ * out[s, h, :] = sum_t softmax_t(scale * q[s,h] . K_t) V_t[:D_v] over the valid tokens t
+ * of the pages sel_pages[s, h / G, 0 .. sel_count - 1]. Accumulation is fp32 with
+ * split-K partials merged by log-sum-exp. Units whose sel_count is negative get NaN.
+ *
+ *   q, k_cache, v_cache, block_table, seq_lens as above (device, read)
+ *   sel_pages, sel_count, b_max   as written by psd_select_pages (device, read)
+ *   scale       softmax scale (1 / sqrt(head_dim) for standard attention)
+ *   out         [B, H_q, D_v] fp32 (device, written)
+ *   workspace   >= psd_decode_workspace_bytes(shape, b_max) bytes (device, scratch)
+ *
+ * Source: EntmaxKV README, introduction (attention exact over the selection) and
+ * package tree (decode over selected pages); LOCKS README, "How it works" (a paged
+ * attention kernel reads only the selected pages).
+ */
+psd_status psd_sparse_decode(const psd_shape* shape, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* sel_pages,
+                             const int32_t* sel_count, int32_t b_max, float scale, float* out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * psd_dense_decode - the same attention over every page of each sequence (baseline).
+ *
+ * workspace >= psd_decode_workspace_bytes(shape, shape->max_pages_per_seq) bytes.
+ * Source: EntmaxKV README, package tree (exact paged decode); AMASS page, "Headline
+ * results" and LOCKS README, "Efficiency" (dense attention as the comparison line).
+ */
+psd_status psd_dense_decode(const psd_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, float scale, float* out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* psd_status_string(psd_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t psd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSD_H */

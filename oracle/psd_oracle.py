@@ -137,7 +137,7 @@ def gather_tokens(cache, block_table_row, length: int, pages, head: int, dims: i
     """Valid tokens of the given logical pages for one KV head: [T, dims] float64."""
     pages = np.asarray(pages, dtype=np.int64)
     blocks = np.asarray(block_table_row, dtype=np.int64)[pages]
-    rows = np.asarray(cache[blocks], dtype=np.float64)[:, :, head, :dims]  # [m, 16, dims]
+    rows = np.asarray(cache[blocks, :, head, :dims], dtype=np.float64)  # [m, 16, dims]
     parts = [rows[i, : valid_in_page(length, p)] for i, p in enumerate(pages)]
     return np.concatenate(parts, axis=0)
 

@@ -1,0 +1,13 @@
+"""Page-selected sparse paged decode attention for AMD Instinct MI355X (gfx950).
+
+The computation lives in libpsd.so (HIP kernels behind the C-ABI of include/psd.h);
+this package only marshals arguments to it and sizes device buffers.
+"""
+from .api import (PsdError, PsdShape, decode_workspace_bytes, dense_decode, make_shape,
+                  page_meta_update, select_pages, select_workspace_bytes, sparse_decode,
+                  status_string, version)
+from .runner import DecodeStep
+
+__all__ = ["DecodeStep", "PsdError", "PsdShape", "decode_workspace_bytes", "dense_decode",
+           "make_shape", "page_meta_update", "select_pages", "select_workspace_bytes",
+           "sparse_decode", "status_string", "version"]

@@ -1,0 +1,64 @@
+"""ctypes view of libpsd.so (the C-ABI in include/psd.h). Loading fails loudly."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpsd.so")
+
+c_i32, c_i64, c_size, c_void_p, c_float = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                            ctypes.c_void_p, ctypes.c_float)
+
+PSD_F32, PSD_BF16 = 0, 1
+
+STATUS = {0: "PSD_OK", -1: "PSD_ERR_INVALID_ARG", -2: "PSD_ERR_UNSUPPORTED",
+          -3: "PSD_ERR_WORKSPACE", -4: "PSD_ERR_CAPACITY", -5: "PSD_ERR_LAUNCH"}
+
+# Every entry point of include/psd.h: name -> (restype, argtypes).
+SIGNATURES = {
+    "psd_page_meta_update": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p]),
+    "psd_select_workspace_bytes": (c_size, [c_void_p, c_i32]),
+    "psd_select_pages": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_i32, c_void_p, c_void_p, c_void_p, c_size, c_void_p]),
+    "psd_decode_workspace_bytes": (c_size, [c_void_p, c_i32]),
+    "psd_sparse_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_i32, c_float, c_void_p, c_void_p, c_size,
+                                  c_void_p]),
+    "psd_dense_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_float, c_void_p, c_void_p, c_size, c_void_p]),
+    "psd_status_string": (ctypes.c_char_p, [c_i32]),
+    "psd_version": (c_i32, []),
+}
+
+
+class PsdShape(ctypes.Structure):
+    """Mirror of psd_shape."""
+
+    _fields_ = [
+        ("batch", c_i32), ("num_q_heads", c_i32), ("num_kv_heads", c_i32), ("head_dim", c_i32),
+        ("head_dim_v", c_i32), ("page_size", c_i32), ("num_blocks", c_i32),
+        ("max_pages_per_seq", c_i32), ("dtype", c_i32), ("reserved", c_i32),
+        ("k_block_stride", c_i64), ("k_token_stride", c_i64), ("k_head_stride", c_i64),
+        ("v_block_stride", c_i64), ("v_token_stride", c_i64), ("v_head_stride", c_i64),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m page_selected_sparse_amd.build`"
+                " (there is no fallback path)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib

@@ -1,0 +1,113 @@
+"""Python names for the C-ABI calls: argument marshalling only.
+
+Tensors are passed by device pointer and the work is queued on torch's current HIP
+stream (or the stream given). Every step of the computation runs in the library's
+kernels; a status other than PSD_OK raises PsdError.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native
+from ._native import PSD_BF16, PSD_F32, PsdShape
+
+__all__ = ["PsdError", "PsdShape", "make_shape", "page_meta_update", "select_workspace_bytes",
+           "select_pages", "decode_workspace_bytes", "sparse_decode", "dense_decode",
+           "status_string", "version"]
+
+
+class PsdError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {_native.STATUS.get(status, status)} "
+                         f"({status_string(status)})")
+
+
+def status_string(status: int) -> str:
+    return _native.lib().psd_status_string(status).decode()
+
+
+def version() -> int:
+    return _native.lib().psd_version()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return PSD_BF16
+    if t == torch.float32:
+        return PSD_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def make_shape(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               block_table: torch.Tensor, head_dim_v: int | None = None) -> PsdShape:
+    """psd_shape for q [B, H_q, D] and caches [num_blocks, 16, H_kv, D(v)] (any strides with
+    a contiguous last axis; V may be a leading-dims view of a latent K)."""
+    B, Hq, D = q.shape
+    NB, page, Hkv, _ = k_cache.shape
+    dv = v_cache.shape[-1] if head_dim_v is None else head_dim_v
+    ks, vs = k_cache.stride(), v_cache.stride()
+    return PsdShape(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, head_dim_v=dv,
+                    page_size=page, num_blocks=NB, max_pages_per_seq=block_table.shape[1],
+                    dtype=_dtype_code(q.dtype), reserved=0, k_block_stride=ks[0],
+                    k_token_stride=ks[1], k_head_stride=ks[2], v_block_stride=vs[0],
+                    v_token_stride=vs[1], v_head_stride=vs[2])
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ok(status: int, call: str):
+    if status != 0:
+        raise PsdError(status, call)
+
+
+def page_meta_update(shape: PsdShape, k_cache, meta, block_table, seq_lens, first_page=None,
+                     stream=None):
+    _ok(_native.lib().psd_page_meta_update(ctypes.byref(shape), _ptr(k_cache), _ptr(meta),
+                                           _ptr(block_table), _ptr(seq_lens), _ptr(first_page),
+                                           _stream(stream)), "psd_page_meta_update")
+
+
+def select_workspace_bytes(shape: PsdShape, b_max: int) -> int:
+    return int(_native.lib().psd_select_workspace_bytes(ctypes.byref(shape), b_max))
+
+
+def select_pages(shape: PsdShape, q, meta, block_table, seq_lens, budgets, b_max: int, sel_pages,
+                 sel_count, workspace, stream=None):
+    _ok(_native.lib().psd_select_pages(ctypes.byref(shape), _ptr(q), _ptr(meta),
+                                       _ptr(block_table), _ptr(seq_lens), _ptr(budgets), b_max,
+                                       _ptr(sel_pages), _ptr(sel_count), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream)), "psd_select_pages")
+
+
+def decode_workspace_bytes(shape: PsdShape, max_pages_attended: int) -> int:
+    return int(_native.lib().psd_decode_workspace_bytes(ctypes.byref(shape), max_pages_attended))
+
+
+def sparse_decode(shape: PsdShape, q, k_cache, v_cache, block_table, seq_lens, sel_pages,
+                  sel_count, b_max: int, scale: float, out, workspace, stream=None):
+    _ok(_native.lib().psd_sparse_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                        _ptr(sel_pages), _ptr(sel_count), b_max, scale,
+                                        _ptr(out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)), "psd_sparse_decode")
+
+
+def dense_decode(shape: PsdShape, q, k_cache, v_cache, block_table, seq_lens, scale: float, out,
+                 workspace, stream=None):
+    _ok(_native.lib().psd_dense_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(block_table), _ptr(seq_lens), scale, _ptr(out),
+                                       _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream)), "psd_dense_decode")

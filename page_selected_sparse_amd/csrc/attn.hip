@@ -1,0 +1,368 @@
+// Split-K paged decode attention over a list of pages, and the log-sum-exp merge.
+//
+// EntmaxKV README, introduction: attention is exact over the selected pages; LOCKS
+// README, "How it works": the paged attention kernel reads only the selected pages.
+// The same kernel, walking every page of the block table, is the dense baseline.
+//
+// Work decomposition: one workgroup per (sequence s, KV head g, split); a split is up to
+// `pps` consecutive entries of the unit's page list. Each wave owns a tile of 16 query
+// heads of the group (G <= 16: one wave, heads past G are zero padding; G = 128: eight
+// waves). Per 16-token page a wave computes
+//   S^T[token, head] = K_page[16 x D] . Q_tile^T         (MFMA 16x16x32 bf16, fp32 acc)
+// so that each lane holds one head's scores for 4 tokens, runs the online softmax in
+// fp32 (base-2 exponent with scale*log2(e) folded in), and accumulates
+//   O[head, d] += P[head, token] . V_page[token, d]     (MFMA 16x16x16 bf16, fp32 acc)
+// with P split into bf16 hi + lo parts, so P keeps ~16 mantissa bits. V's columns are
+// assigned to MFMA columns as d = lane_col * (Dv / 16) + c so that each lane loads
+// contiguous bytes of V rows and a 16-byte load serves 8 MFMAs. fp32 caches are fed to
+// the same MFMAs as bf16 hi + lo pairs (three products: hi*hi + lo*hi + hi*lo).
+// Slots past the sequence length (tail page only) are masked in S and zeroed in V.
+// A wave writes unnormalised fp32 partials (m, l, acc) per head; lse_merge_kernel
+// combines the splits: M = max m_i, out = sum acc_i 2^(m_i - M) / sum l_i 2^(m_i - M).
+#include <math.h>
+
+#include "psd_device.h"
+#include "psd_launch.h"
+
+namespace psd {
+namespace {
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* bt;
+  const int32_t* lens;
+  const int32_t* sel;  // nullptr: dense (every page)
+  const int32_t* cnt;
+  float* pacc;  // [B, Hq, nsplit, Dv]
+  float2* pml;  // [B, Hq, nsplit]
+  int Hq, Hkv, G, max_pages, b_max, pps, nsplit;
+  int64_t kbs, kts, khs, vbs, vts, vhs;
+  float sl2;  // scale * log2(e)
+};
+
+struct MergeArgs {
+  const int32_t* lens;
+  const int32_t* cnt;  // nullptr: dense
+  const float* pacc;
+  const float2* pml;
+  float* out;
+  int Hq, Hkv, G, pps, nsplit, Dv, b_max;
+};
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) {
+  u32x4 v = {w.x, w.y, w.z, w.w};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ short4v as_short4(uint32_t lo, uint32_t hi) {
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+  u32x2 v = {lo, hi};
+  return __builtin_bit_cast(short4v, v);
+}
+
+// 8 fp32 values -> bf16 hi part and bf16 lo (residual) part, packed 2 per word.
+__device__ __forceinline__ void split8(const float* x, uint4& hi, uint4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = f2bf(x[i]);
+    l[i] = f2bf(x[i] - __uint_as_float(h[i] << 16));
+  }
+  hi = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+  lo = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
+}
+
+__device__ __forceinline__ float wave_max4(float x) {  // over lanes l, l^16, l^32, l^48
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float wave_sum4(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+
+// Loads the 8-element fragment of row `row` at dim `d` as bf16 (hi, lo for fp32 data).
+template <bool BF16>
+__device__ __forceinline__ void load_frag8(const void* base, int64_t off, uint4& hi, uint4& lo) {
+  if constexpr (BF16) {
+    hi = load16(static_cast<const uint16_t*>(base) + off);
+  } else {
+    const float* p = static_cast<const float*>(base) + off;
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    split8(x, hi, lo);
+  }
+}
+
+template <bool BF16, int DQK, int DV>
+__global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
+  constexpr int NQ = DQK / 32;   // QK MFMAs per page (K = 32 dims each)
+  constexpr int NC = DV / 16;    // PV MFMAs per page (16 output columns each)
+  static_assert(NC % 4 == 0, "Dv must be a multiple of 64");
+  constexpr bool QREG = DQK <= 128;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int L = a.lens[s];
+  const int n = ceil_div(L, kPage);
+  int count = a.sel ? min(a.cnt[s * a.Hkv + g], a.b_max) : n;
+  if (count < 0) count = 0;  // flagged unit: the merge writes NaN
+  const int p0 = split * a.pps;
+  if (p0 >= count) return;
+  const int np = min(a.pps, count - p0);
+
+  // Page list of this split: lane i holds entry p0 + i.
+  int my_lp = 0, my_blk = 0;
+  if (lane < np) {
+    my_lp = a.sel ? a.sel[(int64_t)(s * a.Hkv + g) * a.b_max + p0 + lane] : p0 + lane;
+    my_blk = a.bt[(int64_t)s * a.max_pages + my_lp];
+  }
+
+  // Q tile as the B operand of S^T = K Q^T: lane holds head r, dims 32c + 8grp .. +8.
+  const int head = wave * 16 + r;  // within the group
+  const bool hvalid = head < a.G;
+  const int64_t qrow = ((int64_t)s * a.Hq + g * a.G + (hvalid ? head : 0)) * DQK;
+  uint4 qhi[QREG ? NQ : 1], qlo[QREG ? NQ : 1];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      qhi[c] = make_uint4(0, 0, 0, 0);
+      qlo[c] = make_uint4(0, 0, 0, 0);
+      if (hvalid) load_frag8<BF16>(a.q, qrow + 32 * c + 8 * grp, qhi[c], qlo[c]);
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float4v acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  for (int i = 0; i < np; ++i) {
+    const int lp = __builtin_amdgcn_readlane(my_lp, i);
+    const int blk = __builtin_amdgcn_readlane(my_blk, i);
+    const int valid = min(kPage, L - lp * kPage);  // tokens of this page before L
+
+    // ---- S^T = K Q^T -------------------------------------------------------------------
+    const int64_t krow = (int64_t)blk * a.kbs + (int64_t)r * a.kts + (int64_t)g * a.khs;
+    float4v sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      uint4 khi, klo, qh, ql;
+      load_frag8<BF16>(a.k, krow + 32 * c + 8 * grp, khi, klo);
+      if constexpr (QREG) {
+        qh = qhi[c];
+        ql = qlo[c];
+      } else {
+        qh = ql = make_uint4(0, 0, 0, 0);
+        if (hvalid) load_frag8<BF16>(a.q, qrow + 32 * c + 8 * grp, qh, ql);
+      }
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(khi), as_bf16x8(qh), sacc, 0, 0, 0);
+      if constexpr (!BF16) {
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(klo), as_bf16x8(qh), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(khi), as_bf16x8(ql), sacc, 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax: lane holds head r, tokens 4grp .. 4grp+3 ----------------------
+    float z[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * grp + j;
+      z[j] = t < valid ? sacc[j] * a.sl2 : -INFINITY;
+    }
+    float m_loc = wave_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    const float m_new = fmaxf(m_run, m_loc);
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? exp2f(m_run - m_new) : 1.f;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = live ? exp2f(z[j] - m_new) : 0.f;
+    l_run = l_run * alpha + wave_sum4(p[0] + p[1] + p[2] + p[3]);
+    m_run = m_new;
+
+    // P as the A operand (head r, tokens 4grp + j), bf16 hi + lo.
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ph[j] = f2bf(p[j]);
+      pl[j] = f2bf(p[j] - __uint_as_float(ph[j] << 16));
+    }
+    const short4v Ph = as_short4(pack2(ph[0], ph[1]), pack2(ph[2], ph[3]));
+    const short4v Pl = as_short4(pack2(pl[0], pl[1]), pack2(pl[2], pl[3]));
+
+    // Rescale the output rows (heads 4grp + j) by their alpha.
+    float al[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 4 * grp + j, 64);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[c][j] *= al[j];
+    }
+
+    // ---- O += P V: lane loads V[token 4grp + j][r*NC .. r*NC + NC) -----------------------
+    const int64_t vrow = (int64_t)blk * a.vbs + (int64_t)g * a.vhs + (int64_t)r * NC;
+    const bool tail = valid < kPage;
+    constexpr int CW = (BF16 && NC >= 8) ? 8 : 4;  // columns per load group
+    constexpr int NG = NC / CW;
+#pragma unroll
+    for (int w = 0; w < NG; ++w) {
+      uint32_t vh[4][4], vl[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 4 * grp + j;
+        const int64_t off = vrow + (int64_t)t * a.vts + w * CW;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) vh[j][x] = vl[j][x] = 0u;
+        if (!tail || t < valid) {
+          if constexpr (BF16 && CW == 8) {
+            const uint4 x4 = load16(static_cast<const uint16_t*>(a.v) + off);
+            vh[j][0] = x4.x; vh[j][1] = x4.y; vh[j][2] = x4.z; vh[j][3] = x4.w;
+          } else if constexpr (BF16) {
+            const uint2 x2 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + off);
+            vh[j][0] = x2.x; vh[j][1] = x2.y;
+          } else {
+            const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + off);
+            const float xs[8] = {f.x, f.y, f.z, f.w, 0.f, 0.f, 0.f, 0.f};
+            uint4 hh, ll;
+            split8(xs, hh, ll);
+            vh[j][0] = hh.x; vh[j][1] = hh.y;
+            vl[j][0] = ll.x; vl[j][1] = ll.y;
+          }
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < CW; ++cc) {
+        const int c = w * CW + cc;
+        const int wd = cc >> 1;
+        const bool hiw = cc & 1;
+        uint32_t e[4], f[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          e[j] = hiw ? (vh[j][wd] >> 16) : (vh[j][wd] & 0xffffu);
+          f[j] = hiw ? (vl[j][wd] >> 16) : (vl[j][wd] & 0xffffu);
+        }
+        const short4v Vb = as_short4(pack2(e[0], e[1]), pack2(e[2], e[3]));
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ph, Vb, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Pl, Vb, acc[c], 0, 0, 0);
+        if constexpr (!BF16) {
+          const short4v Vl = as_short4(pack2(f[0], f[1]), pack2(f[2], f[3]));
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ph, Vl, acc[c], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- partials: acc rows are heads 4grp + j, columns d = r*NC + c ----------------------
+  const int64_t ubase = (int64_t)s * a.Hq + g * a.G;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int hh = wave * 16 + 4 * grp + j;
+    if (hh < a.G) {
+      float* dst = a.pacc + ((ubase + hh) * a.nsplit + split) * DV + r * NC;
+#pragma unroll
+      for (int c = 0; c < NC; c += 4)
+        *reinterpret_cast<float4*>(dst + c) =
+            make_float4(acc[c][j], acc[c + 1][j], acc[c + 2][j], acc[c + 3][j]);
+    }
+  }
+  if (grp == 0 && hvalid) a.pml[(ubase + head) * a.nsplit + split] = make_float2(m_run, l_run);
+}
+
+__global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
+  extern __shared__ float wts[];  // [nsplit + 1]
+  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int g = h / a.G;
+  const int L = a.lens[s];
+  const int n = ceil_div(L, kPage);
+  const int count = a.cnt ? min(a.cnt[s * a.Hkv + g], a.b_max) : n;
+  float* out = a.out + ((int64_t)s * a.Hq + h) * a.Dv;
+  if (count <= 0) {
+    for (int d = tid; d < a.Dv; d += blockDim.x) out[d] = __builtin_nanf("");
+    return;
+  }
+  const int nsp = ceil_div(count, a.pps);
+  const int64_t row = ((int64_t)s * a.Hq + h) * a.nsplit;
+  if (tid == 0) {
+    float M = -INFINITY;
+    for (int i = 0; i < nsp; ++i) M = fmaxf(M, a.pml[row + i].x);
+    float Ls = 0.f;
+    for (int i = 0; i < nsp; ++i) {
+      const float2 ml = a.pml[row + i];
+      const float w = exp2f(ml.x - M);
+      wts[i] = w;
+      Ls += ml.y * w;
+    }
+    wts[nsp] = 1.f / Ls;
+  }
+  __syncthreads();
+  const float inv = wts[nsp];
+  for (int d = tid; d < a.Dv; d += blockDim.x) {
+    float o = 0.f;
+    for (int i = 0; i < nsp; ++i) o += a.pacc[(row + i) * a.Dv + d] * wts[i];
+    out[d] = o * inv;
+  }
+}
+
+template <bool BF16, int DQK, int DV>
+hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) {
+  hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV>), grid, dim3(64 * waves), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool plan_decode(const Geo& g, int max_pages_attended, DecodePlan* p) {
+  if (max_pages_attended < 1) return false;
+  p->waves = (g.G + 15) / 16;
+  const int64_t units = (int64_t)g.B * g.Hkv;
+  // Aim for ~2048 single-wave workgroups (fewer, larger ones for many-head groups).
+  const int64_t target = p->waves > 1 ? 512 : 2048;
+  int64_t pps = (units * max_pages_attended + target - 1) / target;
+  const int64_t lo = p->waves > 1 ? 4 : 1;
+  pps = pps < lo ? lo : (pps > 64 ? 64 : pps);
+  p->pps = (int)pps;
+  p->nsplit = (max_pages_attended + p->pps - 1) / p->pps;
+  const size_t parts = (size_t)g.B * g.Hq * p->nsplit;
+  p->off_ml = (parts * g.Dv * sizeof(float) + 255) / 256 * 256;
+  p->bytes = p->off_ml + parts * sizeof(float2) + 256;
+  return true;
+}
+
+hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const void* k,
+                         const void* v, const int32_t* bt, const int32_t* lens,
+                         const int32_t* sel, const int32_t* cnt, int b_max, float scale,
+                         float* out, void* ws, hipStream_t st) {
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  AttnArgs a{q, k, v, bt, lens, sel, cnt,
+             reinterpret_cast<float*>(w), reinterpret_cast<float2*>(w + p.off_ml),
+             g.Hq, g.Hkv, g.G, g.max_pages, b_max, p.pps, p.nsplit,
+             g.kbs, g.kts, g.khs, g.vbs, g.vts, g.vhs, scale * 1.4426950408889634f};
+  const dim3 grid(p.nsplit, g.Hkv, g.B);
+  hipError_t e;
+  const bool bf = g.dtype == 1;
+  if (g.D == 64)
+    e = bf ? launch_attn<true, 64, 64>(a, grid, p.waves, st)
+           : launch_attn<false, 64, 64>(a, grid, p.waves, st);
+  else if (g.D == 128)
+    e = bf ? launch_attn<true, 128, 128>(a, grid, p.waves, st)
+           : launch_attn<false, 128, 128>(a, grid, p.waves, st);
+  else
+    e = bf ? launch_attn<true, 576, 512>(a, grid, p.waves, st)
+           : launch_attn<false, 576, 512>(a, grid, p.waves, st);
+  if (e != hipSuccess) return e;
+  MergeArgs m{lens, sel ? cnt : nullptr, a.pacc, a.pml, out, g.Hq, g.Hkv, g.G, p.pps,
+              p.nsplit, g.Dv, b_max};
+  const int threads = g.Dv >= 256 ? 256 : g.Dv;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(g.Hq, g.B), dim3(threads),
+                     (p.nsplit + 1) * sizeof(float), st, m);
+  return hipGetLastError();
+}
+
+}  // namespace psd

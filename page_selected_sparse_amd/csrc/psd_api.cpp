@@ -1,0 +1,177 @@
+// C-ABI entry points declared in include/psd.h: host-side argument checks, workspace
+// sizing and stream-ordered kernel launches. Nothing here allocates or synchronises.
+#include "psd.h"
+
+#include <stdint.h>
+
+#include "psd_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dims(int D, int Dv) {
+  return (D == 64 && Dv == 64) || (D == 128 && Dv == 128) || (D == 576 && Dv == 512);
+}
+
+bool supported_group(int G) { return (G >= 1 && G <= 16) || (G % 16 == 0 && G <= 128); }
+
+// Shape checks common to every call; fills the kernel geometry.
+psd_status check_shape(const psd_shape* sh, psd::Geo* g) {
+  if (!sh) return PSD_ERR_INVALID_ARG;
+  if (sh->batch < 1 || sh->num_q_heads < 1 || sh->num_kv_heads < 1 || sh->head_dim < 1 ||
+      sh->head_dim_v < 1 || sh->num_blocks < 1 || sh->max_pages_per_seq < 1 ||
+      sh->reserved != 0)
+    return PSD_ERR_INVALID_ARG;
+  if (sh->page_size != 16) return PSD_ERR_INVALID_ARG;
+  if (sh->dtype != PSD_F32 && sh->dtype != PSD_BF16) return PSD_ERR_INVALID_ARG;
+  if (sh->num_q_heads % sh->num_kv_heads != 0) return PSD_ERR_INVALID_ARG;
+  if (sh->head_dim_v > sh->head_dim) return PSD_ERR_INVALID_ARG;
+  if (!supported_dims(sh->head_dim, sh->head_dim_v)) return PSD_ERR_UNSUPPORTED;
+  const int G = sh->num_q_heads / sh->num_kv_heads;
+  if (!supported_group(G)) return PSD_ERR_UNSUPPORTED;
+  if ((int64_t)sh->batch * sh->max_pages_per_seq > INT32_MAX) return PSD_ERR_UNSUPPORTED;
+  g->B = sh->batch;
+  g->Hq = sh->num_q_heads;
+  g->Hkv = sh->num_kv_heads;
+  g->G = G;
+  g->D = sh->head_dim;
+  g->Dv = sh->head_dim_v;
+  g->num_blocks = sh->num_blocks;
+  g->max_pages = sh->max_pages_per_seq;
+  g->dtype = sh->dtype;
+  g->kbs = sh->k_block_stride;
+  g->kts = sh->k_token_stride;
+  g->khs = sh->k_head_stride;
+  g->vbs = sh->v_block_stride;
+  g->vts = sh->v_token_stride;
+  g->vhs = sh->v_head_stride;
+  return PSD_OK;
+}
+
+// Cache strides: positive, 16-byte multiples, and rows that fit inside a block.
+psd_status check_strides(const psd::Geo& g, bool need_v) {
+  const int64_t es = g.dtype == PSD_BF16 ? 2 : 4;
+  auto ok = [&](int64_t bs, int64_t ts, int64_t hs, int dims) {
+    if (bs <= 0 || ts <= 0 || hs < 0) return false;
+    if ((bs * es) % 16 || (ts * es) % 16 || (hs * es) % 16) return false;
+    if (g.Hkv > 1 && hs < dims) return false;
+    if (ts < (int64_t)(g.Hkv - 1) * hs + dims) return false;
+    if (bs < 15 * ts + (int64_t)(g.Hkv - 1) * hs + dims) return false;
+    return true;
+  };
+  if (!ok(g.kbs, g.kts, g.khs, g.D)) return PSD_ERR_INVALID_ARG;
+  if (need_v && !ok(g.vbs, g.vts, g.vhs, g.Dv)) return PSD_ERR_INVALID_ARG;
+  return PSD_OK;
+}
+
+psd_status launched(hipError_t e) { return e == hipSuccess ? PSD_OK : PSD_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+psd_status psd_page_meta_update(const psd_shape* shape, const void* k_cache, void* meta,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* first_page, hipStream_t stream) {
+  psd::Geo g;
+  psd_status st = check_shape(shape, &g);
+  if (st != PSD_OK) return st;
+  if (!k_cache || !meta || !block_table || !seq_lens) return PSD_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(meta)) return PSD_ERR_INVALID_ARG;
+  if ((st = check_strides(g, false)) != PSD_OK) return st;
+  return launched(psd::launch_meta_update(g, k_cache, meta, block_table, seq_lens, first_page,
+                                          stream));
+}
+
+size_t psd_select_workspace_bytes(const psd_shape* shape, int32_t b_max) {
+  psd::Geo g;
+  if (check_shape(shape, &g) != PSD_OK) return 0;
+  psd::SelectPlan p;
+  if (!psd::plan_select(g, b_max, &p)) return 0;
+  return p.bytes;
+}
+
+psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* meta,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
+                            int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  psd::Geo g;
+  psd_status st = check_shape(shape, &g);
+  if (st != PSD_OK) return st;
+  if (!q || !meta || !block_table || !seq_lens || !budgets || !sel_pages || !sel_count)
+    return PSD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(meta)) return PSD_ERR_INVALID_ARG;
+  if (b_max < 2) return PSD_ERR_INVALID_ARG;
+  psd::SelectPlan p;
+  if (!psd::plan_select(g, b_max, &p)) return PSD_ERR_CAPACITY;
+  if (!workspace || workspace_bytes < p.bytes || !aligned16(workspace)) return PSD_ERR_WORKSPACE;
+  return launched(psd::launch_select(g, p, q, meta, block_table, seq_lens, budgets, b_max,
+                                     sel_pages, sel_count, workspace, stream));
+}
+
+size_t psd_decode_workspace_bytes(const psd_shape* shape, int32_t max_pages_attended) {
+  psd::Geo g;
+  if (check_shape(shape, &g) != PSD_OK) return 0;
+  psd::DecodePlan p;
+  if (!psd::plan_decode(g, max_pages_attended, &p)) return 0;
+  return p.bytes;
+}
+
+static psd_status decode_common(const psd_shape* shape, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* sel_pages,
+                                const int32_t* sel_count, int32_t pages_cap, int32_t b_max,
+                                float scale, float* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  psd::Geo g;
+  psd_status st = check_shape(shape, &g);
+  if (st != PSD_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return PSD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return PSD_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == __builtin_inff()) return PSD_ERR_INVALID_ARG;
+  if ((st = check_strides(g, true)) != PSD_OK) return st;
+  psd::DecodePlan p;
+  if (!psd::plan_decode(g, pages_cap, &p)) return PSD_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < p.bytes || !aligned16(workspace)) return PSD_ERR_WORKSPACE;
+  return launched(psd::launch_decode(g, p, q, k_cache, v_cache, block_table, seq_lens, sel_pages,
+                                     sel_count, b_max, scale, out, workspace, stream));
+}
+
+psd_status psd_sparse_decode(const psd_shape* shape, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* sel_pages,
+                             const int32_t* sel_count, int32_t b_max, float scale, float* out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!sel_pages || !sel_count || b_max < 1) return PSD_ERR_INVALID_ARG;
+  return decode_common(shape, q, k_cache, v_cache, block_table, seq_lens, sel_pages, sel_count,
+                       b_max, b_max, scale, out, workspace, workspace_bytes, stream);
+}
+
+psd_status psd_dense_decode(const psd_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, float scale, float* out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!shape) return PSD_ERR_INVALID_ARG;
+  return decode_common(shape, q, k_cache, v_cache, block_table, seq_lens, nullptr, nullptr,
+                       shape->max_pages_per_seq, 0, scale, out, workspace, workspace_bytes,
+                       stream);
+}
+
+const char* psd_status_string(psd_status s) {
+  switch (s) {
+    case PSD_OK: return "ok";
+    case PSD_ERR_INVALID_ARG: return "invalid argument";
+    case PSD_ERR_UNSUPPORTED: return "unsupported shape";
+    case PSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case PSD_ERR_CAPACITY: return "selection capacity (b_max) exceeded";
+    case PSD_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t psd_version(void) { return 100; }
+
+}  // extern "C"

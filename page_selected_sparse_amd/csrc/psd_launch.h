@@ -1,0 +1,51 @@
+// Host-side launch interface between the C-ABI layer (psd_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace psd {
+
+// Plain geometry copied out of psd_shape after validation.
+struct Geo {
+  int B, Hq, Hkv, G, D, Dv, num_blocks, max_pages, dtype;  // dtype: 0 f32, 1 bf16
+  int64_t kbs, kts, khs, vbs, vts, vhs;
+};
+
+// ---- page statistics ------------------------------------------------------------------
+hipError_t launch_meta_update(const Geo& g, const void* k, void* meta, const int32_t* bt,
+                              const int32_t* lens, const int32_t* first_page, hipStream_t st);
+
+// ---- selection --------------------------------------------------------------------------
+// Chunking of the candidate pages 1..n-2 of a unit for the two-level top-b.
+struct SelectPlan {
+  int chunk;       // candidate pages per scoring workgroup (256 * pages_per_thread)
+  int ppt;         // pages per thread
+  int nchunk;      // chunks covering max_pages - 2 candidates
+  int cap;         // candidate slots per chunk = min(chunk, b_max - 2)
+  int head_block;  // query heads scored per pass (template width)
+  int d_chunk;     // dims of q staged in LDS per pass
+  size_t off_idx, off_cnt, bytes;  // workspace layout
+  size_t merge_lds;                // dynamic LDS of the merge kernel
+};
+// Returns false when no plan fits (b_max too large).
+bool plan_select(const Geo& g, int b_max, SelectPlan* plan);
+hipError_t launch_select(const Geo& g, const SelectPlan& plan, const void* q, const void* meta,
+                         const int32_t* bt, const int32_t* lens, const int32_t* budgets,
+                         int b_max, int32_t* sel, int32_t* cnt, void* ws, hipStream_t st);
+
+// ---- attention -------------------------------------------------------------------------
+struct DecodePlan {
+  int pps;     // pages per split (one workgroup)
+  int nsplit;  // splits per unit
+  int waves;   // waves per workgroup = ceil(G / 16) head tiles
+  size_t off_ml, bytes;
+};
+bool plan_decode(const Geo& g, int max_pages_attended, DecodePlan* plan);
+hipError_t launch_decode(const Geo& g, const DecodePlan& plan, const void* q, const void* k,
+                         const void* v, const int32_t* bt, const int32_t* lens,
+                         const int32_t* sel, const int32_t* cnt, int b_max, float scale,
+                         float* out, void* ws, hipStream_t st);
+
+}  // namespace psd

@@ -1,0 +1,99 @@
+"""Device buffers for one layer's decode step and the three-call step itself.
+
+``DecodeStep`` owns (as torch tensors) the page statistics, the selection rows, the two
+workspaces and the output for a fixed batch geometry, and issues
+
+    page_meta_update (tail page) -> select_pages -> sparse_decode
+
+on one stream. ``dense()`` runs the dense baseline on the same inputs. Nothing here
+computes: it sizes buffers and forwards pointers to the C-ABI.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import api
+
+
+def _to_device_bits(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if dtype == "bf16":
+        return t.view(torch.int16).to(device).view(torch.bfloat16)
+    return t.to(device)
+
+
+class DecodeStep:
+    def __init__(self, q: torch.Tensor, cache: torch.Tensor, block_table: torch.Tensor,
+                 seq_lens: torch.Tensor, budgets: torch.Tensor, head_dim_v: int,
+                 latent: bool, b_max: int | None = None):
+        """q [B, H_q, D]; cache [2, NB, 16, H_kv, D] (or [1, ...] when ``latent``: V is the
+        first ``head_dim_v`` dims of K); block_table [B, max_pages] int32; seq_lens and
+        budgets [B] int32. All on the same HIP device."""
+        self.q, self.cache = q, cache
+        self.block_table, self.seq_lens, self.budgets = block_table, seq_lens, budgets
+        self.k = cache[0]
+        self.v = cache[0][..., :head_dim_v] if latent else cache[1]
+        self.shape = api.make_shape(q, self.k, self.v, block_table, head_dim_v)
+        B, Hq, D = q.shape
+        NB, _, Hkv, _ = self.k.shape
+        dev = q.device
+        if b_max is None:
+            b_max = int(budgets.max().item())
+        self.b_max = max(2, int(b_max))
+        self.scale = 1.0 / float(D) ** 0.5
+        self.meta = torch.empty((NB, Hkv, 2, D), dtype=q.dtype, device=dev)
+        self.sel_pages = torch.empty((B, Hkv, self.b_max), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, Hq, head_dim_v), dtype=torch.float32, device=dev)
+        self.out_dense = torch.empty_like(self.out)
+        sel_ws = api.select_workspace_bytes(self.shape, self.b_max)
+        dec_ws = api.decode_workspace_bytes(self.shape, self.b_max)
+        den_ws = api.decode_workspace_bytes(self.shape, self.shape.max_pages_per_seq)
+        if sel_ws == 0 or dec_ws == 0 or den_ws == 0:
+            raise api.PsdError(-2, "workspace query")
+        self.ws_select = torch.empty(sel_ws, dtype=torch.uint8, device=dev)
+        self.ws_decode = torch.empty(dec_ws, dtype=torch.uint8, device=dev)
+        self.ws_dense = torch.empty(den_ws, dtype=torch.uint8, device=dev)
+        self.first_page_zero = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    @classmethod
+    def from_arrays(cls, q: np.ndarray, cache: np.ndarray, block_table: np.ndarray,
+                    seq_lens: np.ndarray, budgets: np.ndarray, dtype: str, head_dim_v: int,
+                    latent: bool, device="cuda", b_max: int | None = None):
+        dev = torch.device(device)
+        return cls(_to_device_bits(q, dtype, dev), _to_device_bits(cache, dtype, dev),
+                   torch.from_numpy(np.ascontiguousarray(block_table, dtype=np.int32)).to(dev),
+                   torch.from_numpy(np.ascontiguousarray(seq_lens, dtype=np.int32)).to(dev),
+                   torch.from_numpy(np.ascontiguousarray(budgets, dtype=np.int32)).to(dev),
+                   head_dim_v, latent, b_max)
+
+    # -- the calls ------------------------------------------------------------------------
+    def build_meta(self, stream=None):
+        """Rebuild the statistics of every page (prefill)."""
+        api.page_meta_update(self.shape, self.k, self.meta, self.block_table, self.seq_lens,
+                             self.first_page_zero, stream)
+
+    def refresh_tail(self, stream=None):
+        api.page_meta_update(self.shape, self.k, self.meta, self.block_table, self.seq_lens,
+                             None, stream)
+
+    def select(self, stream=None):
+        api.select_pages(self.shape, self.q, self.meta, self.block_table, self.seq_lens,
+                         self.budgets, self.b_max, self.sel_pages, self.sel_count, self.ws_select,
+                         stream)
+
+    def sparse(self, stream=None):
+        api.sparse_decode(self.shape, self.q, self.k, self.v, self.block_table, self.seq_lens,
+                          self.sel_pages, self.sel_count, self.b_max, self.scale, self.out,
+                          self.ws_decode, stream)
+
+    def dense(self, stream=None):
+        api.dense_decode(self.shape, self.q, self.k, self.v, self.block_table, self.seq_lens,
+                         self.scale, self.out_dense, self.ws_dense, stream)
+
+    def step(self, stream=None):
+        """One sparse decode step: tail refresh, selection, attention over kept pages."""
+        self.refresh_tail(stream)
+        self.select(stream)
+        self.sparse(stream)

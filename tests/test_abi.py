@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports every call include/psd.h declares, and rejects bad
+arguments on the host before launching anything (no GPU needed for these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "psd.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(psd_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def native():
+    from page_selected_sparse_amd import _native
+    return _native
+
+
+def test_exports_every_declared_symbol(native):
+    lib = native.lib()
+    names = _declared()
+    assert set(names) == set(native.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(native):
+    lib = native.lib()
+    assert lib.psd_version() >= 100
+    for code in native.STATUS:
+        assert lib.psd_status_string(code)
+    assert lib.psd_status_string(-4) == b"selection capacity (b_max) exceeded"
+
+
+def _shape(native, **kw):
+    base = dict(batch=2, num_q_heads=32, num_kv_heads=8, head_dim=128, head_dim_v=128,
+                page_size=16, num_blocks=100, max_pages_per_seq=50, dtype=1, reserved=0,
+                k_block_stride=16 * 8 * 128, k_token_stride=8 * 128, k_head_stride=128,
+                v_block_stride=16 * 8 * 128, v_token_stride=8 * 128, v_head_stride=128)
+    base.update(kw)
+    return native.PsdShape(**base)
+
+
+def test_workspace_queries(native):
+    lib = native.lib()
+    sh = _shape(native)
+    assert lib.psd_select_workspace_bytes(ctypes.byref(sh), 10) > 0
+    assert lib.psd_decode_workspace_bytes(ctypes.byref(sh), 10) > 0
+    assert lib.psd_select_workspace_bytes(ctypes.byref(sh), 1) == 0  # b_max < 2
+    bad = _shape(native, head_dim=96, head_dim_v=96)
+    assert lib.psd_select_workspace_bytes(ctypes.byref(bad), 10) == 0
+    # 1M tokens, b_max 128: the two-level plan must fit
+    long = _shape(native, batch=1, max_pages_per_seq=65536, num_blocks=65536)
+    assert lib.psd_select_workspace_bytes(ctypes.byref(long), 128) > 0
+    # a capacity no plan can hold
+    assert lib.psd_select_workspace_bytes(ctypes.byref(long), 60000) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("page_size", 32, -1), ("num_q_heads", 30, -1), ("head_dim_v", 64, -2),
+    ("num_q_heads", 8 * 20, -2), ("dtype", 7, -1), ("reserved", 1, -1),
+    ("head_dim_v", 256, -1), ("batch", 0, -1)])
+def test_bad_shapes_rejected(native, field, value, code):
+    lib = native.lib()
+    sh = _shape(native, **{field: value})
+    fake = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    st = lib.psd_select_pages(ctypes.byref(sh), fake, fake, fake, fake, fake, 10, fake, fake,
+                              fake, 1 << 30, None)
+    assert st == code
+
+
+def test_null_and_workspace_errors(native):
+    lib = native.lib()
+    sh = _shape(native)
+    f = ctypes.c_void_p(16)
+    assert lib.psd_select_pages(None, f, f, f, f, f, 10, f, f, f, 1 << 30, None) == -1
+    assert lib.psd_select_pages(ctypes.byref(sh), None, f, f, f, f, 10, f, f, f, 1 << 30,
+                                None) == -1
+    assert lib.psd_select_pages(ctypes.byref(sh), f, f, f, f, f, 1, f, f, f, 1 << 30, None) == -1
+    assert lib.psd_select_pages(ctypes.byref(sh), f, f, f, f, f, 10, f, f, f, 8, None) == -3
+    assert lib.psd_select_pages(ctypes.byref(sh), f, f, f, f, f, 10, f, f, None, 1 << 30,
+                                None) == -3
+    long = _shape(native, batch=1, max_pages_per_seq=65536, num_blocks=65536)
+    assert lib.psd_select_pages(ctypes.byref(long), f, f, f, f, f, 60000, f, f, f, 1 << 40,
+                                None) == -4
+    # misaligned pointer
+    assert lib.psd_page_meta_update(ctypes.byref(sh), ctypes.c_void_p(18), f, f, f, None,
+                                    None) == -1
+    # strides that overlap heads
+    bad = _shape(native, k_head_stride=64)
+    assert lib.psd_page_meta_update(ctypes.byref(bad), f, f, f, f, None, None) == -1
+    # decode: bad scale, small workspace
+    assert lib.psd_dense_decode(ctypes.byref(sh), f, f, f, f, f, 0.0, f, f, 1 << 30, None) == -1
+    assert lib.psd_dense_decode(ctypes.byref(sh), f, f, f, f, f, 0.1, f, f, 4, None) == -3
+    assert lib.psd_sparse_decode(ctypes.byref(sh), f, f, f, f, f, None, f, 10, 0.1, f, f,
+                                 1 << 30, None) == -1

@@ -1,0 +1,159 @@
+"""Parity of the HIP path (through the C-ABI) with the fp64 oracle.
+
+Page statistics and selected pages must match bit for bit; attention outputs within
+2e-3 max abs. Small ragged cases cover several chunks, edge lengths and budgets; the five
+measured workloads run at full size with the oracle checking sampled sequences.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import ATOL, check_selection_row, check_workload, run_gpu
+from oracle import psd_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+SMALL = {
+    "ragged_default": synth.small_spec(),
+    "edge_lengths": synth.small_spec(batch=7, seq_lens=(1, 15, 16, 17, 31, 33, 250),
+                                     budget_pages=5, max_len=256),
+    "budget_0": synth.small_spec(batch=2, seq_lens=(300, 33), budget_pages=0, max_len=320),
+    "budget_3": synth.small_spec(batch=2, seq_lens=(300, 47), budget_pages=3, max_len=320),
+    "full_budget": synth.small_spec(batch=2, seq_lens=(700, 90), budget_percent=100,
+                                    max_len=704),
+    "group1": synth.small_spec(num_q_heads=4, num_kv_heads=4),
+    "group8": synth.small_spec(num_q_heads=16, num_kv_heads=2),
+    "group16": synth.small_spec(num_q_heads=16, num_kv_heads=1),
+    "group32": synth.small_spec(num_q_heads=64, num_kv_heads=2),
+    "d64_bf16": synth.small_spec(head_dim=64, head_dim_v=64),
+    "d64_f32": synth.small_spec(head_dim=64, head_dim_v=64, dtype="f32"),
+    "d128_f32": synth.small_spec(dtype="f32", seq_lens=(500, 37, 1200), max_len=1200),
+    "latent576": synth.small_spec(batch=2, num_q_heads=128, num_kv_heads=1, head_dim=576,
+                                  head_dim_v=512, latent=True, seq_lens=(1500, 333),
+                                  max_len=1504),
+    "many_chunks": synth.small_spec(batch=2, seq_lens=(16 * 3000 - 5, 16 * 700), budget_pages=40,
+                                    max_len=16 * 3000),
+    "tiny_cfg_seed1": dataclasses.replace(synth.SPECS["tiny"], seed=1),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name):
+    w = synth.make_workload(SMALL[name])
+    res = run_gpu(w)
+    check_workload(w, res)
+
+
+def test_full_budget_sparse_equals_dense_on_gpu():
+    w = synth.make_workload(SMALL["full_budget"])
+    res = run_gpu(w)
+    assert np.max(np.abs(res["out"] - res["dense"])) <= 1e-5
+
+
+def test_b_max_padding():
+    w = synth.make_workload(SMALL["ragged_default"])
+    res = run_gpu(w, b_max=int(w.budgets.max()) + 9)
+    check_workload(w, res)
+
+
+def test_capacity_flag_not_truncation():
+    w = synth.make_workload(synth.small_spec(batch=2, seq_lens=(1000, 100), budget_pages=20,
+                                             max_len=1008))
+    res = run_gpu(w, b_max=10, dense=False)
+    for s in range(2):
+        n = O.pages_of(int(w.seq_lens[s]))
+        for g in range(2):
+            if n > 10:
+                assert res["cnt"][s, g] == -1 and np.all(res["sel"][s, g] == -1)
+    assert np.all(np.isnan(res["out"][0]))
+
+
+def test_tie_break_across_chunks():
+    # 40 pages spread over several 256-page chunks get identical keys that beat every
+    # other page; with 25 free slots the 25 lowest-index copies must win.
+    spec = synth.small_spec(batch=1, seq_lens=(16 * 3000,), budget_pages=27, needles=0,
+                            num_q_heads=8, num_kv_heads=2, max_len=16 * 3000)
+    w = synth.make_workload(spec)
+    rng = np.random.default_rng(5)
+    pages = np.sort(rng.choice(np.arange(1, 2999), size=40, replace=False))
+    q = synth.to_f64(w.q, "bf16")[0]
+    for g in range(2):
+        vec = np.where(q[g * 4] >= 0, 4.0, -4.0).astype(np.float32)
+        bits = synth.f32_to_bf16_bits(vec)
+        for p in pages:
+            w.cache[0, w.block_table[0, p], :, g, :] = bits
+    res = run_gpu(w, dense=False)
+    for g in range(2):
+        expect = [0] + sorted(pages[:25].tolist()) + [2999]
+        check_selection_row(res["sel"][0, g], int(res["cnt"][0, g]), expect, res["b_max"])
+    check_workload(w, res, dense_seqs=[])
+
+
+def test_all_pages_tie():
+    spec = synth.small_spec(batch=1, seq_lens=(16 * 1200,), budget_pages=30, needles=0,
+                            num_q_heads=8, num_kv_heads=2, max_len=16 * 1200)
+    w = synth.make_workload(spec)
+    src = w.cache[0, w.block_table[0, 0]].copy()
+    w.cache[0] = src[None]
+    res = run_gpu(w, dense=False)
+    for g in range(2):
+        check_selection_row(res["sel"][0, g], int(res["cnt"][0, g]),
+                            list(range(29)) + [1199], res["b_max"])
+    check_workload(w, res, dense_seqs=[])
+
+
+# The five measured workloads at full size. Sequences checked against the oracle:
+# every one where the oracle is quick, a spread sample otherwise.
+FULL = [
+    ("tiny", None, None),
+    ("gqa8b_32k", None, None),
+    ("ragged_b32_32k", "sample8", "sample2"),
+    ("long_1m", None, []),
+    ("mla_64k", [0, 7, 15], [3]),
+]
+
+
+@pytest.mark.parametrize("name,seqs,dense_seqs", FULL)
+def test_measured_workloads(name, seqs, dense_seqs):
+    w = synth.make_workload(name)
+    res = run_gpu(w)
+    if seqs == "sample8":
+        order = np.argsort(w.seq_lens)
+        seqs = sorted({int(order[0]), int(order[-1])} | set(range(0, 32, 5)))
+    if dense_seqs == "sample2":
+        dense_seqs = [int(np.argmin(w.seq_lens)), int(np.argmax(w.seq_lens))]
+    check_workload(w, res, seqs=seqs, dense_seqs=dense_seqs)
+    # every unit, sampled or not, satisfies the selection invariants
+    for s in range(w.spec.batch):
+        n = O.pages_of(int(w.seq_lens[s]))
+        b = O.effective_budget(n, int(w.budgets[s]))
+        for g in range(w.spec.num_kv_heads):
+            c = int(res["cnt"][s, g])
+            row = res["sel"][s, g, :c]
+            assert c == min(n, b) and row[0] == 0 and row[-1] == n - 1
+            assert np.all(np.diff(row) > 0)
+
+
+def test_long_1m_dense_sampled_heads():
+    w = synth.make_workload("long_1m")
+    res = run_gpu(w)
+    inp = synth.oracle_inputs(w)
+    L = int(w.seq_lens[0])
+    every = np.arange(O.pages_of(L))
+    for g in (0, 7):
+        keys = O.gather_tokens(inp["k_cache"], w.block_table[0], L, every, g, 128)
+        vals = O.gather_tokens(inp["v_cache"], w.block_table[0], L, every, g, 128)
+        ref = O.attend(inp["q"][0, 4 * g:4 * g + 4], keys, vals, w.scale)
+        err = float(np.max(np.abs(res["dense"][0, 4 * g:4 * g + 4] - ref)))
+        print(f"[ok] long_1m dense head group {g}: max abs err {err:.2e}", flush=True)
+        assert err <= ATOL
