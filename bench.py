@@ -1,0 +1,217 @@
+"""Benchmark: page-selected sparse decode attention steps/s on one MI355X.
+
+A step is one layer's decode for the whole batch through the three C-ABI calls:
+page_meta_update (tail page) -> select_pages -> sparse_decode. The default workload is the
+ragged batch: B=32 sequences of 16K..32K tokens, 32 query / 8 KV heads, D=128, bf16,
+5% page budget (sink and tail included). Inputs are resident in HBM before timing; steps
+rotate over --rotate device copies of (cache, statistics, q) so that consecutive steps
+do not hit in the last-level cache.
+
+Prints one JSON line. Besides the contract fields it carries:
+  roofline      achieved algorithmic GB/s of the dominant kernel against 8 TB/s
+  cpu_baseline  the fp64 oracle's step on the host, on a bounded sample of sequences
+  calls         per-call average durations (HIP events on the launch stream)
+  dense         the dense baseline (psd_dense_decode) on the same inputs
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse decode attn steps/s + effective HBM GB/s (% peak), B=32 @32K ctx"
+
+
+def algorithmic_bytes(w, sel_counts: np.ndarray) -> dict:
+    """Bytes each call must move at minimum (reads + writes), from the workload and the
+    selection sizes: statistics of the scored pages, K/V of the kept pages' valid tokens,
+    q, block-table entries, the tail-page refresh and the outputs."""
+    sp = w.spec
+    es = 2 if sp.dtype == "bf16" else 4
+    B, Hq, Hkv, D, Dv = sp.batch, sp.num_q_heads, sp.num_kv_heads, sp.head_dim, sp.head_dim_v
+    lens = w.seq_lens.astype(np.int64)
+    n = (lens + 15) // 16
+    tail_valid = lens - 16 * (n - 1)
+    meta_b = int(np.sum(tail_valid * Hkv * D * es + 2 * Hkv * D * es + 8))  # K tail + stats
+    scored = np.where(n > w.budgets, n - 2, 0)  # pages whose bound is computed
+    b_max = int(w.budgets.max())
+    select_b = int(np.sum(scored) * (Hkv * 2 * D * es + 4) + B * Hq * D * es +
+                   B * Hkv * (b_max + 1) * 4 + B * 8)
+    # valid tokens: every kept page is full except the tail page (always kept)
+    kv_tok_valid = int(np.sum(sel_counts.sum(axis=1) * 16 - Hkv * (16 - tail_valid)))
+    kdim = D + (0 if sp.latent else Dv)  # latent rows are read once for K and V
+    sparse_b = int(kv_tok_valid * kdim * es + B * Hq * D * es +
+                   int(sel_counts.sum()) * 8 + B * Hq * Dv * 4)
+    dense_tok = int(np.sum(lens)) * Hkv
+    dense_b = int(dense_tok * kdim * es + int(np.sum(n)) * 4 + B * Hq * D * es + B * Hq * Dv * 4)
+    return dict(meta_update=meta_b, select=select_b, sparse_decode=sparse_b,
+                step=meta_b + select_b + sparse_b, dense_decode=dense_b,
+                score_stats=int(np.sum(scored) * Hkv * 2 * D * es))
+
+
+def cpu_baseline(w, budget_s: float = 15.0) -> dict:
+    """Time the fp64 oracle's decode step (tail refresh, bound, selection, attention) on
+    as many sequences as fit in ~budget_s, with BLAS pinned to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import psd_oracle as O
+
+    inp = synth.oracle_inputs(w)
+    Hkv = w.spec.num_kv_heads
+    total, done = 0.0, 0
+    with threadpool_limits(limits=1):
+        for s in range(w.spec.batch):
+            L = int(w.seq_lens[s])
+            n = O.pages_of(L)
+            kmin, kmax = O.sequence_meta(inp["k_cache"], w.block_table[s], L)  # prefill, untimed
+            t0 = time.perf_counter()
+            tail = inp["k_cache"][w.block_table[s, n - 1: n]][0, : O.valid_in_page(L, n - 1)]
+            kmin[n - 1], kmax[n - 1] = O.page_minmax(tail)
+            sel, _ = O.select_sequence(inp["q"][s], kmin, kmax, Hkv, n, int(w.budgets[s]))
+            O.decode_sequence(inp["q"][s], inp["k_cache"], inp["v_cache"], w.block_table[s], L,
+                              sel, w.scale, w.spec.head_dim_v)
+            total += time.perf_counter() - t0
+            done += 1
+            if total >= budget_s:
+                break
+    per_step = total / done * w.spec.batch
+    return {"value": round(1.0 / per_step, 6), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.spec.batch} sequences of the {w.spec.name} step "
+                      f"({total:.1f} s of fp64 NumPy on one thread), scaled to the full batch"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="ragged_b32_32k")
+    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from page_selected_sparse_amd import DecodeStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    w = synth.make_workload(args.workload)
+    print(f"[bench] workload {w.spec.name} generated in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    base = DecodeStep.from_arrays(w.q, w.cache, w.block_table, w.seq_lens, w.budgets,
+                                  w.spec.dtype, w.spec.head_dim_v, w.spec.latent, device=dev)
+    steps = [base]
+    for _ in range(args.rotate - 1):
+        steps.append(DecodeStep(base.q.clone(), base.cache.clone(), base.block_table.clone(),
+                                base.seq_lens.clone(), base.budgets.clone(), w.spec.head_dim_v,
+                                w.spec.latent, b_max=base.b_max))
+    for st in steps:
+        st.build_meta()
+    torch.cuda.synchronize()
+    R = len(steps)
+
+    def timed(fn, iters):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            fn(steps[i % R])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters  # ms
+
+    for i in range(args.warmup):
+        steps[i % R].step()
+        if not args.no_dense:
+            steps[i % R].dense()
+    torch.cuda.synchronize()
+
+    # The measured region: K whole steps, rotating copies.
+    ms_step = timed(lambda st: st.step(), args.steps)
+
+    # Per-call averages (each call timed in its own loop on the launch stream).
+    calls = {"page_meta_update": timed(lambda st: st.refresh_tail(), args.steps),
+             "select_pages": timed(lambda st: st.select(), args.steps),
+             "sparse_decode": timed(lambda st: st.sparse(), args.steps)}
+    dense_ms = timed(lambda st: st.dense(), max(10, args.steps // 4)) if not args.no_dense else None
+
+    if args.calibrate_copy:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+
+    sel_counts = steps[0].sel_count.cpu().numpy()
+    ab = algorithmic_bytes(w, sel_counts)
+    # Dominant call of the step and its achieved algorithmic bandwidth.
+    dom = max(("select_pages", "sparse_decode"), key=lambda k: calls[k])
+    dom_bytes = ab["select"] if dom == "select_pages" else ab["sparse_decode"]
+    achieved = dom_bytes / (calls[dom] * 1e-3) / 1e9
+    step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_step, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.spec.name, "batch": w.spec.batch,
+                   "seq_lens": f"uniform [{w.spec.len_range[0]}, {w.spec.len_range[1]}]"
+                   if w.spec.len_range else list(map(int, w.seq_lens[:1])),
+                   "q_heads": w.spec.num_q_heads, "kv_heads": w.spec.num_kv_heads,
+                   "head_dim": w.spec.head_dim, "page": 16,
+                   "budget": f"{w.spec.budget_percent}% of pages" if w.spec.budget_percent
+                   else f"{w.spec.budget_pages} pages",
+                   "rotated_copies": R},
+        "effective_hbm_gbs": round(step_gbs, 1),
+        "effective_hbm_pct_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "calls_ms": {k: round(v, 5) for k, v in calls.items()},
+        "algorithmic_bytes": ab,
+    }
+    if dense_ms is not None:
+        result["dense"] = {"ms": round(dense_ms, 5),
+                           "gbs": round(ab["dense_decode"] / (dense_ms * 1e-3) / 1e9, 1),
+                           "step_speedup_vs_dense": round(dense_ms / ms_step, 3)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

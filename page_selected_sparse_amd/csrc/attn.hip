@@ -37,7 +37,7 @@ struct AttnArgs {
   const int32_t* cnt;
   float* pacc;  // [B, Hq, nsplit, Dv]
   float2* pml;  // [B, Hq, nsplit]
-  int Hq, Hkv, G, max_pages, b_max, pps, nsplit;
+  int Hq, Hkv, G, max_pages, b_max, pps, nsplit, num_blocks;
   int64_t kbs, kts, khs, vbs, vts, vhs;
   float sl2;  // scale * log2(e)
 };
@@ -99,8 +99,9 @@ __device__ __forceinline__ void load_frag8(const void* base, int64_t off, uint4&
   }
 }
 
-template <bool BF16, int DQK, int DV>
-__global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
+template <bool BF16, int DQK, int DV, int WAVES, int MIN_WAVES_PER_SIMD>
+__global__ __launch_bounds__(64 * WAVES)
+__attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnArgs a) {
   constexpr int NQ = DQK / 32;   // QK MFMAs per page (K = 32 dims each)
   constexpr int NC = DV / 16;    // PV MFMAs per page (16 output columns each)
   static_assert(NC % 4 == 0, "Dv must be a multiple of 64");
@@ -117,11 +118,14 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   if (p0 >= count) return;
   const int np = min(a.pps, count - p0);
 
-  // Page list of this split: lane i holds entry p0 + i.
+  // Page list of this split: lane i holds entry p0 + i. Entries are clamped to the
+  // sequence's pages so that a malformed list can never address outside the table.
   int my_lp = 0, my_blk = 0;
   if (lane < np) {
     my_lp = a.sel ? a.sel[(int64_t)(s * a.Hkv + g) * a.b_max + p0 + lane] : p0 + lane;
+    my_lp = min(max(my_lp, 0), n - 1);
     my_blk = a.bt[(int64_t)s * a.max_pages + my_lp];
+    my_blk = min(max(my_blk, 0), a.num_blocks - 1);
   }
 
   // Q tile as the B operand of S^T = K Q^T: lane holds head r, dims 32c + 8grp .. +8.
@@ -143,18 +147,70 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
 
+  // Raw fragments of one page: K row r at dims 32c + 8grp (A operand of S^T = K Q^T) and
+  // V rows 4grp + j at columns r*NC + w*CW (B operand of O += P V). For D <= 128 all of a
+  // page's K and V loads are issued together at the start of the page; for the wide
+  // latent rows they are streamed next to the MFMAs that use them (register budget).
+  constexpr int CW = (BF16 && NC >= 8) ? 8 : 4;  // V columns per load group
+  constexpr int NG = NC / CW;
+  constexpr bool EARLY = DQK <= 128;
+  auto load_k = [&](int blk, int c, uint4& k0, uint4& k1) {
+    const int64_t off = (int64_t)blk * a.kbs + (int64_t)r * a.kts + (int64_t)g * a.khs +
+                        32 * c + 8 * grp;
+    if constexpr (BF16) {
+      k0 = load16(static_cast<const uint16_t*>(a.k) + off);
+    } else {
+      k0 = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.k) + off);
+      k1 = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.k) + off + 4);
+    }
+  };
+  auto load_v = [&](int blk, int w, int j) -> uint4 {
+    const int64_t off = (int64_t)blk * a.vbs + (int64_t)g * a.vhs + (int64_t)r * NC +
+                        (int64_t)(4 * grp + j) * a.vts + w * CW;
+    if constexpr (BF16 && CW == 8) {
+      return load16(static_cast<const uint16_t*>(a.v) + off);
+    } else if constexpr (BF16) {
+      const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + off);
+      return make_uint4(x.x, x.y, 0u, 0u);
+    } else {
+      return *reinterpret_cast<const uint4*>(static_cast<const float*>(a.v) + off);
+    }
+  };
+
   for (int i = 0; i < np; ++i) {
     const int lp = __builtin_amdgcn_readlane(my_lp, i);
     const int blk = __builtin_amdgcn_readlane(my_blk, i);
     const int valid = min(kPage, L - lp * kPage);  // tokens of this page before L
 
+    uint4 kr[EARLY ? NQ : 1][2], vr[EARLY ? NG : 1][4];
+    if constexpr (EARLY) {
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) load_k(blk, c, kr[c][0], kr[c][1]);
+#pragma unroll
+      for (int w = 0; w < NG; ++w)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vr[w][j] = load_v(blk, w, j);
+    }
+
     // ---- S^T = K Q^T -------------------------------------------------------------------
-    const int64_t krow = (int64_t)blk * a.kbs + (int64_t)r * a.kts + (int64_t)g * a.khs;
     float4v sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-      uint4 khi, klo, qh, ql;
-      load_frag8<BF16>(a.k, krow + 32 * c + 8 * grp, khi, klo);
+      uint4 x0, x1, khi, klo, qh, ql;
+      if constexpr (EARLY) {
+        x0 = kr[c][0];
+        x1 = kr[c][1];
+      } else {
+        load_k(blk, c, x0, x1);
+      }
+      if constexpr (BF16) {
+        khi = x0;
+      } else {
+        const float x[8] = {__uint_as_float(x0.x), __uint_as_float(x0.y), __uint_as_float(x0.z),
+                            __uint_as_float(x0.w), __uint_as_float(x1.x), __uint_as_float(x1.y),
+                            __uint_as_float(x1.z), __uint_as_float(x1.w)};
+        split8(x, khi, klo);
+      }
       if constexpr (QREG) {
         qh = qhi[c];
         ql = qlo[c];
@@ -176,7 +232,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       const int t = 4 * grp + j;
       z[j] = t < valid ? sacc[j] * a.sl2 : -INFINITY;
     }
-    float m_loc = wave_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    const float m_loc = wave_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
     const float m_new = fmaxf(m_run, m_loc);
     const bool live = m_new != -INFINITY;
     const float alpha = live ? exp2f(m_run - m_new) : 1.f;
@@ -206,35 +262,29 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
       for (int j = 0; j < 4; ++j) acc[c][j] *= al[j];
     }
 
-    // ---- O += P V: lane loads V[token 4grp + j][r*NC .. r*NC + NC) -----------------------
-    const int64_t vrow = (int64_t)blk * a.vbs + (int64_t)g * a.vhs + (int64_t)r * NC;
+    // ---- O += P V ------------------------------------------------------------------------
     const bool tail = valid < kPage;
-    constexpr int CW = (BF16 && NC >= 8) ? 8 : 4;  // columns per load group
-    constexpr int NG = NC / CW;
 #pragma unroll
     for (int w = 0; w < NG; ++w) {
       uint32_t vh[4][4], vl[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int t = 4 * grp + j;
-        const int64_t off = vrow + (int64_t)t * a.vts + w * CW;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) vh[j][x] = vl[j][x] = 0u;
-        if (!tail || t < valid) {
-          if constexpr (BF16 && CW == 8) {
-            const uint4 x4 = load16(static_cast<const uint16_t*>(a.v) + off);
-            vh[j][0] = x4.x; vh[j][1] = x4.y; vh[j][2] = x4.z; vh[j][3] = x4.w;
-          } else if constexpr (BF16) {
-            const uint2 x2 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + off);
-            vh[j][0] = x2.x; vh[j][1] = x2.y;
-          } else {
-            const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + off);
-            const float xs[8] = {f.x, f.y, f.z, f.w, 0.f, 0.f, 0.f, 0.f};
-            uint4 hh, ll;
-            split8(xs, hh, ll);
-            vh[j][0] = hh.x; vh[j][1] = hh.y;
-            vl[j][0] = ll.x; vl[j][1] = ll.y;
-          }
+        uint4 x;
+        if constexpr (EARLY) {
+          x = vr[w][j];
+        } else {
+          x = load_v(blk, w, j);
+        }
+        if (tail && 4 * grp + j >= valid) x = make_uint4(0u, 0u, 0u, 0u);  // unwritten slots
+        if constexpr (BF16) {
+          vh[j][0] = x.x; vh[j][1] = x.y; vh[j][2] = x.z; vh[j][3] = x.w;
+        } else {
+          const float xs[8] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                               __uint_as_float(x.w), 0.f, 0.f, 0.f, 0.f};
+          uint4 hh, ll;
+          split8(xs, hh, ll);
+          vh[j][0] = hh.x; vh[j][1] = hh.y; vh[j][2] = 0u; vh[j][3] = 0u;
+          vl[j][0] = ll.x; vl[j][1] = ll.y; vl[j][2] = 0u; vl[j][3] = 0u;
         }
       }
 #pragma unroll
@@ -242,16 +292,16 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
         const int c = w * CW + cc;
         const int wd = cc >> 1;
         const bool hiw = cc & 1;
-        uint32_t e[4], f[4];
+        uint32_t e[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          e[j] = hiw ? (vh[j][wd] >> 16) : (vh[j][wd] & 0xffffu);
-          f[j] = hiw ? (vl[j][wd] >> 16) : (vl[j][wd] & 0xffffu);
-        }
+        for (int j = 0; j < 4; ++j) e[j] = hiw ? (vh[j][wd] >> 16) : (vh[j][wd] & 0xffffu);
         const short4v Vb = as_short4(pack2(e[0], e[1]), pack2(e[2], e[3]));
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ph, Vb, acc[c], 0, 0, 0);
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Pl, Vb, acc[c], 0, 0, 0);
         if constexpr (!BF16) {
+          uint32_t f[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) f[j] = hiw ? (vl[j][wd] >> 16) : (vl[j][wd] & 0xffffu);
           const short4v Vl = as_short4(pack2(f[0], f[1]), pack2(f[2], f[3]));
           acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ph, Vl, acc[c], 0, 0, 0);
         }
@@ -312,7 +362,16 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
 
 template <bool BF16, int DQK, int DV>
 hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) {
-  hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV>), grid, dim3(64 * waves), 0, st, a);
+  // occupancy target per variant: the smallest register budget that does not spill
+  constexpr int W1 = DQK > 128 ? 1 : (BF16 ? 4 : 2);
+  constexpr int W2 = DQK > 128 ? 1 : 2;
+  if (waves == 1) {
+    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 1, W1>), grid, dim3(64), 0, st, a);
+  } else if (waves == 2) {
+    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 2, W2>), grid, dim3(128), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 8, 1>), grid, dim3(64 * waves), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -323,7 +382,7 @@ bool plan_decode(const Geo& g, int max_pages_attended, DecodePlan* p) {
   p->waves = (g.G + 15) / 16;
   const int64_t units = (int64_t)g.B * g.Hkv;
   // Aim for ~2048 single-wave workgroups (fewer, larger ones for many-head groups).
-  const int64_t target = p->waves > 1 ? 512 : 2048;
+  const int64_t target = p->waves > 1 ? 512 : 8192;
   int64_t pps = (units * max_pages_attended + target - 1) / target;
   const int64_t lo = p->waves > 1 ? 4 : 1;
   pps = pps < lo ? lo : (pps > 64 ? 64 : pps);
@@ -342,7 +401,7 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
   unsigned char* w = static_cast<unsigned char*>(ws);
   AttnArgs a{q, k, v, bt, lens, sel, cnt,
              reinterpret_cast<float*>(w), reinterpret_cast<float2*>(w + p.off_ml),
-             g.Hq, g.Hkv, g.G, g.max_pages, b_max, p.pps, p.nsplit,
+             g.Hq, g.Hkv, g.G, g.max_pages, b_max, p.pps, p.nsplit, g.num_blocks,
              g.kbs, g.kts, g.khs, g.vbs, g.vts, g.vhs, scale * 1.4426950408889634f};
   const dim3 grid(p.nsplit, g.Hkv, g.B);
   hipError_t e;

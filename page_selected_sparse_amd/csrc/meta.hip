@@ -3,10 +3,10 @@
 //
 // One workgroup refreshes one logical page of one sequence for every KV head: the page's
 // K rows for all heads form a [16, H_kv * D] tile whose rows are token-strided, so each
-// thread owns 16 contiguous bytes of a row and walks the page's valid tokens. Loads are
-// coalesced across the workgroup (consecutive threads read consecutive 16-byte pieces of
-// a token row) and each statistic is written once. Min/max are exact, so the values
-// written are key values themselves.
+// thread owns 16 contiguous bytes of a row, requests all 16 rows at once and folds the
+// page's valid tokens. Loads are coalesced across the workgroup (consecutive threads read
+// consecutive 16-byte pieces of a token row) and each statistic is written once. Min/max
+// are exact, so the values written are key values themselves.
 #include "psd_device.h"
 #include "psd_launch.h"
 
@@ -43,27 +43,36 @@ __global__ __launch_bounds__(256) void meta_kernel(MetaArgs a) {
   for (int col = threadIdx.x * VEC; col < cols; col += blockDim.x * VEC) {
     const int h = col / a.D, d = col - h * a.D;
     const int64_t base = (int64_t)blk * a.kbs + (int64_t)h * a.khs + d;
-    float mn[VEC], mx[VEC];
-    for (int t = 0; t < valid; ++t) {
-      float v[VEC];
+    // all 16 token rows are requested at once; rows past the length are not used
+    float v[kPage][VEC];
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+      const int tt = t < valid ? t : 0;
       if constexpr (BF16) {
-        const uint4 w = load16(static_cast<const uint16_t*>(a.k) + base + (int64_t)t * a.kts);
+        const uint4 w = load16(static_cast<const uint16_t*>(a.k) + base + (int64_t)tt * a.kts);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[2 * i] = bf_lo(ws[i]);
-          v[2 * i + 1] = bf_hi(ws[i]);
+          v[t][2 * i] = bf_lo(ws[i]);
+          v[t][2 * i + 1] = bf_hi(ws[i]);
         }
       } else {
-        const float4 w =
-            *reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + base +
-                                             (int64_t)t * a.kts);
-        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + base +
+                                                          (int64_t)tt * a.kts);
+        v[t][0] = w.x; v[t][1] = w.y; v[t][2] = w.z; v[t][3] = w.w;
       }
+    }
+    float mn[VEC], mx[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        mn[i] = (t == 0 || v[i] < mn[i]) ? v[i] : mn[i];
-        mx[i] = (t == 0 || v[i] > mx[i]) ? v[i] : mx[i];
+    for (int i = 0; i < VEC; ++i) mn[i] = mx[i] = v[0][i];
+#pragma unroll
+    for (int t = 1; t < kPage; ++t) {
+      if (t < valid) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          mn[i] = v[t][i] < mn[i] ? v[t][i] : mn[i];
+          mx[i] = v[t][i] > mx[i] ? v[t][i] : mx[i];
+        }
       }
     }
     const int64_t mrow = ((int64_t)blk * a.Hkv + h) * 2 * a.D + d;

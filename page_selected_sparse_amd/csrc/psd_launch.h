@@ -20,14 +20,18 @@ hipError_t launch_meta_update(const Geo& g, const void* k, void* meta, const int
 // ---- selection --------------------------------------------------------------------------
 // Chunking of the candidate pages 1..n-2 of a unit for the two-level top-b.
 struct SelectPlan {
-  int chunk;       // candidate pages per scoring workgroup (256 * pages_per_thread)
+  int chunk;       // candidate pages per scoring workgroup (threads * pages_per_thread)
+  int threads;     // threads per scoring workgroup
   int ppt;         // pages per thread
   int nchunk;      // chunks covering max_pages - 2 candidates
   int cap;         // candidate slots per chunk = min(chunk, b_max - 2)
   int head_block;  // query heads scored per pass (template width)
-  int d_chunk;     // dims of q staged in LDS per pass
-  size_t off_idx, off_cnt, bytes;  // workspace layout
-  size_t merge_lds;                // dynamic LDS of the merge kernel
+  int d_chunk;     // dims of q staged in LDS per pass (LDS q path)
+  bool qtab;       // (q+, q-) from an fp64 table in the workspace via scalar loads
+  bool fused;      // the last chunk workgroup of a unit merges (no merge kernel)
+  size_t off_idx, off_cnt, off_arrive, off_qtab, bytes;  // workspace layout
+  size_t merge_lds;  // LDS of a unit merge
+  size_t score_lds;  // dynamic LDS of the scoring kernel
 };
 // Returns false when no plan fits (b_max too large).
 bool plan_select(const Geo& g, int b_max, SelectPlan* plan);

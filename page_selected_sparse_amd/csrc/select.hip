@@ -37,33 +37,29 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMergeCap = 8192;  // candidates one merge workgroup holds in LDS
 constexpr int kMaxChunks = 1024;  // chunks per unit
+constexpr int kFusedCap = 2048;   // candidates the last chunk workgroup merges in LDS
 
-struct ScoreArgs {
+// Everything the three selection kernels need; device pointers into the caller's
+// buffers and the select workspace.
+struct SelArgs {
   const void* q;
   const void* meta;
   const int32_t* bt;
   const int32_t* lens;
   const int32_t* budgets;
-  uint64_t* ckey;
-  int32_t* cidx;
-  int32_t* ccnt;
-  int Hq, Hkv, G, max_pages, chunk, ppt, nchunk, cap;
-};
-
-struct MergeArgs {
-  const int32_t* lens;
-  const int32_t* budgets;
-  const uint64_t* ckey;
-  const int32_t* cidx;
-  const int32_t* ccnt;
+  uint64_t* ckey;    // [unit][nchunk][cap] chunk candidates (order-preserving keys)
+  int32_t* cidx;     // [unit][nchunk][cap] their logical pages
+  int32_t* ccnt;     // [unit][nchunk] candidates written per chunk
+  uint32_t* arrive;  // [unit] chunks done (fused merge)
+  double2* qtab;     // [unit][D][HB] (q+, q-) in fp64 (single-pass plans)
   int32_t* sel;
   int32_t* cnt;
-  int Hkv, b_max, chunk, nchunk, cap;
+  int Hq, Hkv, G, D, max_pages, b_max, chunk, ppt, nchunk, cap, fused;
 };
 
 struct SelScratch {
   uint32_t hist[256];
-  int wave_cnt[4];
+  int wave_cnt[16];
   int digit, k;
 };
 
@@ -78,17 +74,23 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 }
 
 // Exclusive count of `flag` over the threads before this one (thread order), and the
-// total, for a 256-thread workgroup. Contains barriers: every thread must call it.
+// total, for an NT-thread workgroup. Contains barriers: every thread must call it.
+template <int NT>
 __device__ __forceinline__ int block_excl_count(bool flag, SelScratch& sc, int& total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t m = __ballot(flag);
   const int below = __popcll(m & ((1ull << lane) - 1ull));
+  if constexpr (NW == 1) {
+    total = __popcll(m);
+    return below;
+  }
   if (lane == 0) sc.wave_cnt[w] = __popcll(m);
   __syncthreads();
   int off = 0;
   total = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int c = sc.wave_cnt[i];
     off += i < w ? c : 0;
     total += c;
@@ -100,16 +102,17 @@ __device__ __forceinline__ int block_excl_count(bool flag, SelScratch& sc, int& 
 // K-th largest (1-based) of keys[0..N) in LDS, 1 <= K <= N. Returns the key T and how
 // many of the keys equal to T belong to the top K. Radix select over 8-bit digits from
 // the most significant; equal digits met in a row by one thread are counted once.
+template <int NT>
 __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch& sc,
                                   uint64_t& T, int& need) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0, mask = 0;
   int k = K;
   for (int shift = 56; shift >= 0; shift -= 8) {
-    sc.hist[tid] = 0;
+    for (int i = tid; i < 256; i += NT) sc.hist[i] = 0;
     __syncthreads();
     int run_d = -1, run_c = 0;
-    for (int i = tid; i < N; i += kThreads) {
+    for (int i = tid; i < N; i += NT) {
       const uint64_t key = keys[i];
       if ((key & mask) == prefix) {
         const int dg = (int)((key >> shift) & 255u);
@@ -161,19 +164,19 @@ __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch
 
 // Emits, in position order, every key > T and the first `need` keys == T; calls
 // out(rank, position) for each. Returns the number emitted. Every thread must call it.
-template <typename Out>
+template <int NT, typename Out>
 __device__ int block_emit_top(const uint64_t* keys, int N, uint64_t T, int need, SelScratch& sc,
                               Out out) {
   int run_eq = 0, run_out = 0;
-  for (int base = 0; base < N; base += kThreads) {
+  for (int base = 0; base < N; base += NT) {
     const int i = base + threadIdx.x;
     const bool ok = i < N;
     const uint64_t key = ok ? keys[i] : 0;
     const bool gt = ok && key > T, eq = ok && key == T;
     int tot_eq, tot_sel;
-    const int eq_rank = run_eq + block_excl_count(eq, sc, tot_eq);
+    const int eq_rank = run_eq + block_excl_count<NT>(eq, sc, tot_eq);
     const bool pick = gt || (eq && eq_rank < need);
-    const int pos = run_out + block_excl_count(pick, sc, tot_sel);
+    const int pos = run_out + block_excl_count<NT>(pick, sc, tot_sel);
     if (pick) out(pos, i);
     run_eq += tot_eq;
     run_out += tot_sel;
@@ -190,21 +193,176 @@ __device__ __forceinline__ double q_value(const void* q, int64_t idx) {
   }
 }
 
-// Bound contribution of dims [d0, d0 + DC) of one page for HB heads, ascending d.
+
+// Unit status shared by the three kernels: pages n, effective budget b, free slots kp.
+struct UnitInfo {
+  int n, b, kp;
+  bool trivial;  // no ranking needed (all pages, sink + tail only, or over capacity)
+};
+
+__device__ __forceinline__ UnitInfo unit_info(const SelArgs& a, int s) {
+  UnitInfo u;
+  u.n = ceil_div(a.lens[s], kPage);
+  u.b = effective_budget(u.n, a.budgets[s]);
+  u.kp = u.b - 2;
+  u.trivial = u.n <= u.b || u.kp <= 0 || u.b > a.b_max;
+  return u;
+}
+
+// Prepares a call: the fp64 (q+, q-) table of every unit, zeroed arrival counters, and
+// every selection row except the ranked winners (sink, tail, padding and count; the whole
+// row for units that need no ranking; -1 rows for units over capacity).
+template <bool BF16, int HB, bool QTAB>
+__global__ __launch_bounds__(kThreads) void prep_kernel(SelArgs a) {
+  const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int unit = s * a.Hkv + g;
+  if constexpr (QTAB) {
+    double2* qt = a.qtab + (int64_t)unit * a.D * HB;
+    for (int e = tid; e < a.D * HB; e += kThreads) {
+      const int d = e / HB, h = e - d * HB;
+      double qv = 0.0;
+      if (h < a.G) qv = q_value<BF16>(a.q, ((int64_t)s * a.Hq + g * a.G + h) * a.D + d);
+      qt[e] = make_double2(qv >= 0.0 ? qv : 0.0, qv >= 0.0 ? 0.0 : qv);
+    }
+  }
+  if (tid == 0 && a.fused) a.arrive[unit] = 0u;
+  const UnitInfo u = unit_info(a, s);
+  int32_t* row = a.sel + (int64_t)unit * a.b_max;
+  if (u.b > a.b_max) {  // never truncate: flag the unit
+    for (int i = tid; i < a.b_max; i += kThreads) row[i] = -1;
+    if (tid == 0) a.cnt[unit] = -1;
+    return;
+  }
+  if (u.n <= u.b) {
+    for (int i = tid; i < a.b_max; i += kThreads) row[i] = i < u.n ? i : -1;
+    if (tid == 0) a.cnt[unit] = u.n;
+    return;
+  }
+  for (int i = u.b + tid; i < a.b_max; i += kThreads) row[i] = -1;
+  if (tid == 0) {
+    a.cnt[unit] = u.b;
+    row[0] = 0;
+    row[u.b - 1] = u.n - 1;
+  }
+}
+
+// Element j of a 64-byte chunk held as four 16-byte vectors, widened exactly to fp64.
+template <bool BF16>
+__device__ __forceinline__ double chunk_elem(const uint4* v, int j) {
+  if constexpr (BF16) {
+    const uint4 w = v[j >> 3];
+    const int k = (j >> 1) & 3;
+    const uint32_t word = k == 0 ? w.x : (k == 1 ? w.y : (k == 2 ? w.z : w.w));
+    return (double)((j & 1) ? bf_hi(word) : bf_lo(word));
+  } else {
+    const uint4 w = v[j >> 2];
+    const int k = j & 3;
+    return (double)__uint_as_float(k == 0 ? w.x : (k == 1 ? w.y : (k == 2 ? w.z : w.w)));
+  }
+}
+
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+
+// 64 bytes of a wave-uniform table into SGPRs. The value may only be used after
+// smem_wait(); the wait redefines it, so no use can be scheduled above the wait.
+__device__ __forceinline__ u32x16 smem_load64(const void* base, uint32_t byte_off) {
+  u32x16 v;
+  asm volatile("s_load_dwordx16 %0, %1, %2" : "=s"(v) : "s"(base), "s"(byte_off));
+  return v;
+}
+__device__ __forceinline__ void smem_wait(u32x16& v) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v));
+}
+__device__ __forceinline__ double sgpr_f64(const u32x16& v, int i) {
+  return __builtin_bit_cast(double, ((uint64_t)v[2 * i + 1] << 32) | v[2 * i]);
+}
+
+// Bound of one page for HB heads with (q+, q-) read from the unit's fp64 table, which
+// is wave-uniform: it is loaded into SGPRs, 64 bytes (4 heads) per load, one dim ahead,
+// and used directly as the fp64 FMA operand. The page's min/max rows are read in
+// 64-byte chunks, the next chunk in flight while the current one is accumulated. The
+// dims ascend.
+template <bool BF16, int D, int HB>
+__device__ __forceinline__ void bound_qtab(const void* meta, int64_t row,
+                                           const double2* __restrict__ qt, double* acc) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int CH = 64 / ES;  // dims per chunk
+  constexpr int NCH = D / CH;
+  constexpr int NQ = HB / 4;   // 64-byte q loads per dim
+  constexpr bool PREF = NQ <= 2;  // double-buffer the q loads when the SGPRs allow
+  const unsigned char* mn = static_cast<const unsigned char*>(meta) + row * ES;
+  const unsigned char* mx = mn + D * ES;
+  uint4 cur[8], nxt[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cur[i] = *reinterpret_cast<const uint4*>(mn + 16 * i);
+    cur[4 + i] = *reinterpret_cast<const uint4*>(mx + 16 * i);
+  }
+  u32x16 qa[NQ], qb[NQ];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) qa[k] = smem_load64(qt, 64 * k);
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) smem_wait(qa[k]);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c + 1 < NCH) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        nxt[i] = *reinterpret_cast<const uint4*>(mn + 64 * (c + 1) + 16 * i);
+        nxt[4 + i] = *reinterpret_cast<const uint4*>(mx + 64 * (c + 1) + 16 * i);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int d = c * CH + j;
+      const bool more = PREF && d + 1 < D;
+      if (more) {  // next dim's q in flight while this dim is accumulated
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) qb[k] = smem_load64(qt, (d + 1) * HB * 16 + 64 * k);
+      } else if (!PREF && d > 0) {  // 16 heads: no SGPRs left for a second buffer
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) qa[k] = smem_load64(qt, d * HB * 16 + 64 * k);
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) smem_wait(qa[k]);
+      }
+      const double kmn = chunk_elem<BF16>(cur, j), kmx = chunk_elem<BF16>(cur + 4, j);
+#pragma unroll
+      for (int h = 0; h < HB; ++h) {
+        const double qp = sgpr_f64(qa[h >> 2], 2 * (h & 3));
+        const double qn = sgpr_f64(qa[h >> 2], 2 * (h & 3) + 1);
+        acc[h] = __builtin_fma(qp, kmx, acc[h]);
+        acc[h] = __builtin_fma(qn, kmn, acc[h]);
+      }
+      if (more) {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+          smem_wait(qb[k]);
+          qa[k] = qb[k];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep each dim's loads next to its FMAs
+    }
+    if (c + 1 < NCH) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
+    }
+  }
+}
+
+// Bound contribution of dims [0, DC) of one page row segment for HB heads, with the
+// (q+, q-) table for those dims staged in LDS (many-head groups), ascending d.
 template <bool BF16, int DC, int HB>
-__device__ __forceinline__ void accumulate_bound(const void* meta, int64_t row, int D,
-                                                 const double2* qt, double* acc) {
+__device__ __forceinline__ void bound_lds(const void* meta, int64_t row, int D,
+                                          const double2* qt, double* acc) {
   if constexpr (BF16) {
     const uint16_t* mn = static_cast<const uint16_t*>(meta) + row;
     const uint16_t* mx = mn + D;
 #pragma unroll
     for (int d0 = 0; d0 < DC; d0 += 8) {
-      const uint4 a = load16(mn + d0), b = load16(mx + d0);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+      const uint4 av = load16(mn + d0), bv = load16(mx + d0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const double kmn = (double)((j & 1) ? bf_hi(aw[j >> 1]) : bf_lo(aw[j >> 1]));
-        const double kmx = (double)((j & 1) ? bf_hi(bw[j >> 1]) : bf_lo(bw[j >> 1]));
+        const double kmn = chunk_elem<true>(&av, j), kmx = chunk_elem<true>(&bv, j);
 #pragma unroll
         for (int h = 0; h < HB; ++h) {
           const double2 qq = qt[(d0 + j) * HB + h];
@@ -218,12 +376,11 @@ __device__ __forceinline__ void accumulate_bound(const void* meta, int64_t row, 
     const float* mx = mn + D;
 #pragma unroll
     for (int d0 = 0; d0 < DC; d0 += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(mn + d0);
-      const float4 b = *reinterpret_cast<const float4*>(mx + d0);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+      const uint4 av = *reinterpret_cast<const uint4*>(mn + d0);
+      const uint4 bv = *reinterpret_cast<const uint4*>(mx + d0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const double kmn = (double)av[j], kmx = (double)bv[j];
+        const double kmn = chunk_elem<false>(&av, j), kmx = chunk_elem<false>(&bv, j);
 #pragma unroll
         for (int h = 0; h < HB; ++h) {
           const double2 qq = qt[(d0 + j) * HB + h];
@@ -235,127 +392,21 @@ __device__ __forceinline__ void accumulate_bound(const void* meta, int64_t row, 
   }
 }
 
-template <bool BF16, int D, int HB>
-__global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
-  // q table (q+, q-) for HB heads over DC dims; whole D when it fits in 32 KB.
-  constexpr int DC = (HB * D * 16 <= 32768) ? D : 32;
-  constexpr int NDC = D / DC;
-  __shared__ double2 qtab[DC * HB];
-  __shared__ SelScratch sc;
-  extern __shared__ uint64_t keys[];  // [chunk]
-
-  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+// Global top-kp of one unit from its chunk candidate lists (in page order), written to
+// row[1 .. kp] in ascending page order. `lds` holds nchunk * cap keys then indices.
+template <int NT>
+__device__ void merge_unit(const SelArgs& a, int unit, int n, int kp, unsigned char* lds,
+                           int* chunk_off, SelScratch& sc) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
-  const int L = a.lens[s];
-  const int n = ceil_div(L, kPage);
-  const int b = effective_budget(n, a.budgets[s]);
-  if (n <= b) return;  // every page kept; the merge writes them
-  const int kp = b - 2;
-  if (kp <= 0 || kp > a.cap) return;  // kp > cap: budget beyond b_max, the merge flags it
-  const int lo = 1 + c * a.chunk;
-  const int hi = min(lo + a.chunk, n - 1);
-  if (lo >= hi) return;
-  const int cnt = hi - lo;
-  const int unit = s * a.Hkv + g;
-  const int nhp = ceil_div(a.G, HB);
-  const bool once = (nhp == 1 && NDC == 1);
-
-  auto load_qtab = [&](int hp, int dc) {
-    for (int e = tid; e < DC * HB; e += kThreads) {
-      const int d = e / HB, h = e - d * HB, hh = hp * HB + h;
-      double qv = 0.0;
-      if (hh < a.G) qv = q_value<BF16>(a.q, ((int64_t)s * a.Hq + g * a.G + hh) * D + dc * DC + d);
-      qtab[e] = make_double2(qv >= 0.0 ? qv : 0.0, qv >= 0.0 ? 0.0 : qv);
-    }
-  };
-
-  if (once) {
-    load_qtab(0, 0);
-    __syncthreads();
-  }
-  for (int it = 0; it < a.ppt; ++it) {
-    const int o = it * kThreads + tid;
-    const bool have = o < cnt;
-    const int blk = have ? a.bt[(int64_t)s * a.max_pages + lo + o] : 0;
-    const int64_t row = ((int64_t)blk * a.Hkv + g) * 2 * D;
-    double best = -__builtin_inf();
-    for (int hp = 0; hp < nhp; ++hp) {
-      double acc[HB];
-#pragma unroll
-      for (int h = 0; h < HB; ++h) acc[h] = 0.0;
-      for (int dc = 0; dc < NDC; ++dc) {
-        if (!once) {
-          __syncthreads();
-          load_qtab(hp, dc);
-          __syncthreads();
-        }
-        if (have) accumulate_bound<BF16, DC, HB>(a.meta, row + dc * DC, D, qtab, acc);
-      }
-#pragma unroll
-      for (int h = 0; h < HB; ++h)
-        if (hp * HB + h < a.G && acc[h] > best) best = acc[h];
-    }
-    if (have) keys[o] = score_key(best);
-  }
-  __syncthreads();
-
-  uint64_t* okey = a.ckey + ((int64_t)unit * a.nchunk + c) * a.cap;
-  int32_t* oidx = a.cidx + ((int64_t)unit * a.nchunk + c) * a.cap;
-  if (cnt <= kp) {
-    for (int o = tid; o < cnt; o += kThreads) {
-      okey[o] = keys[o];
-      oidx[o] = lo + o;
-    }
-    if (tid == 0) a.ccnt[(int64_t)unit * a.nchunk + c] = cnt;
-    return;
-  }
-  uint64_t T;
-  int need;
-  block_kth_largest(keys, cnt, kp, sc, T, need);
-  const int emitted = block_emit_top(keys, cnt, T, need, sc, [&](int pos, int i) {
-    okey[pos] = keys[i];
-    oidx[pos] = lo + i;
-  });
-  if (tid == 0) a.ccnt[(int64_t)unit * a.nchunk + c] = emitted;
-}
-
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  __shared__ SelScratch sc;
-  __shared__ int chunk_off[kMaxChunks + 1];
-  extern __shared__ unsigned char lds[];
-  const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
-  const int unit = s * a.Hkv + g;
-  const int L = a.lens[s];
-  const int n = ceil_div(L, kPage);
-  const int b = effective_budget(n, a.budgets[s]);
   int32_t* row = a.sel + (int64_t)unit * a.b_max;
-  if (b > a.b_max) {  // never truncate: flag the unit
-    for (int i = tid; i < a.b_max; i += kThreads) row[i] = -1;
-    if (tid == 0) a.cnt[unit] = -1;
-    return;
-  }
-  if (n <= b) {
-    for (int i = tid; i < a.b_max; i += kThreads) row[i] = i < n ? i : -1;
-    if (tid == 0) a.cnt[unit] = n;
-    return;
-  }
-  for (int i = b + tid; i < a.b_max; i += kThreads) row[i] = -1;
-  if (tid == 0) {
-    a.cnt[unit] = b;
-    row[0] = 0;
-    row[b - 1] = n - 1;
-  }
-  const int kp = b - 2;
-  if (kp <= 0) return;
-
-  // Concatenate the chunk candidate lists; chunks are in page order and so is each list.
   const int nch = ceil_div(n - 2, a.chunk);
   uint64_t* keys = reinterpret_cast<uint64_t*>(lds);
   int32_t* idx = reinterpret_cast<int32_t*>(lds + sizeof(uint64_t) * (size_t)a.nchunk * a.cap);
-  for (int c = tid; c < nch; c += kThreads) chunk_off[c] = a.ccnt[(int64_t)unit * a.nchunk + c];
+  for (int c = tid; c < nch; c += NT) chunk_off[c] = a.ccnt[(int64_t)unit * a.nchunk + c];
   __syncthreads();
   int carry = 0;
-  for (int base = 0; base < nch; base += kThreads) {  // exclusive scan of the counts
+  for (int base = 0; base < nch; base += NT) {  // exclusive scan of the counts
     const int c = base + tid;
     const int v = c < nch ? chunk_off[c] : 0;
     const int lane = tid & 63, w = tid >> 6;
@@ -364,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     __syncthreads();
     int off = carry, tot = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NW; ++i) {
       off += i < w ? sc.wave_cnt[i] : 0;
       tot += sc.wave_cnt[i];
     }
@@ -375,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   if (tid == 0) chunk_off[nch] = carry;
   __syncthreads();
   const int total = carry;
-  for (int j = tid; j < nch * a.cap; j += kThreads) {
+  for (int j = tid; j < nch * a.cap; j += NT) {
     const int c = j / a.cap, i = j - c * a.cap;
     const int o = chunk_off[c];
     if (i < chunk_off[c + 1] - o) {
@@ -385,28 +436,177 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     }
   }
   __syncthreads();
-
   uint64_t T;
   int need;
-  block_kth_largest(keys, total, kp, sc, T, need);
-  block_emit_top(keys, total, T, need, sc, [&](int pos, int i) { row[1 + pos] = idx[i]; });
+  block_kth_largest<NT>(keys, total, kp, sc, T, need);
+  block_emit_top<NT>(keys, total, T, need, sc, [&](int pos, int i) { row[1 + pos] = idx[i]; });
+}
+
+template <bool BF16, int D, int HB, bool QTAB, int NT>
+__global__ __launch_bounds__(NT) void score_kernel(SelArgs a, const double2* __restrict__ qtab) {
+  // LDS q table for many-head groups: HB heads over DC dims, whole D when it fits.
+  constexpr int DC = QTAB ? 1 : ((HB * D * 16 <= 32768) ? D : 32);
+  constexpr int NDC = QTAB ? 1 : D / DC;
+  __shared__ double2 qlds[QTAB ? 1 : DC * HB];
+  __shared__ SelScratch sc;
+  __shared__ int chunk_off[kMaxChunks + 1];
+  __shared__ int s_last;
+  extern __shared__ unsigned char lds[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(lds);  // [chunk]
+
+  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x;
+  const UnitInfo u = unit_info(a, s);
+  if (u.trivial) return;  // rows written by prep_kernel
+  const int kp = u.kp, n = u.n;
+  const int lo = 1 + c * a.chunk;
+  const int hi = min(lo + a.chunk, n - 1);
+  if (lo >= hi) return;
+  const int cnt = hi - lo;
+  const int unit = s * a.Hkv + g;
+  const int nhp = ceil_div(a.G, HB);
+  const double2* qt = qtab + (int64_t)unit * D * HB;
+
+  auto load_qlds = [&](int hp, int dc) {
+    for (int e = tid; e < DC * HB; e += NT) {
+      const int d = e / HB, h = e - d * HB, hh = hp * HB + h;
+      double qv = 0.0;
+      if (hh < a.G) qv = q_value<BF16>(a.q, ((int64_t)s * a.Hq + g * a.G + hh) * D + dc * DC + d);
+      qlds[e] = make_double2(qv >= 0.0 ? qv : 0.0, qv >= 0.0 ? 0.0 : qv);
+    }
+  };
+  const bool once = !QTAB && nhp == 1 && NDC == 1;
+  if (once) {
+    load_qlds(0, 0);
+    __syncthreads();
+  }
+  for (int it = 0; it < a.ppt; ++it) {
+    const int o = it * NT + tid;
+    const bool have = o < cnt;
+    const int blk = have ? a.bt[(int64_t)s * a.max_pages + lo + o] : a.bt[(int64_t)s * a.max_pages];
+    const int64_t row = ((int64_t)blk * a.Hkv + g) * 2 * D;
+    double best = -__builtin_inf();
+    if constexpr (QTAB) {
+      double acc[HB];
+#pragma unroll
+      for (int h = 0; h < HB; ++h) acc[h] = 0.0;
+      bound_qtab<BF16, D, HB>(a.meta, row, qt, acc);
+#pragma unroll
+      for (int h = 0; h < HB; ++h)
+        if (h < a.G && acc[h] > best) best = acc[h];
+    } else {
+      for (int hp = 0; hp < nhp; ++hp) {
+        double acc[HB];
+#pragma unroll
+        for (int h = 0; h < HB; ++h) acc[h] = 0.0;
+        for (int dc = 0; dc < NDC; ++dc) {
+          if (!once) {
+            __syncthreads();
+            load_qlds(hp, dc);
+            __syncthreads();
+          }
+          if (have) bound_lds<BF16, DC, HB>(a.meta, row + dc * DC, D, qlds, acc);
+        }
+#pragma unroll
+        for (int h = 0; h < HB; ++h)
+          if (hp * HB + h < a.G && acc[h] > best) best = acc[h];
+      }
+    }
+    // written for every thread (slots past cnt are never read) so that the bound is not
+    // sunk into a branch below the scalar q loads
+    keys[o] = score_key(best);
+  }
+  __syncthreads();
+
+  // Chunk candidates: all pages when they fit in kp, else the chunk's top-kp.
+  uint64_t* okey = a.ckey + ((int64_t)unit * a.nchunk + c) * a.cap;
+  int32_t* oidx = a.cidx + ((int64_t)unit * a.nchunk + c) * a.cap;
+  if (cnt <= kp) {
+    for (int o = tid; o < cnt; o += NT) {
+      okey[o] = keys[o];
+      oidx[o] = lo + o;
+    }
+    if (tid == 0) a.ccnt[(int64_t)unit * a.nchunk + c] = cnt;
+  } else {
+    uint64_t T;
+    int need;
+    block_kth_largest<NT>(keys, cnt, kp, sc, T, need);
+    const int emitted = block_emit_top<NT>(keys, cnt, T, need, sc, [&](int pos, int i) {
+      okey[pos] = keys[i];
+      oidx[pos] = lo + i;
+    });
+    if (tid == 0) a.ccnt[(int64_t)unit * a.nchunk + c] = emitted;
+  }
+  if (!a.fused) return;
+
+  // The last chunk workgroup of the unit to finish merges (release / acquire fences
+  // around the arrival counter make the other chunks' candidates visible).
+  __threadfence();
+  __syncthreads();
+  const int nch = ceil_div(n - 2, a.chunk);
+  if (tid == 0) s_last = atomicAdd(&a.arrive[unit], 1u) == (unsigned)(nch - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  merge_unit<NT>(a, unit, n, kp, lds, chunk_off, sc);
+}
+
+__global__ __launch_bounds__(kThreads) void merge_kernel(SelArgs a) {
+  __shared__ SelScratch sc;
+  __shared__ int chunk_off[kMaxChunks + 1];
+  extern __shared__ unsigned char lds[];
+  const int g = blockIdx.x, s = blockIdx.y;
+  const UnitInfo u = unit_info(a, s);
+  if (u.trivial) return;
+  merge_unit<kThreads>(a, s * a.Hkv + g, u.n, u.kp, lds, chunk_off, sc);
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, size_t lds) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <bool BF16, int D, int HB, bool QTAB, int NT>
+hipError_t launch_all(const SelArgs& a, const SelectPlan& p, dim3 sgrid, size_t slds,
+                      hipStream_t st) {
+  const dim3 ugrid(a.Hkv, sgrid.z);
+  hipLaunchKernelGGL((prep_kernel<BF16, HB, QTAB>), ugrid, dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = set_lds(&score_kernel<BF16, D, HB, QTAB, NT>, slds)) != hipSuccess) return e;
+  hipLaunchKernelGGL((score_kernel<BF16, D, HB, QTAB, NT>), sgrid, dim3(NT), slds, st, a, a.qtab);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!a.fused) {
+    if ((e = set_lds(&merge_kernel, p.merge_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_kernel, ugrid, dim3(kThreads), p.merge_lds, st, a);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <bool BF16, int D, int HB>
-hipError_t launch_score(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_kernel<BF16, D, HB>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((score_kernel<BF16, D, HB>), grid, dim3(kThreads), lds, st, a);
-  return hipGetLastError();
+hipError_t dispatch_nt(const SelArgs& a, const SelectPlan& p, dim3 grid, size_t lds,
+                       hipStream_t st) {
+  switch (p.threads) {
+    case 64: return launch_all<BF16, D, HB, true, 64>(a, p, grid, lds, st);
+    case 256: return launch_all<BF16, D, HB, true, 256>(a, p, grid, lds, st);
+    default: return launch_all<BF16, D, HB, true, 512>(a, p, grid, lds, st);
+  }
 }
 
 template <bool BF16, int D>
-hipError_t dispatch_hb(const ScoreArgs& a, int hb, dim3 grid, size_t lds, hipStream_t st) {
-  switch (hb) {
-    case 4: return launch_score<BF16, D, 4>(a, grid, lds, st);
-    case 8: return launch_score<BF16, D, 8>(a, grid, lds, st);
-    default: return launch_score<BF16, D, 16>(a, grid, lds, st);
+hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, size_t lds,
+                       hipStream_t st) {
+  if constexpr (D > 128) {
+    return launch_all<BF16, D, 16, false, kThreads>(a, p, grid, lds, st);
+  } else {
+    if (!p.qtab) return launch_all<BF16, D, 16, false, kThreads>(a, p, grid, lds, st);
+    switch (p.head_block) {
+      case 4: return dispatch_nt<BF16, D, 4>(a, p, grid, lds, st);
+      case 8: return dispatch_nt<BF16, D, 8>(a, p, grid, lds, st);
+      default: return dispatch_nt<BF16, D, 16>(a, p, grid, lds, st);
+    }
   }
 }
 
@@ -416,14 +616,26 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   if (b_max < 2) return false;
   const int kcap = b_max - 2;
   const int inner = g.max_pages > 2 ? g.max_pages - 2 : 1;
-  p->head_block = g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16);
-  const int hb = p->head_block;
-  const bool multi_pass = (g.G > hb) || (hb * g.D * 16 > 32768);
-  p->d_chunk = (hb * g.D * 16 <= 32768) ? g.D : 32;
+  const int64_t units = (int64_t)g.B * g.Hkv;
+  // Groups of up to 16 heads with D <= 128 read (q+, q-) from an fp64 table through
+  // scalar loads; larger groups stage it in LDS, 16 heads at a time.
+  p->qtab = g.G <= 16 && g.D <= 128;
+  p->head_block = !p->qtab ? 16 : (g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16));
+  p->d_chunk = p->qtab ? g.D : ((16 * g.D * 16 <= 32768) ? g.D : 32);
+  const bool multi_pass = !p->qtab && (g.G > 16 || 16 * g.D * 16 > 32768);
+  // Workgroup size: large workgroups keep the waves resident on a CU on one unit (its q
+  // table stays in the scalar cache); small batches use one-wave workgroups for enough
+  // workgroups in flight.
+  p->threads = kThreads;
+  if (p->qtab) {
+    const int64_t wg512 = units * ((inner + 511) / 512);
+    p->threads = wg512 >= 512 ? 512 : (units * ((inner + 255) / 256) >= 512 ? 256 : 64);
+  }
   bool ok = false;
-  for (int ppt = 1; ppt <= 32; ppt *= 2) {
+  for (int ppt = 1; ppt <= 64; ppt *= 2) {
     if (multi_pass && ppt > 1) break;
-    const int chunk = kThreads * ppt;
+    const int chunk = p->threads * ppt;
+    if (chunk * sizeof(uint64_t) > 65536) break;
     const int nchunk = (inner + chunk - 1) / chunk;
     const int cap = kcap < 1 ? 1 : (kcap < chunk ? kcap : chunk);
     if ((int64_t)nchunk * cap <= kMergeCap && nchunk <= kMaxChunks) {
@@ -436,11 +648,17 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
     }
   }
   if (!ok) return false;
-  const size_t slots = (size_t)g.B * g.Hkv * p->nchunk * p->cap;
-  p->off_idx = slots * sizeof(uint64_t);
-  p->off_cnt = (p->off_idx + slots * sizeof(int32_t) + 255) / 256 * 256;
-  p->bytes = p->off_cnt + (size_t)g.B * g.Hkv * p->nchunk * sizeof(int32_t) + 256;
+  const size_t slots = (size_t)units * p->nchunk * p->cap;
+  p->fused = (size_t)p->nchunk * p->cap <= (size_t)kFusedCap;
   p->merge_lds = (size_t)p->nchunk * p->cap * (sizeof(uint64_t) + sizeof(int32_t));
+  p->score_lds = p->chunk * sizeof(uint64_t);
+  if (p->fused && p->merge_lds > p->score_lds) p->score_lds = p->merge_lds;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  p->off_idx = al(slots * sizeof(uint64_t));
+  p->off_cnt = al(p->off_idx + slots * sizeof(int32_t));
+  p->off_arrive = al(p->off_cnt + units * p->nchunk * sizeof(int32_t));
+  p->off_qtab = al(p->off_arrive + units * sizeof(uint32_t));
+  p->bytes = p->off_qtab + (p->qtab ? units * g.D * p->head_block * 16 : 0) + 256;
   return true;
 }
 
@@ -448,30 +666,22 @@ hipError_t launch_select(const Geo& g, const SelectPlan& p, const void* q, const
                          const int32_t* bt, const int32_t* lens, const int32_t* budgets,
                          int b_max, int32_t* sel, int32_t* cnt, void* ws, hipStream_t st) {
   unsigned char* w = static_cast<unsigned char*>(ws);
-  ScoreArgs sa{q, meta, bt, lens, budgets,
-               reinterpret_cast<uint64_t*>(w), reinterpret_cast<int32_t*>(w + p.off_idx),
-               reinterpret_cast<int32_t*>(w + p.off_cnt),
-               g.Hq, g.Hkv, g.G, g.max_pages, p.chunk, p.ppt, p.nchunk, p.cap};
+  SelArgs a{q, meta, bt, lens, budgets,
+            reinterpret_cast<uint64_t*>(w), reinterpret_cast<int32_t*>(w + p.off_idx),
+            reinterpret_cast<int32_t*>(w + p.off_cnt), reinterpret_cast<uint32_t*>(w + p.off_arrive),
+            reinterpret_cast<double2*>(w + p.off_qtab), sel, cnt,
+            g.Hq, g.Hkv, g.G, g.D, g.max_pages, b_max, p.chunk, p.ppt, p.nchunk, p.cap,
+            p.fused ? 1 : 0};
   const dim3 sgrid(p.nchunk, g.Hkv, g.B);
-  const size_t slds = (size_t)p.chunk * sizeof(uint64_t);
-  hipError_t e;
   const bool bf = g.dtype == 1;
   switch (g.D) {
-    case 64: e = bf ? dispatch_hb<true, 64>(sa, p.head_block, sgrid, slds, st)
-                    : dispatch_hb<false, 64>(sa, p.head_block, sgrid, slds, st); break;
-    case 128: e = bf ? dispatch_hb<true, 128>(sa, p.head_block, sgrid, slds, st)
-                     : dispatch_hb<false, 128>(sa, p.head_block, sgrid, slds, st); break;
-    default: e = bf ? dispatch_hb<true, 576>(sa, p.head_block, sgrid, slds, st)
-                    : dispatch_hb<false, 576>(sa, p.head_block, sgrid, slds, st); break;
+    case 64: return bf ? dispatch_hb<true, 64>(a, p, sgrid, p.score_lds, st)
+                       : dispatch_hb<false, 64>(a, p, sgrid, p.score_lds, st);
+    case 128: return bf ? dispatch_hb<true, 128>(a, p, sgrid, p.score_lds, st)
+                        : dispatch_hb<false, 128>(a, p, sgrid, p.score_lds, st);
+    default: return bf ? dispatch_hb<true, 576>(a, p, sgrid, p.score_lds, st)
+                       : dispatch_hb<false, 576>(a, p, sgrid, p.score_lds, st);
   }
-  if (e != hipSuccess) return e;
-  MergeArgs ma{lens, budgets, sa.ckey, sa.cidx, sa.ccnt, sel, cnt,
-               g.Hkv, b_max, p.chunk, p.nchunk, p.cap};
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&merge_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.merge_lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(g.Hkv, g.B), dim3(kThreads), p.merge_lds, st, ma);
-  return hipGetLastError();
 }
 
 }  // namespace psd

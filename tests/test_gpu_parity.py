@@ -44,6 +44,12 @@ SMALL = {
     "many_chunks": synth.small_spec(batch=2, seq_lens=(16 * 3000 - 5, 16 * 700), budget_pages=40,
                                     max_len=16 * 3000),
     "tiny_cfg_seed1": dataclasses.replace(synth.SPECS["tiny"], seed=1),
+    # more kept pages than one scoring workgroup's chunk of candidates
+    "budget_over_chunk": synth.small_spec(batch=1, seq_lens=(16 * 3000,), budget_pages=120,
+                                          max_len=16 * 3000),
+    # enough units for the widest scoring workgroups
+    "wide_batch": synth.small_spec(batch=64, num_q_heads=32, num_kv_heads=8, seq_lens=(),
+                                   len_range=(3000, 9000), budget_percent=5, max_len=9008),
 }
 
 
