@@ -91,9 +91,13 @@ typedef struct psd_shape {
 } psd_shape;
 
 /*
- * Page statistics layout (`meta`): [num_blocks, num_kv_heads, 2, head_dim] in `dtype`,
- * indexed by PHYSICAL block like the cache; plane 0 holds the per-dim minimum of the
- * page's valid keys, plane 1 the maximum. Values are exact (copied key values).
+ * Page statistics layout (`meta`), in `dtype`, indexed by PHYSICAL block like the cache:
+ *   [head_dim / CD][num_blocks][num_kv_heads][2][CD],  CD = 64 bytes of dims
+ *   (32 for bf16, 16 for fp32),
+ * i.e. the per-dim minimum (plane 0) and maximum (plane 1) of a page's valid keys, cut
+ * into chunks of CD dims; the minima and maxima of one chunk of one (block, head) form
+ * one 128-byte line. Total size: 2 * num_blocks * num_kv_heads * head_dim elements.
+ * Values are exact (copied key values).
  */
 
 /*
@@ -103,10 +107,10 @@ typedef struct psd_shape {
  * first_page on), or only the page holding token L_s - 1 when first_page is NULL (the
  * decode-time refresh after the new token's K/V has been written into the cache).
  * Passing first_page[s] = 0 rebuilds every page (prefill). first_page values < 0 are
- * treated as 0. Writes meta[block_table[s][p], h, 0/1, :] for those pages only.
+ * treated as 0. Writes the statistics of blocks block_table[s][p] of those pages only.
  *
  *   k_cache     [num_blocks, 16, H_kv, D] through the k_* strides (device, read)
- *   meta        [num_blocks, H_kv, 2, D] (device, written)
+ *   meta        statistics in the layout above (device, written)
  *   block_table [B, max_pages_per_seq] int32 physical block ids (device, read)
  *   seq_lens    [B] int32 tokens per sequence including the newest (device, read)
  *   first_page  [B] int32 or NULL (device, read)

@@ -6,7 +6,9 @@
 // thread owns 16 contiguous bytes of a row, requests all 16 rows at once and folds the
 // page's valid tokens. Loads are coalesced across the workgroup (consecutive threads read
 // consecutive 16-byte pieces of a token row) and each statistic is written once. Min/max
-// are exact, so the values written are key values themselves.
+// are exact, so the values written are key values themselves. The statistics are stored
+// chunk-major so that the min and max of 64 bytes' worth of dims of one (block, head) form
+// one 128-byte line (the unit the scoring kernel reads).
 #include "psd_device.h"
 #include "psd_launch.h"
 
@@ -19,7 +21,7 @@ struct MetaArgs {
   const int32_t* bt;
   const int32_t* lens;
   const int32_t* first_page;
-  int Hkv, D, max_pages;
+  int Hkv, D, max_pages, num_blocks;
   int64_t kbs, kts, khs;
 };
 
@@ -75,7 +77,9 @@ __global__ __launch_bounds__(256) void meta_kernel(MetaArgs a) {
         }
       }
     }
-    const int64_t mrow = ((int64_t)blk * a.Hkv + h) * 2 * a.D + d;
+    // chunk-major statistics: [D / CD][num_blocks][H_kv][2][CD], CD = 64 bytes of dims
+    constexpr int CD = BF16 ? 32 : 16;
+    const int64_t mrow = (((int64_t)(d / CD) * a.num_blocks + blk) * a.Hkv + h) * 2 * CD + d % CD;
     if constexpr (BF16) {
       uint16_t* m = static_cast<uint16_t*>(a.meta);
       uint4 lo, hi;
@@ -88,11 +92,11 @@ __global__ __launch_bounds__(256) void meta_kernel(MetaArgs a) {
       hi.z = pack2(__float_as_uint(mx[4]) >> 16, __float_as_uint(mx[5]) >> 16);
       hi.w = pack2(__float_as_uint(mx[6]) >> 16, __float_as_uint(mx[7]) >> 16);
       *reinterpret_cast<uint4*>(m + mrow) = lo;
-      *reinterpret_cast<uint4*>(m + mrow + a.D) = hi;
+      *reinterpret_cast<uint4*>(m + mrow + CD) = hi;
     } else {
       float* m = static_cast<float*>(a.meta);
       *reinterpret_cast<float4*>(m + mrow) = make_float4(mn[0], mn[1], mn[2], mn[3]);
-      *reinterpret_cast<float4*>(m + mrow + a.D) = make_float4(mx[0], mx[1], mx[2], mx[3]);
+      *reinterpret_cast<float4*>(m + mrow + CD) = make_float4(mx[0], mx[1], mx[2], mx[3]);
     }
   }
 }
@@ -101,7 +105,8 @@ __global__ __launch_bounds__(256) void meta_kernel(MetaArgs a) {
 
 hipError_t launch_meta_update(const Geo& g, const void* k, void* meta, const int32_t* bt,
                               const int32_t* lens, const int32_t* first_page, hipStream_t st) {
-  MetaArgs a{k, meta, bt, lens, first_page, g.Hkv, g.D, g.max_pages, g.kbs, g.kts, g.khs};
+  MetaArgs a{k, meta, bt, lens, first_page, g.Hkv, g.D, g.max_pages, g.num_blocks, g.kbs, g.kts,
+             g.khs};
   const dim3 grid(first_page ? g.max_pages : 1, g.B);
   const int vec = g.dtype == 1 ? 8 : 4;
   int threads = (g.Hkv * g.D / vec + 63) / 64 * 64;

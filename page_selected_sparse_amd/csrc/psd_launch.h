@@ -27,9 +27,10 @@ struct SelectPlan {
   int cap;         // candidate slots per chunk = min(chunk, b_max - 2)
   int head_block;  // query heads scored per pass (template width)
   int d_chunk;     // dims of q staged in LDS per pass (LDS q path)
-  bool qtab;       // (q+, q-) from an fp64 table in the workspace via scalar loads
-  bool fused;      // the last chunk workgroup of a unit merges (no merge kernel)
-  size_t off_idx, off_cnt, off_arrive, off_qtab, bytes;  // workspace layout
+  bool all_q;           // whole (q+, q-) table of the group in LDS
+  int pages_per_lane;   // pages scored together per thread (all_q plans)
+  int merge_threads;  // threads of the per-unit merge workgroup
+  size_t off_idx, off_cnt, bytes;  // workspace layout
   size_t merge_lds;  // LDS of a unit merge
   size_t score_lds;  // dynamic LDS of the scoring kernel
 };

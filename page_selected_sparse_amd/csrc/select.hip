@@ -37,7 +37,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMergeCap = 8192;  // candidates one merge workgroup holds in LDS
 constexpr int kMaxChunks = 1024;  // chunks per unit
-constexpr int kFusedCap = 2048;   // candidates the last chunk workgroup merges in LDS
 
 // Everything the three selection kernels need; device pointers into the caller's
 // buffers and the select workspace.
@@ -50,11 +49,9 @@ struct SelArgs {
   uint64_t* ckey;    // [unit][nchunk][cap] chunk candidates (order-preserving keys)
   int32_t* cidx;     // [unit][nchunk][cap] their logical pages
   int32_t* ccnt;     // [unit][nchunk] candidates written per chunk
-  uint32_t* arrive;  // [unit] chunks done (fused merge)
-  double2* qtab;     // [unit][D][HB] (q+, q-) in fp64 (single-pass plans)
   int32_t* sel;
   int32_t* cnt;
-  int Hq, Hkv, G, D, max_pages, b_max, chunk, ppt, nchunk, cap, fused;
+  int Hq, Hkv, G, D, max_pages, b_max, chunk, ppt, nchunk, cap, num_blocks;
 };
 
 struct SelScratch {
@@ -209,23 +206,12 @@ __device__ __forceinline__ UnitInfo unit_info(const SelArgs& a, int s) {
   return u;
 }
 
-// Prepares a call: the fp64 (q+, q-) table of every unit, zeroed arrival counters, and
-// every selection row except the ranked winners (sink, tail, padding and count; the whole
-// row for units that need no ranking; -1 rows for units over capacity).
-template <bool BF16, int HB, bool QTAB>
+// Prepares a call: zeroed arrival counters and every selection row except the ranked
+// winners (sink, tail, padding and count; the whole row for units that need no ranking;
+// -1 rows for units over capacity).
 __global__ __launch_bounds__(kThreads) void prep_kernel(SelArgs a) {
   const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int unit = s * a.Hkv + g;
-  if constexpr (QTAB) {
-    double2* qt = a.qtab + (int64_t)unit * a.D * HB;
-    for (int e = tid; e < a.D * HB; e += kThreads) {
-      const int d = e / HB, h = e - d * HB;
-      double qv = 0.0;
-      if (h < a.G) qv = q_value<BF16>(a.q, ((int64_t)s * a.Hq + g * a.G + h) * a.D + d);
-      qt[e] = make_double2(qv >= 0.0 ? qv : 0.0, qv >= 0.0 ? 0.0 : qv);
-    }
-  }
-  if (tid == 0 && a.fused) a.arrive[unit] = 0u;
   const UnitInfo u = unit_info(a, s);
   int32_t* row = a.sel + (int64_t)unit * a.b_max;
   if (u.b > a.b_max) {  // never truncate: flag the unit
@@ -246,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(SelArgs a) {
   }
 }
 
-// Element j of a 64-byte chunk held as four 16-byte vectors, widened exactly to fp64.
+// Element j of a chunk held as 16-byte vectors, widened exactly to fp64.
 template <bool BF16>
 __device__ __forceinline__ double chunk_elem(const uint4* v, int j) {
   if constexpr (BF16) {
@@ -261,132 +247,100 @@ __device__ __forceinline__ double chunk_elem(const uint4* v, int j) {
   }
 }
 
-typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
-
-// 64 bytes of a wave-uniform table into SGPRs. The value may only be used after
-// smem_wait(); the wait redefines it, so no use can be scheduled above the wait.
-__device__ __forceinline__ u32x16 smem_load64(const void* base, uint32_t byte_off) {
-  u32x16 v;
-  asm volatile("s_load_dwordx16 %0, %1, %2" : "=s"(v) : "s"(base), "s"(byte_off));
-  return v;
-}
-__device__ __forceinline__ void smem_wait(u32x16& v) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v));
-}
-__device__ __forceinline__ double sgpr_f64(const u32x16& v, int i) {
-  return __builtin_bit_cast(double, ((uint64_t)v[2 * i + 1] << 32) | v[2 * i]);
-}
-
-// Bound of one page for HB heads with (q+, q-) read from the unit's fp64 table, which
-// is wave-uniform: it is loaded into SGPRs, 64 bytes (4 heads) per load, one dim ahead,
-// and used directly as the fp64 FMA operand. The page's min/max rows are read in
-// 64-byte chunks, the next chunk in flight while the current one is accumulated. The
-// dims ascend.
-template <bool BF16, int D, int HB>
-__device__ __forceinline__ void bound_qtab(const void* meta, int64_t row,
-                                           const double2* __restrict__ qt, double* acc) {
-  constexpr int ES = BF16 ? 2 : 4;
-  constexpr int CH = 64 / ES;  // dims per chunk
-  constexpr int NCH = D / CH;
-  constexpr int NQ = HB / 4;   // 64-byte q loads per dim
-  constexpr bool PREF = NQ <= 2;  // double-buffer the q loads when the SGPRs allow
-  const unsigned char* mn = static_cast<const unsigned char*>(meta) + row * ES;
-  const unsigned char* mx = mn + D * ES;
-  uint4 cur[8], nxt[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    cur[i] = *reinterpret_cast<const uint4*>(mn + 16 * i);
-    cur[4 + i] = *reinterpret_cast<const uint4*>(mx + 16 * i);
+// Statistics are chunk-major: [D / CD][num_blocks][H_kv][2][CD] with CD = 64 bytes of
+// dims, so the minima and maxima of CD dims of one (block, head) are one 128-byte line.
+template <bool BF16>
+struct MetaGeo {
+  static constexpr int ES = BF16 ? 2 : 4;
+  static constexpr int CD = 64 / ES;  // dims per chunk
+  // byte offset of chunk c of (block, head)
+  __device__ static int64_t piece(int c, int nb, int hkv, int blk, int g) {
+    return (((int64_t)c * nb + blk) * hkv + g) * 128;
   }
-  u32x16 qa[NQ], qb[NQ];
+};
+
+// Four fp64 FMAs per head pair of one dim: acc_h += q+_h kmax + q-_h kmin, with q read
+// from lane B + 2h (+1) of each 16-lane row of `q` by a DPP row broadcast. The leading
+// s_nop covers the VALU-write -> DPP-read hazard on the q register.
+template <int B>
+__device__ __forceinline__ void fma4_dpp(double& a0, double& a1, double& a2, double& a3, double q,
+                                         double kx, double kn) {
+  asm("s_nop 1\n\t"
+      "v_fmac_f64_dpp %0, %4, %5 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %1, %4, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %1, %4, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %2, %4, %5 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %2, %4, %6 row_newbcast:%12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %3, %4, %5 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %3, %4, %6 row_newbcast:%14 row_mask:0xf bank_mask:0xf"
+      : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)
+      : "v"(q), "v"(kx), "v"(kn), "n"(B), "n"(B + 1), "n"(B + 2), "n"(B + 3), "n"(B + 4),
+        "n"(B + 5), "n"(B + 6), "n"(B + 7));
+}
+
+// Bound of one page for HB (4 or 8) heads. The group's (q+, q-) values for a chunk of CD
+// dims are spread over the lanes of each 16-lane row (value v of the chunk in register
+// v / 16 of lane v % 16, loaded from the LDS table once per chunk) and reach the fp64
+// FMAs through DPP row broadcasts, so no per-dim operand traffic is needed. Each chunk
+// of the page's statistics is one 128-byte line; dims ascend.
+template <bool BF16, int D, int HB>
+__device__ __forceinline__ void bound_dpp(const void* meta, int nb, int hkv, int blk, int g,
+                                          const double* qv, double* acc) {
+  using M = MetaGeo<BF16>;
+  constexpr int CD = M::CD;
+  constexpr int NQ = CD * 2 * HB / 16;  // q registers per chunk
+  const int lane16 = threadIdx.x & 15;
+  const unsigned char* base = static_cast<const unsigned char*>(meta);
+  // kept rolled: the loads and q reads of one chunk stay inside its iteration
+#pragma unroll 1
+  for (int c = 0; c < D / CD; ++c) {
+    const uint4* pc = reinterpret_cast<const uint4*>(base + M::piece(c, nb, hkv, blk, g));
+    uint4 mv[8];
 #pragma unroll
-  for (int k = 0; k < NQ; ++k) qa[k] = smem_load64(qt, 64 * k);
+    for (int i = 0; i < 8; ++i) mv[i] = pc[i];
+    double Q[NQ];
 #pragma unroll
-  for (int k = 0; k < NQ; ++k) smem_wait(qa[k]);
+    for (int m = 0; m < NQ; ++m) Q[m] = qv[c * CD * 2 * HB + 16 * m + lane16];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (c + 1 < NCH) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        nxt[i] = *reinterpret_cast<const uint4*>(mn + 64 * (c + 1) + 16 * i);
-        nxt[4 + i] = *reinterpret_cast<const uint4*>(mx + 64 * (c + 1) + 16 * i);
+    for (int j = 0; j < CD; ++j) {
+      const double kmn = chunk_elem<BF16>(mv, j), kmx = chunk_elem<BF16>(mv + 4, j);
+      if constexpr (HB == 4) {
+        if (j & 1)
+          fma4_dpp<8>(acc[0], acc[1], acc[2], acc[3], Q[j >> 1], kmx, kmn);
+        else
+          fma4_dpp<0>(acc[0], acc[1], acc[2], acc[3], Q[j >> 1], kmx, kmn);
+      } else {
+        fma4_dpp<0>(acc[0], acc[1], acc[2], acc[3], Q[j], kmx, kmn);
+        fma4_dpp<8>(acc[4], acc[5], acc[6], acc[7], Q[j], kmx, kmn);
       }
     }
+  }
+}
+
+// Bound contribution of dims [d0, d0 + DC) of one page for HB heads, with the (q+, q-)
+// table of those dims staged in LDS and read as broadcasts; dims ascend.
+template <bool BF16, int DC, int HB>
+__device__ __forceinline__ void bound_lds(const void* meta, int nb, int hkv, int blk, int g,
+                                          int d0, const double2* qt, double* acc) {
+  using M = MetaGeo<BF16>;
+  constexpr int CD = M::CD;
+  constexpr int PER = 16 / M::ES;  // dims per 16-byte vector
+  const unsigned char* base = static_cast<const unsigned char*>(meta);
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int d = c * CH + j;
-      const bool more = PREF && d + 1 < D;
-      if (more) {  // next dim's q in flight while this dim is accumulated
+  for (int dd = 0; dd < DC; dd += PER) {
+    const int d = d0 + dd;
+    const unsigned char* pc = base + M::piece(d / CD, nb, hkv, blk, g) + (d % CD) * M::ES;
+    const uint4 av = *reinterpret_cast<const uint4*>(pc);
+    const uint4 bv = *reinterpret_cast<const uint4*>(pc + 64);
 #pragma unroll
-        for (int k = 0; k < NQ; ++k) qb[k] = smem_load64(qt, (d + 1) * HB * 16 + 64 * k);
-      } else if (!PREF && d > 0) {  // 16 heads: no SGPRs left for a second buffer
-#pragma unroll
-        for (int k = 0; k < NQ; ++k) qa[k] = smem_load64(qt, d * HB * 16 + 64 * k);
-#pragma unroll
-        for (int k = 0; k < NQ; ++k) smem_wait(qa[k]);
-      }
-      const double kmn = chunk_elem<BF16>(cur, j), kmx = chunk_elem<BF16>(cur + 4, j);
+    for (int j = 0; j < PER; ++j) {
+      const double kmn = chunk_elem<BF16>(&av, j), kmx = chunk_elem<BF16>(&bv, j);
 #pragma unroll
       for (int h = 0; h < HB; ++h) {
-        const double qp = sgpr_f64(qa[h >> 2], 2 * (h & 3));
-        const double qn = sgpr_f64(qa[h >> 2], 2 * (h & 3) + 1);
-        acc[h] = __builtin_fma(qp, kmx, acc[h]);
-        acc[h] = __builtin_fma(qn, kmn, acc[h]);
-      }
-      if (more) {
-#pragma unroll
-        for (int k = 0; k < NQ; ++k) {
-          smem_wait(qb[k]);
-          qa[k] = qb[k];
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep each dim's loads next to its FMAs
-    }
-    if (c + 1 < NCH) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
-    }
-  }
-}
-
-// Bound contribution of dims [0, DC) of one page row segment for HB heads, with the
-// (q+, q-) table for those dims staged in LDS (many-head groups), ascending d.
-template <bool BF16, int DC, int HB>
-__device__ __forceinline__ void bound_lds(const void* meta, int64_t row, int D,
-                                          const double2* qt, double* acc) {
-  if constexpr (BF16) {
-    const uint16_t* mn = static_cast<const uint16_t*>(meta) + row;
-    const uint16_t* mx = mn + D;
-#pragma unroll
-    for (int d0 = 0; d0 < DC; d0 += 8) {
-      const uint4 av = load16(mn + d0), bv = load16(mx + d0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double kmn = chunk_elem<true>(&av, j), kmx = chunk_elem<true>(&bv, j);
-#pragma unroll
-        for (int h = 0; h < HB; ++h) {
-          const double2 qq = qt[(d0 + j) * HB + h];
-          acc[h] = __builtin_fma(qq.x, kmx, acc[h]);
-          acc[h] = __builtin_fma(qq.y, kmn, acc[h]);
-        }
-      }
-    }
-  } else {
-    const float* mn = static_cast<const float*>(meta) + row;
-    const float* mx = mn + D;
-#pragma unroll
-    for (int d0 = 0; d0 < DC; d0 += 4) {
-      const uint4 av = *reinterpret_cast<const uint4*>(mn + d0);
-      const uint4 bv = *reinterpret_cast<const uint4*>(mx + d0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const double kmn = chunk_elem<false>(&av, j), kmx = chunk_elem<false>(&bv, j);
-#pragma unroll
-        for (int h = 0; h < HB; ++h) {
-          const double2 qq = qt[(d0 + j) * HB + h];
-          acc[h] = __builtin_fma(qq.x, kmx, acc[h]);
-          acc[h] = __builtin_fma(qq.y, kmn, acc[h]);
-        }
+        const double2 qq = qt[(dd + j) * HB + h];
+        acc[h] = __builtin_fma(qq.x, kmx, acc[h]);
+        acc[h] = __builtin_fma(qq.y, kmn, acc[h]);
       }
     }
   }
@@ -442,15 +396,16 @@ __device__ void merge_unit(const SelArgs& a, int unit, int n, int kp, unsigned c
   block_emit_top<NT>(keys, total, T, need, sc, [&](int pos, int i) { row[1 + pos] = idx[i]; });
 }
 
-template <bool BF16, int D, int HB, bool QTAB, int NT>
-__global__ __launch_bounds__(NT) void score_kernel(SelArgs a, const double2* __restrict__ qtab) {
-  // LDS q table for many-head groups: HB heads over DC dims, whole D when it fits.
-  constexpr int DC = QTAB ? 1 : ((HB * D * 16 <= 32768) ? D : 32);
-  constexpr int NDC = QTAB ? 1 : D / DC;
-  __shared__ double2 qlds[QTAB ? 1 : DC * HB];
+// One workgroup scores one chunk of a unit's candidate pages 1..n-2, one page per thread.
+// DPP (groups of up to 8 heads, D <= 128): the whole (q+, q-) table in LDS, fed to the
+// FMAs by row broadcasts. Otherwise the table is staged 16 heads x DC dims at a time and
+// read as LDS broadcasts.
+template <bool BF16, int D, int HB, bool DPP, int NT>
+__global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
+  constexpr int DC = DPP ? D : ((HB * D * 16 <= 32768) ? D : 32);
+  constexpr int NDC = D / DC;
+  __shared__ double2 qlds[DC * HB];
   __shared__ SelScratch sc;
-  __shared__ int chunk_off[kMaxChunks + 1];
-  __shared__ int s_last;
   extern __shared__ unsigned char lds[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(lds);  // [chunk]
 
@@ -465,7 +420,6 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a, const double2* __r
   const int cnt = hi - lo;
   const int unit = s * a.Hkv + g;
   const int nhp = ceil_div(a.G, HB);
-  const double2* qt = qtab + (int64_t)unit * D * HB;
 
   auto load_qlds = [&](int hp, int dc) {
     for (int e = tid; e < DC * HB; e += NT) {
@@ -475,22 +429,23 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a, const double2* __r
       qlds[e] = make_double2(qv >= 0.0 ? qv : 0.0, qv >= 0.0 ? 0.0 : qv);
     }
   };
-  const bool once = !QTAB && nhp == 1 && NDC == 1;
+  const bool once = nhp == 1 && NDC == 1;
   if (once) {
     load_qlds(0, 0);
     __syncthreads();
   }
+  const int64_t bt0 = (int64_t)s * a.max_pages;
   for (int it = 0; it < a.ppt; ++it) {
     const int o = it * NT + tid;
     const bool have = o < cnt;
-    const int blk = have ? a.bt[(int64_t)s * a.max_pages + lo + o] : a.bt[(int64_t)s * a.max_pages];
-    const int64_t row = ((int64_t)blk * a.Hkv + g) * 2 * D;
+    const int blk = a.bt[bt0 + (have ? lo + o : 0)];
     double best = -__builtin_inf();
-    if constexpr (QTAB) {
+    if constexpr (DPP) {
       double acc[HB];
 #pragma unroll
       for (int h = 0; h < HB; ++h) acc[h] = 0.0;
-      bound_qtab<BF16, D, HB>(a.meta, row, qt, acc);
+      bound_dpp<BF16, D, HB>(a.meta, a.num_blocks, a.Hkv, blk, g,
+                             reinterpret_cast<const double*>(qlds), acc);
 #pragma unroll
       for (int h = 0; h < HB; ++h)
         if (h < a.G && acc[h] > best) best = acc[h];
@@ -505,16 +460,14 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a, const double2* __r
             load_qlds(hp, dc);
             __syncthreads();
           }
-          if (have) bound_lds<BF16, DC, HB>(a.meta, row + dc * DC, D, qlds, acc);
+          bound_lds<BF16, DC, HB>(a.meta, a.num_blocks, a.Hkv, blk, g, dc * DC, qlds, acc);
         }
 #pragma unroll
         for (int h = 0; h < HB; ++h)
           if (hp * HB + h < a.G && acc[h] > best) best = acc[h];
       }
     }
-    // written for every thread (slots past cnt are never read) so that the bound is not
-    // sunk into a branch below the scalar q loads
-    keys[o] = score_key(best);
+    keys[o] = score_key(best);  // every slot written; slots past cnt are never read
   }
   __syncthreads();
 
@@ -537,28 +490,17 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a, const double2* __r
     });
     if (tid == 0) a.ccnt[(int64_t)unit * a.nchunk + c] = emitted;
   }
-  if (!a.fused) return;
-
-  // The last chunk workgroup of the unit to finish merges (release / acquire fences
-  // around the arrival counter make the other chunks' candidates visible).
-  __threadfence();
-  __syncthreads();
-  const int nch = ceil_div(n - 2, a.chunk);
-  if (tid == 0) s_last = atomicAdd(&a.arrive[unit], 1u) == (unsigned)(nch - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  merge_unit<NT>(a, unit, n, kp, lds, chunk_off, sc);
 }
 
-__global__ __launch_bounds__(kThreads) void merge_kernel(SelArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void merge_kernel(SelArgs a) {
   __shared__ SelScratch sc;
   __shared__ int chunk_off[kMaxChunks + 1];
   extern __shared__ unsigned char lds[];
   const int g = blockIdx.x, s = blockIdx.y;
   const UnitInfo u = unit_info(a, s);
   if (u.trivial) return;
-  merge_unit<kThreads>(a, s * a.Hkv + g, u.n, u.kp, lds, chunk_off, sc);
+  merge_unit<NT>(a, s * a.Hkv + g, u.n, u.kp, lds, chunk_off, sc);
 }
 
 template <typename K>
@@ -567,45 +509,42 @@ hipError_t set_lds(K kernel, size_t lds) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-template <bool BF16, int D, int HB, bool QTAB, int NT>
-hipError_t launch_all(const SelArgs& a, const SelectPlan& p, dim3 sgrid, size_t slds,
-                      hipStream_t st) {
+template <bool BF16, int D, int HB, bool DPP, int NT>
+hipError_t launch_all(const SelArgs& a, const SelectPlan& p, dim3 sgrid, hipStream_t st) {
   const dim3 ugrid(a.Hkv, sgrid.z);
-  hipLaunchKernelGGL((prep_kernel<BF16, HB, QTAB>), ugrid, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(prep_kernel, ugrid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = set_lds(&score_kernel<BF16, D, HB, QTAB, NT>, slds)) != hipSuccess) return e;
-  hipLaunchKernelGGL((score_kernel<BF16, D, HB, QTAB, NT>), sgrid, dim3(NT), slds, st, a, a.qtab);
+  if ((e = set_lds(&score_kernel<BF16, D, HB, DPP, NT>, p.score_lds)) != hipSuccess) return e;
+  hipLaunchKernelGGL((score_kernel<BF16, D, HB, DPP, NT>), sgrid, dim3(NT), p.score_lds, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (!a.fused) {
-    if ((e = set_lds(&merge_kernel, p.merge_lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(merge_kernel, ugrid, dim3(kThreads), p.merge_lds, st, a);
-    e = hipGetLastError();
+  // Merge in its own launch: the kernel boundary makes every chunk's candidates visible
+  // (a device-scope fence inside the scoring kernel would write back and invalidate the L2).
+  if (p.merge_threads == 64) {
+    if ((e = set_lds(&merge_kernel<64>, p.merge_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_kernel<64>, ugrid, dim3(64), p.merge_lds, st, a);
+  } else {
+    if ((e = set_lds(&merge_kernel<kThreads>, p.merge_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_kernel<kThreads>, ugrid, dim3(kThreads), p.merge_lds, st, a);
   }
-  return e;
+  return hipGetLastError();
 }
 
-template <bool BF16, int D, int HB>
-hipError_t dispatch_nt(const SelArgs& a, const SelectPlan& p, dim3 grid, size_t lds,
-                       hipStream_t st) {
-  switch (p.threads) {
-    case 64: return launch_all<BF16, D, HB, true, 64>(a, p, grid, lds, st);
-    case 256: return launch_all<BF16, D, HB, true, 256>(a, p, grid, lds, st);
-    default: return launch_all<BF16, D, HB, true, 512>(a, p, grid, lds, st);
-  }
+template <bool BF16, int D, int HB, bool DPP>
+hipError_t dispatch_nt(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStream_t st) {
+  return p.threads == 64 ? launch_all<BF16, D, HB, DPP, 64>(a, p, grid, st)
+                         : launch_all<BF16, D, HB, DPP, kThreads>(a, p, grid, st);
 }
 
 template <bool BF16, int D>
-hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, size_t lds,
-                       hipStream_t st) {
+hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStream_t st) {
   if constexpr (D > 128) {
-    return launch_all<BF16, D, 16, false, kThreads>(a, p, grid, lds, st);
+    return launch_all<BF16, D, 16, false, kThreads>(a, p, grid, st);
   } else {
-    if (!p.qtab) return launch_all<BF16, D, 16, false, kThreads>(a, p, grid, lds, st);
     switch (p.head_block) {
-      case 4: return dispatch_nt<BF16, D, 4>(a, p, grid, lds, st);
-      case 8: return dispatch_nt<BF16, D, 8>(a, p, grid, lds, st);
-      default: return dispatch_nt<BF16, D, 16>(a, p, grid, lds, st);
+      case 4: return dispatch_nt<BF16, D, 4, true>(a, p, grid, st);
+      case 8: return dispatch_nt<BF16, D, 8, true>(a, p, grid, st);
+      default: return dispatch_nt<BF16, D, 16, false>(a, p, grid, st);
     }
   }
 }
@@ -617,28 +556,27 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   const int kcap = b_max - 2;
   const int inner = g.max_pages > 2 ? g.max_pages - 2 : 1;
   const int64_t units = (int64_t)g.B * g.Hkv;
-  // Groups of up to 16 heads with D <= 128 read (q+, q-) from an fp64 table through
-  // scalar loads; larger groups stage it in LDS, 16 heads at a time.
-  p->qtab = g.G <= 16 && g.D <= 128;
-  p->head_block = !p->qtab ? 16 : (g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16));
-  p->d_chunk = p->qtab ? g.D : ((16 * g.D * 16 <= 32768) ? g.D : 32);
-  const bool multi_pass = !p->qtab && (g.G > 16 || 16 * g.D * 16 > 32768);
-  // Workgroup size: large workgroups keep the waves resident on a CU on one unit (its q
-  // table stays in the scalar cache); small batches use one-wave workgroups for enough
-  // workgroups in flight.
-  p->threads = kThreads;
-  if (p->qtab) {
-    const int64_t wg512 = units * ((inner + 511) / 512);
-    p->threads = wg512 >= 512 ? 512 : (units * ((inner + 255) / 256) >= 512 ? 256 : 64);
-  }
+  // Groups of up to 8 heads with D <= 128 take q through DPP broadcasts (whole table in
+  // LDS); other groups read it as LDS broadcasts, 16 heads at a time.
+  p->all_q = g.G <= 16 && g.D <= 128;
+  p->head_block = !p->all_q ? 16 : (g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16));
+  p->d_chunk = p->all_q ? g.D : ((16 * g.D * 16 <= 32768) ? g.D : 32);
+  p->pages_per_lane = 1;
+  // one-wave workgroups when 256-thread ones would leave the GPU mostly idle
+  p->threads = (p->all_q && units * ((inner + kThreads - 1) / kThreads) < 512) ? 64 : kThreads;
+  const bool multi_pass = !p->all_q && (g.G > 16 || 16 * g.D * 16 > 32768);
   bool ok = false;
   for (int ppt = 1; ppt <= 64; ppt *= 2) {
     if (multi_pass && ppt > 1) break;
-    const int chunk = p->threads * ppt;
+    const int chunk = p->threads * p->pages_per_lane * ppt;
     if (chunk * sizeof(uint64_t) > 65536) break;
     const int nchunk = (inner + chunk - 1) / chunk;
-    const int cap = kcap < 1 ? 1 : (kcap < chunk ? kcap : chunk);
-    if ((int64_t)nchunk * cap <= kMergeCap && nchunk <= kMaxChunks) {
+    if (nchunk > kMaxChunks) continue;
+    // Every page of a chunk is a candidate when they all fit in the merge; otherwise a
+    // chunk keeps only its own top b-2.
+    int cap = chunk;
+    if ((int64_t)nchunk * chunk > kMergeCap) cap = kcap < 1 ? 1 : (kcap < chunk ? kcap : chunk);
+    if ((int64_t)nchunk * cap <= kMergeCap) {
       p->ppt = ppt;
       p->chunk = chunk;
       p->nchunk = nchunk;
@@ -649,16 +587,13 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   }
   if (!ok) return false;
   const size_t slots = (size_t)units * p->nchunk * p->cap;
-  p->fused = (size_t)p->nchunk * p->cap <= (size_t)kFusedCap;
   p->merge_lds = (size_t)p->nchunk * p->cap * (sizeof(uint64_t) + sizeof(int32_t));
+  p->merge_threads = (int64_t)p->nchunk * p->cap <= 2048 ? 64 : kThreads;
   p->score_lds = p->chunk * sizeof(uint64_t);
-  if (p->fused && p->merge_lds > p->score_lds) p->score_lds = p->merge_lds;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   p->off_idx = al(slots * sizeof(uint64_t));
   p->off_cnt = al(p->off_idx + slots * sizeof(int32_t));
-  p->off_arrive = al(p->off_cnt + units * p->nchunk * sizeof(int32_t));
-  p->off_qtab = al(p->off_arrive + units * sizeof(uint32_t));
-  p->bytes = p->off_qtab + (p->qtab ? units * g.D * p->head_block * 16 : 0) + 256;
+  p->bytes = p->off_cnt + units * p->nchunk * sizeof(int32_t) + 256;
   return true;
 }
 
@@ -668,19 +603,18 @@ hipError_t launch_select(const Geo& g, const SelectPlan& p, const void* q, const
   unsigned char* w = static_cast<unsigned char*>(ws);
   SelArgs a{q, meta, bt, lens, budgets,
             reinterpret_cast<uint64_t*>(w), reinterpret_cast<int32_t*>(w + p.off_idx),
-            reinterpret_cast<int32_t*>(w + p.off_cnt), reinterpret_cast<uint32_t*>(w + p.off_arrive),
-            reinterpret_cast<double2*>(w + p.off_qtab), sel, cnt,
+            reinterpret_cast<int32_t*>(w + p.off_cnt), sel, cnt,
             g.Hq, g.Hkv, g.G, g.D, g.max_pages, b_max, p.chunk, p.ppt, p.nchunk, p.cap,
-            p.fused ? 1 : 0};
+            g.num_blocks};
   const dim3 sgrid(p.nchunk, g.Hkv, g.B);
   const bool bf = g.dtype == 1;
   switch (g.D) {
-    case 64: return bf ? dispatch_hb<true, 64>(a, p, sgrid, p.score_lds, st)
-                       : dispatch_hb<false, 64>(a, p, sgrid, p.score_lds, st);
-    case 128: return bf ? dispatch_hb<true, 128>(a, p, sgrid, p.score_lds, st)
-                        : dispatch_hb<false, 128>(a, p, sgrid, p.score_lds, st);
-    default: return bf ? dispatch_hb<true, 576>(a, p, sgrid, p.score_lds, st)
-                       : dispatch_hb<false, 576>(a, p, sgrid, p.score_lds, st);
+    case 64: return bf ? dispatch_hb<true, 64>(a, p, sgrid, st)
+                       : dispatch_hb<false, 64>(a, p, sgrid, st);
+    case 128: return bf ? dispatch_hb<true, 128>(a, p, sgrid, st)
+                        : dispatch_hb<false, 128>(a, p, sgrid, st);
+    default: return bf ? dispatch_hb<true, 576>(a, p, sgrid, st)
+                       : dispatch_hb<false, 576>(a, p, sgrid, st);
   }
 }
 
