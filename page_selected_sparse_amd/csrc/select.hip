@@ -58,6 +58,7 @@ struct SelScratch {
   uint32_t hist[256];
   int wave_cnt[16];
   int digit, k;
+  bool done;
 };
 
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
@@ -96,12 +97,15 @@ __device__ __forceinline__ int block_excl_count(bool flag, SelScratch& sc, int& 
   return off + below;
 }
 
-// K-th largest (1-based) of keys[0..N) in LDS, 1 <= K <= N. Returns the key T and how
-// many of the keys equal to T belong to the top K. Radix select over 8-bit digits from
-// the most significant; equal digits met in a row by one thread are counted once.
+// Finds the top K (1 <= K <= N) of keys[0..N) in LDS by radix select over 8-bit digits
+// from the most significant. Returns a prefix P over the bits covered by `mask` such that
+// every key with (key & mask) > P is in the top K and `need` of the keys with
+// (key & mask) == P complete it (the lowest positions among them). It stops as soon as all
+// keys of the chosen digit are needed; otherwise it ends with mask = all bits, P = the
+// K-th largest key. Equal digits met in a row by one thread are counted once.
 template <int NT>
 __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch& sc,
-                                  uint64_t& T, int& need) {
+                                  uint64_t& P, uint64_t& M, int& need) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0, mask = 0;
   int k = K;
@@ -133,43 +137,53 @@ __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch
       const int incl = wave_inclusive_scan(local);
       const int excl = incl - local;
       if (excl < k && k <= incl) {
-        int r = k - excl, dg;
+        int r = k - excl, dg, cnt;
         if (r <= c0) {
           dg = base;
+          cnt = c0;
         } else if (r <= c0 + c1) {
           r -= c0;
           dg = base - 1;
+          cnt = c1;
         } else if (r <= c0 + c1 + c2) {
           r -= c0 + c1;
           dg = base - 2;
+          cnt = c2;
         } else {
           r -= c0 + c1 + c2;
           dg = base - 3;
+          cnt = c3;
         }
         sc.digit = dg;
         sc.k = r;
+        sc.done = r == cnt;  // every key of this digit is in the top K
       }
     }
     __syncthreads();
     prefix |= (uint64_t)sc.digit << shift;
     mask |= 255ull << shift;
     k = sc.k;
+    const bool done = sc.done;
+    __syncthreads();  // sc is rewritten by the next pass
+    if (done) break;
   }
-  T = prefix;
+  P = prefix;
+  M = mask;
   need = k;
 }
 
-// Emits, in position order, every key > T and the first `need` keys == T; calls
-// out(rank, position) for each. Returns the number emitted. Every thread must call it.
+// Emits, in position order, every key with (key & M) > P and the first `need` keys with
+// (key & M) == P; calls out(rank, position) for each. Returns the number emitted. Every
+// thread must call it.
 template <int NT, typename Out>
-__device__ int block_emit_top(const uint64_t* keys, int N, uint64_t T, int need, SelScratch& sc,
-                              Out out) {
+__device__ int block_emit_top(const uint64_t* keys, int N, uint64_t P, uint64_t M, int need,
+                              SelScratch& sc, Out out) {
   int run_eq = 0, run_out = 0;
   for (int base = 0; base < N; base += NT) {
     const int i = base + threadIdx.x;
     const bool ok = i < N;
-    const uint64_t key = ok ? keys[i] : 0;
-    const bool gt = ok && key > T, eq = ok && key == T;
+    const uint64_t key = ok ? (keys[i] & M) : 0;
+    const bool gt = ok && key > P, eq = ok && key == P;
     int tot_eq, tot_sel;
     const int eq_rank = run_eq + block_excl_count<NT>(eq, sc, tot_eq);
     const bool pick = gt || (eq && eq_rank < need);
@@ -292,13 +306,12 @@ __device__ __forceinline__ void bound_dpp(const void* meta, int nb, int hkv, int
   constexpr int NQ = CD * 2 * HB / 16;  // q registers per chunk
   const int lane16 = threadIdx.x & 15;
   const unsigned char* base = static_cast<const unsigned char*>(meta);
-  // kept rolled: the loads and q reads of one chunk stay inside its iteration
-#pragma unroll 1
-  for (int c = 0; c < D / CD; ++c) {
+  auto load = [&](int c, uint4* mv) {
     const uint4* pc = reinterpret_cast<const uint4*>(base + M::piece(c, nb, hkv, blk, g));
-    uint4 mv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) mv[i] = pc[i];
+  };
+  auto accumulate = [&](int c, const uint4* mv) {
     double Q[NQ];
 #pragma unroll
     for (int m = 0; m < NQ; ++m) Q[m] = qv[c * CD * 2 * HB + 16 * m + lane16];
@@ -315,6 +328,18 @@ __device__ __forceinline__ void bound_dpp(const void* meta, int nb, int hkv, int
         fma4_dpp<8>(acc[4], acc[5], acc[6], acc[7], Q[j], kmx, kmn);
       }
     }
+  };
+  // Two line buffers: the next chunk's line is in flight while one is accumulated. The
+  // loop is kept rolled so that each chunk's q reads stay inside their iteration.
+  constexpr int NCH = D / CD;  // even for every supported D
+  uint4 ma[8], mb[8];
+  load(0, ma);
+#pragma unroll 1
+  for (int c = 0; c < NCH; c += 2) {
+    load(c + 1, mb);
+    accumulate(c, ma);
+    if (c + 2 < NCH) load(c + 2, ma);
+    accumulate(c + 1, mb);
   }
 }
 
@@ -346,54 +371,39 @@ __device__ __forceinline__ void bound_lds(const void* meta, int nb, int hkv, int
   }
 }
 
-// Global top-kp of one unit from its chunk candidate lists (in page order), written to
-// row[1 .. kp] in ascending page order. `lds` holds nchunk * cap keys then indices.
+// Global top-kp of one unit from its chunk candidate lists, written to row[1 .. kp] in
+// ascending page order. The unit's slots are copied as one block (chunk-major, so in page
+// order); slots past a chunk's count get key 0, below every score key. When every chunk
+// keeps all its pages (cap == chunk) a slot's page is its position + 1.
 template <int NT>
 __device__ void merge_unit(const SelArgs& a, int unit, int n, int kp, unsigned char* lds,
-                           int* chunk_off, SelScratch& sc) {
-  constexpr int NW = NT / 64;
+                           SelScratch& sc) {
   const int tid = threadIdx.x;
   int32_t* row = a.sel + (int64_t)unit * a.b_max;
   const int nch = ceil_div(n - 2, a.chunk);
+  const int total = nch * a.cap;
+  const bool dense = a.cap == a.chunk;
   uint64_t* keys = reinterpret_cast<uint64_t*>(lds);
   int32_t* idx = reinterpret_cast<int32_t*>(lds + sizeof(uint64_t) * (size_t)a.nchunk * a.cap);
-  for (int c = tid; c < nch; c += NT) chunk_off[c] = a.ccnt[(int64_t)unit * a.nchunk + c];
-  __syncthreads();
-  int carry = 0;
-  for (int base = 0; base < nch; base += NT) {  // exclusive scan of the counts
-    const int c = base + tid;
-    const int v = c < nch ? chunk_off[c] : 0;
-    const int lane = tid & 63, w = tid >> 6;
-    const int incl = wave_inclusive_scan(v);
-    if (lane == 63) sc.wave_cnt[w] = incl;
-    __syncthreads();
-    int off = carry, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      off += i < w ? sc.wave_cnt[i] : 0;
-      tot += sc.wave_cnt[i];
-    }
-    __syncthreads();
-    if (c < nch) chunk_off[c] = off + incl - v;
-    carry += tot;
-  }
-  if (tid == 0) chunk_off[nch] = carry;
-  __syncthreads();
-  const int total = carry;
-  for (int j = tid; j < nch * a.cap; j += NT) {
-    const int c = j / a.cap, i = j - c * a.cap;
-    const int o = chunk_off[c];
-    if (i < chunk_off[c + 1] - o) {
-      const int64_t src = ((int64_t)unit * a.nchunk + c) * a.cap + i;
-      keys[o + i] = a.ckey[src];
-      idx[o + i] = a.cidx[src];
-    }
+  int* cnts = reinterpret_cast<int*>(idx + (size_t)a.nchunk * a.cap);
+  const int64_t src = (int64_t)unit * a.nchunk * a.cap;
+  for (int c = tid; c < nch; c += NT) cnts[c] = a.ccnt[(int64_t)unit * a.nchunk + c];
+#pragma unroll 4
+  for (int j = tid; j < total; j += NT) {
+    keys[j] = a.ckey[src + j];
+    if (!dense) idx[j] = a.cidx[src + j];
   }
   __syncthreads();
-  uint64_t T;
+  for (int j = tid; j < total; j += NT) {
+    const int c = j / a.cap;
+    if (j - c * a.cap >= cnts[c]) keys[j] = 0;
+  }
+  __syncthreads();
+  uint64_t P, M;
   int need;
-  block_kth_largest<NT>(keys, total, kp, sc, T, need);
-  block_emit_top<NT>(keys, total, T, need, sc, [&](int pos, int i) { row[1 + pos] = idx[i]; });
+  block_kth_largest<NT>(keys, total, kp, sc, P, M, need);
+  block_emit_top<NT>(keys, total, P, M, need, sc,
+                     [&](int pos, int i) { row[1 + pos] = dense ? i + 1 : idx[i]; });
 }
 
 // One workgroup scores one chunk of a unit's candidate pages 1..n-2, one page per thread.
@@ -474,17 +484,17 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   // Chunk candidates: all pages when they fit in kp, else the chunk's top-kp.
   uint64_t* okey = a.ckey + ((int64_t)unit * a.nchunk + c) * a.cap;
   int32_t* oidx = a.cidx + ((int64_t)unit * a.nchunk + c) * a.cap;
-  if (cnt <= kp) {
+  if (cnt <= kp || a.cap == a.chunk) {  // every page of the chunk is a candidate
     for (int o = tid; o < cnt; o += NT) {
       okey[o] = keys[o];
-      oidx[o] = lo + o;
+      if (a.cap < a.chunk) oidx[o] = lo + o;
     }
     if (tid == 0) a.ccnt[(int64_t)unit * a.nchunk + c] = cnt;
   } else {
-    uint64_t T;
+    uint64_t P, M;
     int need;
-    block_kth_largest<NT>(keys, cnt, kp, sc, T, need);
-    const int emitted = block_emit_top<NT>(keys, cnt, T, need, sc, [&](int pos, int i) {
+    block_kth_largest<NT>(keys, cnt, kp, sc, P, M, need);
+    const int emitted = block_emit_top<NT>(keys, cnt, P, M, need, sc, [&](int pos, int i) {
       okey[pos] = keys[i];
       oidx[pos] = lo + i;
     });
@@ -495,12 +505,11 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
 template <int NT>
 __global__ __launch_bounds__(NT) void merge_kernel(SelArgs a) {
   __shared__ SelScratch sc;
-  __shared__ int chunk_off[kMaxChunks + 1];
   extern __shared__ unsigned char lds[];
   const int g = blockIdx.x, s = blockIdx.y;
   const UnitInfo u = unit_info(a, s);
   if (u.trivial) return;
-  merge_unit<NT>(a, s * a.Hkv + g, u.n, u.kp, lds, chunk_off, sc);
+  merge_unit<NT>(a, s * a.Hkv + g, u.n, u.kp, lds, sc);
 }
 
 template <typename K>
@@ -587,8 +596,9 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   }
   if (!ok) return false;
   const size_t slots = (size_t)units * p->nchunk * p->cap;
-  p->merge_lds = (size_t)p->nchunk * p->cap * (sizeof(uint64_t) + sizeof(int32_t));
-  p->merge_threads = (int64_t)p->nchunk * p->cap <= 2048 ? 64 : kThreads;
+  p->merge_lds = (size_t)p->nchunk * p->cap * (sizeof(uint64_t) + sizeof(int32_t)) +
+                 (size_t)p->nchunk * sizeof(int32_t);
+  p->merge_threads = (int64_t)p->nchunk * p->cap <= 512 ? 64 : kThreads;
   p->score_lds = p->chunk * sizeof(uint64_t);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   p->off_idx = al(slots * sizeof(uint64_t));
