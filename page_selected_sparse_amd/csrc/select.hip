@@ -293,23 +293,41 @@ __device__ __forceinline__ void fma4_dpp(double& a0, double& a1, double& a2, dou
         "n"(B + 5), "n"(B + 6), "n"(B + 7));
 }
 
-// Bound of one page for HB (4 or 8) heads. The group's (q+, q-) values for a chunk of CD
-// dims are spread over the lanes of each 16-lane row (value v of the chunk in register
-// v / 16 of lane v % 16, loaded from the LDS table once per chunk) and reach the fp64
-// FMAs through DPP row broadcasts, so no per-dim operand traffic is needed. Each chunk
-// of the page's statistics is one 128-byte line; dims ascend.
+// Bound of one page per lane for HB (4 or 8) heads. The group's (q+, q-) values for a
+// chunk of CD dims are spread over the lanes of each 16-lane row (value v of the chunk in
+// register v / 16 of lane v % 16, loaded from the LDS table once per chunk) and reach the
+// fp64 FMAs through DPP row broadcasts, so no per-dim operand traffic is needed.
+// Statistics lines (128 bytes per page and chunk) are loaded cooperatively and straight
+// into LDS: in each of 8 load instructions, 8 lanes read the 8 pieces of one page's line,
+// so every line is one coalesced request. The wave's `stage` (8 KB) holds its 64 lines
+// with each page's pieces rotated by the page index, so that each lane reads back its own
+// line without bank conflicts. The next chunk's lines land while the current one is
+// accumulated; dims ascend.
 template <bool BF16, int D, int HB>
 __device__ __forceinline__ void bound_dpp(const void* meta, int nb, int hkv, int blk, int g,
-                                          const double* qv, double* acc) {
+                                          const double* qv, uint4* stage, double* acc) {
   using M = MetaGeo<BF16>;
   constexpr int CD = M::CD;
   constexpr int NQ = CD * 2 * HB / 16;  // q registers per chunk
-  const int lane16 = threadIdx.x & 15;
+  constexpr int NCH = D / CD;
+  const int lane = threadIdx.x & 63, lane16 = lane & 15;
+  const int sub = lane & 7;  // which slot of its line this lane fills
   const unsigned char* base = static_cast<const unsigned char*>(meta);
-  auto load = [&](int c, uint4* mv) {
-    const uint4* pc = reinterpret_cast<const uint4*>(base + M::piece(c, nb, hkv, blk, g));
+  // In load step i this lane fills slot `sub` of page 8i + lane / 8 with piece
+  // (sub + page) & 7 of that page's line.
+  int64_t src[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mv[i] = pc[i];
+  for (int i = 0; i < 8; ++i) {
+    const int page = 8 * i + (lane >> 3);
+    src[i] = M::piece(0, nb, hkv, __shfl(blk, page, 64), g) + 16 * ((sub + page) & 7);
+  }
+  const int64_t cstride = (int64_t)nb * hkv * 128;  // bytes between chunks of one line
+  auto load = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(base + src[i] + c * cstride,
+                                       (__attribute__((address_space(3))) void*)(stage + 64 * i),
+                                       16, 0, 0);
   };
   auto accumulate = [&](int c, const uint4* mv) {
     double Q[NQ];
@@ -329,18 +347,19 @@ __device__ __forceinline__ void bound_dpp(const void* meta, int nb, int hkv, int
       }
     }
   };
-  // Two line buffers: the next chunk's line is in flight while one is accumulated. The
-  // loop is kept rolled so that each chunk's q reads stay inside their iteration.
-  constexpr int NCH = D / CD;  // even for every supported D
-  uint4 ma[8], mb[8];
-  load(0, ma);
+  load(0);
+  // kept rolled: the q reads and loads of one chunk stay inside their iteration
 #pragma unroll 1
-  for (int c = 0; c < NCH; c += 2) {
-    load(c + 1, mb);
-    accumulate(c, ma);
-    if (c + 2 < NCH) load(c + 2, ma);
-    accumulate(c + 1, mb);
+  for (int c = 0; c < NCH; ++c) {
+    __builtin_amdgcn_s_waitcnt(0);  // this chunk's lines have landed in LDS
+    uint4 mv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mv[k] = stage[lane * 8 + ((k - lane) & 7)];
+    __builtin_amdgcn_s_waitcnt(0);  // read back before the next lines overwrite the stage
+    if (c + 1 < NCH) load(c + 1);
+    accumulate(c, mv);
   }
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Bound contribution of dims [d0, d0 + DC) of one page for HB heads, with the (q+, q-)
@@ -454,8 +473,9 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
       double acc[HB];
 #pragma unroll
       for (int h = 0; h < HB; ++h) acc[h] = 0.0;
+      uint4* stage = reinterpret_cast<uint4*>(lds + a.chunk * sizeof(uint64_t)) + (tid >> 6) * 512;
       bound_dpp<BF16, D, HB>(a.meta, a.num_blocks, a.Hkv, blk, g,
-                             reinterpret_cast<const double*>(qlds), acc);
+                             reinterpret_cast<const double*>(qlds), stage, acc);
 #pragma unroll
       for (int h = 0; h < HB; ++h)
         if (h < a.G && acc[h] > best) best = acc[h];
@@ -600,6 +620,7 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
                  (size_t)p->nchunk * sizeof(int32_t);
   p->merge_threads = (int64_t)p->nchunk * p->cap <= 512 ? 64 : kThreads;
   p->score_lds = p->chunk * sizeof(uint64_t);
+  if (p->head_block <= 8 && p->all_q) p->score_lds += (size_t)(p->threads / 64) * 8192;  // staging
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   p->off_idx = al(slots * sizeof(uint64_t));
   p->off_cnt = al(p->off_idx + slots * sizeof(int32_t));
