@@ -43,9 +43,13 @@ def algorithmic_bytes(w, sel_counts: np.ndarray) -> dict:
     tail_valid = lens - 16 * (n - 1)
     meta_b = int(np.sum(tail_valid * Hkv * D * es + 2 * Hkv * D * es + 8))  # K tail + stats
     scored = np.where(n > w.budgets, n - 2, 0)  # pages whose bound is computed
-    b_max = int(w.budgets.max())
-    select_b = int(np.sum(scored) * (Hkv * 2 * D * es + 4) + B * Hq * D * es +
-                   B * Hkv * (b_max + 1) * 4 + B * 8)
+    # scoring: statistics and block-table entries of the scored pages, q, and the row
+    # headers; merging: the ranked winners it writes
+    score_b = int(np.sum(scored) * (Hkv * 2 * D * es + 4) + B * Hq * D * es + B * 8 +
+                  B * Hkv * 4)
+    ranked = np.where(n > w.budgets, np.maximum(np.minimum(n, w.budgets), 2) - 2, 0)
+    merge_b = int(np.sum(ranked) * Hkv * 4)
+    select_b = score_b + merge_b
     # valid tokens: every kept page is full except the tail page (always kept)
     kv_tok_valid = int(np.sum(sel_counts.sum(axis=1) * 16 - Hkv * (16 - tail_valid)))
     kdim = D + (0 if sp.latent else Dv)  # latent rows are read once for K and V
@@ -53,9 +57,47 @@ def algorithmic_bytes(w, sel_counts: np.ndarray) -> dict:
                    int(sel_counts.sum()) * 8 + B * Hq * Dv * 4)
     dense_tok = int(np.sum(lens)) * Hkv
     dense_b = int(dense_tok * kdim * es + int(np.sum(n)) * 4 + B * Hq * D * es + B * Hq * Dv * 4)
-    return dict(meta_update=meta_b, select=select_b, sparse_decode=sparse_b,
-                step=meta_b + select_b + sparse_b, dense_decode=dense_b,
-                score_stats=int(np.sum(scored) * Hkv * 2 * D * es))
+    return dict(meta_update=meta_b, select_score=score_b, select_merge=merge_b,
+                select=select_b, sparse_decode=sparse_b, step=meta_b + select_b + sparse_b,
+                dense_decode=dense_b, score_stats=int(np.sum(scored) * Hkv * 2 * D * es))
+
+
+KERNEL_SOURCES = {"score_kernel": "select.hip", "merge_kernel": "select.hip",
+                  "meta_kernel": "meta.hip", "attn_kernel": "attn.hip"}
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 of the HIP source a kernel is built from (with the shared device header)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "page_selected_sparse_amd", "csrc")
+    for f in (KERNEL_SOURCES[kernel], "psd_device.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>_<workload>_hbm_counters.txt (FETCH_SIZE + WRITE_SIZE, scaled by the
+    copy calibration), or None when there is none or the kernel source has changed since
+    the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != source_digest(kernel):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, budget_s: float = 15.0) -> dict:
@@ -154,9 +196,12 @@ def main():
     # The measured region: K whole steps, rotating copies.
     ms_step = timed(lambda st: st.step(), args.steps)
 
-    # Per-call averages (each call timed in its own loop on the launch stream).
+    # Per-call averages, each call timed in its own loop with events on the stream the
+    # kernels are launched on (torch's current stream). Every call below but sparse_decode
+    # is a single kernel; sparse_decode is the attention kernel plus the split merge.
     calls = {"page_meta_update": timed(lambda st: st.refresh_tail(), args.steps),
-             "select_pages": timed(lambda st: st.select(), args.steps),
+             "select_score": timed(lambda st: st.select_score(), args.steps),
+             "select_merge": timed(lambda st: st.select_merge(), args.steps),
              "sparse_decode": timed(lambda st: st.sparse(), args.steps)}
     dense_ms = timed(lambda st: st.dense(), max(10, args.steps // 4)) if not args.no_dense else None
 
@@ -169,11 +214,15 @@ def main():
 
     sel_counts = steps[0].sel_count.cpu().numpy()
     ab = algorithmic_bytes(w, sel_counts)
-    # Dominant call of the step and its achieved algorithmic bandwidth.
-    dom = max(("select_pages", "sparse_decode"), key=lambda k: calls[k])
-    dom_bytes = ab["select"] if dom == "select_pages" else ab["sparse_decode"]
+    # The dominant single-kernel call and its achieved algorithmic bandwidth.
+    kernel_of = {"select_score": ("score_kernel", ab["select_score"]),
+                 "select_merge": ("merge_kernel", ab["select_merge"]),
+                 "page_meta_update": ("meta_kernel", ab["meta_update"])}
+    dom = max(kernel_of, key=lambda k: calls[k])
+    kname, dom_bytes = kernel_of[dom]
     achieved = dom_bytes / (calls[dom] * 1e-3) / 1e9
     step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
+    traffic = measured_traffic(kname, w.spec.name)
 
     result = {
         "metric": METRIC,
@@ -198,9 +247,11 @@ def main():
                    "rotated_copies": R},
         "effective_hbm_gbs": round(step_gbs, 1),
         "effective_hbm_pct_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": kname, "call": dom,
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": dom_bytes, "ms": round(calls[dom], 5),
+                     "traffic": traffic},
         "calls_ms": {k: round(v, 5) for k, v in calls.items()},
         "algorithmic_bytes": ab,
     }

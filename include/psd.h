@@ -160,6 +160,29 @@ psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* m
                             hipStream_t stream);
 
 /*
+ * The two stages of psd_select_pages, for callers that schedule or time them apart.
+ * psd_select_pages(args) is exactly psd_select_score(args) followed, on the same stream,
+ * by psd_select_merge with the same shape, seq_lens, budgets, b_max, sel_pages and
+ * workspace.
+ *
+ * psd_select_score scores every page and ranks each chunk of pages, leaving each chunk's
+ * candidates in the workspace; it writes sel_count and every sel_pages entry except the
+ * ranked winners (sink, tail and -1 padding; whole rows of units that keep every page or
+ * exceed b_max). psd_select_merge reads the candidates back, takes the b-2 winners of
+ * every ranking unit and writes them into sel_pages[..., 1 .. b-2] in ascending order.
+ * The workspace must not be touched between the two calls. Arguments, errors and
+ * sources as for psd_select_pages.
+ */
+psd_status psd_select_score(const psd_shape* shape, const void* q, const void* meta,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
+                            int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+psd_status psd_select_merge(const psd_shape* shape, const int32_t* seq_lens,
+                            const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Workspace bytes psd_sparse_decode (max_pages_attended = its b_max) or psd_dense_decode
  * (max_pages_attended = max_pages_per_seq) needs. 0 if unsupported.
  */

@@ -90,6 +90,23 @@ def select_pages(shape: PsdShape, q, meta, block_table, seq_lens, budgets, b_max
                                        _stream(stream)), "psd_select_pages")
 
 
+def select_score(shape: PsdShape, q, meta, block_table, seq_lens, budgets, b_max: int, sel_pages,
+                 sel_count, workspace, stream=None):
+    _ok(_native.lib().psd_select_score(ctypes.byref(shape), _ptr(q), _ptr(meta),
+                                       _ptr(block_table), _ptr(seq_lens), _ptr(budgets), b_max,
+                                       _ptr(sel_pages), _ptr(sel_count), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream)), "psd_select_score")
+
+
+def select_merge(shape: PsdShape, seq_lens, budgets, b_max: int, sel_pages, workspace,
+                 stream=None):
+    _ok(_native.lib().psd_select_merge(ctypes.byref(shape), _ptr(seq_lens), _ptr(budgets), b_max,
+                                       _ptr(sel_pages), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream)), "psd_select_merge")
+
+
 def decode_workspace_bytes(shape: PsdShape, max_pages_attended: int) -> int:
     return int(_native.lib().psd_decode_workspace_bytes(ctypes.byref(shape), max_pages_attended))
 

@@ -92,23 +92,66 @@ size_t psd_select_workspace_bytes(const psd_shape* shape, int32_t b_max) {
   return p.bytes;
 }
 
-psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* meta,
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the selection calls; fills the geometry and the plan.
+psd_status select_common(const psd_shape* shape, const int32_t* seq_lens,
+                         const int32_t* budgets, int32_t b_max, const int32_t* sel_pages,
+                         const void* workspace, size_t workspace_bytes, psd::Geo* g,
+                         psd::SelectPlan* p) {
+  psd_status st = check_shape(shape, g);
+  if (st != PSD_OK) return st;
+  if (!seq_lens || !budgets || !sel_pages) return PSD_ERR_INVALID_ARG;
+  if (b_max < 2) return PSD_ERR_INVALID_ARG;
+  if (!psd::plan_select(*g, b_max, p)) return PSD_ERR_CAPACITY;
+  if (!workspace || workspace_bytes < p->bytes || !aligned16(workspace)) return PSD_ERR_WORKSPACE;
+  return PSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+psd_status psd_select_score(const psd_shape* shape, const void* q, const void* meta,
                             const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
                             int32_t* sel_count, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   psd::Geo g;
-  psd_status st = check_shape(shape, &g);
-  if (st != PSD_OK) return st;
-  if (!q || !meta || !block_table || !seq_lens || !budgets || !sel_pages || !sel_count)
-    return PSD_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(meta)) return PSD_ERR_INVALID_ARG;
-  if (b_max < 2) return PSD_ERR_INVALID_ARG;
   psd::SelectPlan p;
-  if (!psd::plan_select(g, b_max, &p)) return PSD_ERR_CAPACITY;
-  if (!workspace || workspace_bytes < p.bytes || !aligned16(workspace)) return PSD_ERR_WORKSPACE;
-  return launched(psd::launch_select(g, p, q, meta, block_table, seq_lens, budgets, b_max,
-                                     sel_pages, sel_count, workspace, stream));
+  psd_status st = select_common(shape, seq_lens, budgets, b_max, sel_pages, workspace,
+                                workspace_bytes, &g, &p);
+  if (st != PSD_OK) return st;
+  if (!q || !meta || !block_table || !sel_count) return PSD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(meta)) return PSD_ERR_INVALID_ARG;
+  return launched(psd::launch_select_score(g, p, q, meta, block_table, seq_lens, budgets, b_max,
+                                           sel_pages, sel_count, workspace, stream));
+}
+
+psd_status psd_select_merge(const psd_shape* shape, const int32_t* seq_lens,
+                            const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  psd::Geo g;
+  psd::SelectPlan p;
+  psd_status st = select_common(shape, seq_lens, budgets, b_max, sel_pages, workspace,
+                                workspace_bytes, &g, &p);
+  if (st != PSD_OK) return st;
+  return launched(psd::launch_select_merge(g, p, seq_lens, budgets, b_max, sel_pages, workspace,
+                                           stream));
+}
+
+psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* meta,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
+                            int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  psd_status st = psd_select_score(shape, q, meta, block_table, seq_lens, budgets, b_max,
+                                   sel_pages, sel_count, workspace, workspace_bytes, stream);
+  if (st != PSD_OK) return st;
+  return psd_select_merge(shape, seq_lens, budgets, b_max, sel_pages, workspace,
+                          workspace_bytes, stream);
 }
 
 size_t psd_decode_workspace_bytes(const psd_shape* shape, int32_t max_pages_attended) {

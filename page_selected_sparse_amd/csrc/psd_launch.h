@@ -36,9 +36,15 @@ struct SelectPlan {
 };
 // Returns false when no plan fits (b_max too large).
 bool plan_select(const Geo& g, int b_max, SelectPlan* plan);
-hipError_t launch_select(const Geo& g, const SelectPlan& plan, const void* q, const void* meta,
-                         const int32_t* bt, const int32_t* lens, const int32_t* budgets,
-                         int b_max, int32_t* sel, int32_t* cnt, void* ws, hipStream_t st);
+// Scoring stage: chunk candidates into the workspace and every row entry except the
+// ranked winners. Merge stage: the winners, from the workspace.
+hipError_t launch_select_score(const Geo& g, const SelectPlan& plan, const void* q,
+                               const void* meta, const int32_t* bt, const int32_t* lens,
+                               const int32_t* budgets, int b_max, int32_t* sel, int32_t* cnt,
+                               void* ws, hipStream_t st);
+hipError_t launch_select_merge(const Geo& g, const SelectPlan& plan, const int32_t* lens,
+                               const int32_t* budgets, int b_max, int32_t* sel, void* ws,
+                               hipStream_t st);
 
 // ---- attention -------------------------------------------------------------------------
 struct DecodePlan {

@@ -220,25 +220,24 @@ __device__ __forceinline__ UnitInfo unit_info(const SelArgs& a, int s) {
   return u;
 }
 
-// Prepares a call: zeroed arrival counters and every selection row except the ranked
-// winners (sink, tail, padding and count; the whole row for units that need no ranking;
-// -1 rows for units over capacity).
-__global__ __launch_bounds__(kThreads) void prep_kernel(SelArgs a) {
-  const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
-  const int unit = s * a.Hkv + g;
-  const UnitInfo u = unit_info(a, s);
+// Writes every selection row entry except the ranked winners: sink, tail, padding and
+// count for units that rank; the whole row for units that need no ranking; a -1 row and
+// count for units over capacity (never truncated). NT threads of one workgroup.
+template <int NT>
+__device__ void write_row_header(const SelArgs& a, int unit, const UnitInfo& u) {
+  const int tid = threadIdx.x;
   int32_t* row = a.sel + (int64_t)unit * a.b_max;
-  if (u.b > a.b_max) {  // never truncate: flag the unit
-    for (int i = tid; i < a.b_max; i += kThreads) row[i] = -1;
+  if (u.b > a.b_max) {
+    for (int i = tid; i < a.b_max; i += NT) row[i] = -1;
     if (tid == 0) a.cnt[unit] = -1;
     return;
   }
   if (u.n <= u.b) {
-    for (int i = tid; i < a.b_max; i += kThreads) row[i] = i < u.n ? i : -1;
+    for (int i = tid; i < a.b_max; i += NT) row[i] = i < u.n ? i : -1;
     if (tid == 0) a.cnt[unit] = u.n;
     return;
   }
-  for (int i = u.b + tid; i < a.b_max; i += kThreads) row[i] = -1;
+  for (int i = u.b + tid; i < a.b_max; i += NT) row[i] = -1;
   if (tid == 0) {
     a.cnt[unit] = u.b;
     row[0] = 0;
@@ -441,7 +440,8 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
   const UnitInfo u = unit_info(a, s);
-  if (u.trivial) return;  // rows written by prep_kernel
+  if (c == 0) write_row_header<NT>(a, s * a.Hkv + g, u);
+  if (u.trivial) return;
   const int kp = u.kp, n = u.n;
   const int lo = 1 + c * a.chunk;
   const int hi = min(lo + a.chunk, n - 1);
@@ -539,36 +539,23 @@ hipError_t set_lds(K kernel, size_t lds) {
 }
 
 template <bool BF16, int D, int HB, bool DPP, int NT>
-hipError_t launch_all(const SelArgs& a, const SelectPlan& p, dim3 sgrid, hipStream_t st) {
-  const dim3 ugrid(a.Hkv, sgrid.z);
-  hipLaunchKernelGGL(prep_kernel, ugrid, dim3(kThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
+hipError_t launch_score(const SelArgs& a, const SelectPlan& p, dim3 sgrid, hipStream_t st) {
+  hipError_t e = set_lds(&score_kernel<BF16, D, HB, DPP, NT>, p.score_lds);
   if (e != hipSuccess) return e;
-  if ((e = set_lds(&score_kernel<BF16, D, HB, DPP, NT>, p.score_lds)) != hipSuccess) return e;
   hipLaunchKernelGGL((score_kernel<BF16, D, HB, DPP, NT>), sgrid, dim3(NT), p.score_lds, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // Merge in its own launch: the kernel boundary makes every chunk's candidates visible
-  // (a device-scope fence inside the scoring kernel would write back and invalidate the L2).
-  if (p.merge_threads == 64) {
-    if ((e = set_lds(&merge_kernel<64>, p.merge_lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(merge_kernel<64>, ugrid, dim3(64), p.merge_lds, st, a);
-  } else {
-    if ((e = set_lds(&merge_kernel<kThreads>, p.merge_lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(merge_kernel<kThreads>, ugrid, dim3(kThreads), p.merge_lds, st, a);
-  }
   return hipGetLastError();
 }
 
 template <bool BF16, int D, int HB, bool DPP>
 hipError_t dispatch_nt(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStream_t st) {
-  return p.threads == 64 ? launch_all<BF16, D, HB, DPP, 64>(a, p, grid, st)
-                         : launch_all<BF16, D, HB, DPP, kThreads>(a, p, grid, st);
+  return p.threads == 64 ? launch_score<BF16, D, HB, DPP, 64>(a, p, grid, st)
+                         : launch_score<BF16, D, HB, DPP, kThreads>(a, p, grid, st);
 }
 
 template <bool BF16, int D>
 hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStream_t st) {
   if constexpr (D > 128) {
-    return launch_all<BF16, D, 16, false, kThreads>(a, p, grid, st);
+    return launch_score<BF16, D, 16, false, kThreads>(a, p, grid, st);
   } else {
     switch (p.head_block) {
       case 4: return dispatch_nt<BF16, D, 4, true>(a, p, grid, st);
@@ -628,15 +615,22 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   return true;
 }
 
-hipError_t launch_select(const Geo& g, const SelectPlan& p, const void* q, const void* meta,
+static SelArgs make_args(const Geo& g, const SelectPlan& p, const void* q, const void* meta,
                          const int32_t* bt, const int32_t* lens, const int32_t* budgets,
-                         int b_max, int32_t* sel, int32_t* cnt, void* ws, hipStream_t st) {
+                         int b_max, int32_t* sel, int32_t* cnt, void* ws) {
   unsigned char* w = static_cast<unsigned char*>(ws);
-  SelArgs a{q, meta, bt, lens, budgets,
-            reinterpret_cast<uint64_t*>(w), reinterpret_cast<int32_t*>(w + p.off_idx),
-            reinterpret_cast<int32_t*>(w + p.off_cnt), sel, cnt,
-            g.Hq, g.Hkv, g.G, g.D, g.max_pages, b_max, p.chunk, p.ppt, p.nchunk, p.cap,
-            g.num_blocks};
+  return SelArgs{q, meta, bt, lens, budgets,
+                 reinterpret_cast<uint64_t*>(w), reinterpret_cast<int32_t*>(w + p.off_idx),
+                 reinterpret_cast<int32_t*>(w + p.off_cnt), sel, cnt,
+                 g.Hq, g.Hkv, g.G, g.D, g.max_pages, b_max, p.chunk, p.ppt, p.nchunk, p.cap,
+                 g.num_blocks};
+}
+
+hipError_t launch_select_score(const Geo& g, const SelectPlan& p, const void* q,
+                               const void* meta, const int32_t* bt, const int32_t* lens,
+                               const int32_t* budgets, int b_max, int32_t* sel, int32_t* cnt,
+                               void* ws, hipStream_t st) {
+  const SelArgs a = make_args(g, p, q, meta, bt, lens, budgets, b_max, sel, cnt, ws);
   const dim3 sgrid(p.nchunk, g.Hkv, g.B);
   const bool bf = g.dtype == 1;
   switch (g.D) {
@@ -647,6 +641,26 @@ hipError_t launch_select(const Geo& g, const SelectPlan& p, const void* q, const
     default: return bf ? dispatch_hb<true, 576>(a, p, sgrid, st)
                        : dispatch_hb<false, 576>(a, p, sgrid, st);
   }
+}
+
+// The merge runs as its own launch: the kernel boundary makes every chunk's candidates
+// visible (a device-scope fence inside the scoring kernel writes back and invalidates
+// the L2).
+hipError_t launch_select_merge(const Geo& g, const SelectPlan& p, const int32_t* lens,
+                               const int32_t* budgets, int b_max, int32_t* sel, void* ws,
+                               hipStream_t st) {
+  const SelArgs a = make_args(g, p, nullptr, nullptr, nullptr, lens, budgets, b_max, sel,
+                              nullptr, ws);
+  const dim3 ugrid(g.Hkv, g.B);
+  hipError_t e;
+  if (p.merge_threads == 64) {
+    if ((e = set_lds(&merge_kernel<64>, p.merge_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_kernel<64>, ugrid, dim3(64), p.merge_lds, st, a);
+  } else {
+    if ((e = set_lds(&merge_kernel<kThreads>, p.merge_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_kernel<kThreads>, ugrid, dim3(kThreads), p.merge_lds, st, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace psd

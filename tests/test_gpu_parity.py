@@ -163,3 +163,22 @@ def test_long_1m_dense_sampled_heads():
         err = float(np.max(np.abs(res["dense"][0, 4 * g:4 * g + 4] - ref)))
         print(f"[ok] long_1m dense head group {g}: max abs err {err:.2e}", flush=True)
         assert err <= ATOL
+
+
+def test_selection_stages_compose():
+    """psd_select_score then psd_select_merge gives psd_select_pages' rows exactly."""
+    from page_selected_sparse_amd import DecodeStep
+
+    w = synth.make_workload(SMALL["wide_batch"])
+    step = DecodeStep.from_arrays(w.q, w.cache, w.block_table, w.seq_lens, w.budgets,
+                                  w.spec.dtype, w.spec.head_dim_v, w.spec.latent)
+    step.build_meta()
+    step.select()
+    torch.cuda.synchronize()
+    sel, cnt = step.sel_pages.clone(), step.sel_count.clone()
+    step.sel_pages.fill_(-7)
+    step.sel_count.fill_(-7)
+    step.select_score()
+    step.select_merge()
+    torch.cuda.synchronize()
+    assert torch.equal(step.sel_pages, sel) and torch.equal(step.sel_count, cnt)
