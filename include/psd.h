@@ -92,14 +92,14 @@ typedef struct psd_shape {
 
 /*
  * Page statistics layout (`meta`), in `dtype`, indexed by PHYSICAL block like the cache:
- *   [head_dim / CD][num_blocks][num_kv_heads][2][CD],  CD = 64 bytes of dims
+ *   [num_blocks][num_kv_heads][head_dim / CD][2][CD],  CD = 64 bytes of dims
  *   (32 for bf16, 16 for fp32),
- * i.e. the per-dim minimum (plane 0) and maximum (plane 1) of a page's valid keys, cut
- * into chunks of CD dims; the minima and maxima of one chunk of one (block, head) form
- * one 128-byte line. Total size: 2 * num_blocks * num_kv_heads * head_dim elements.
- * Values are exact (copied key values).
+ * i.e. the per-dim minimum (index 0) and maximum (index 1) of a page's valid keys, cut
+ * into chunks of CD dims; the minima and maxima of one chunk form one 128-byte line and
+ * the lines of one (block, head) are one contiguous record of 2 * head_dim elements.
+ * Total size: 2 * num_blocks * num_kv_heads * head_dim elements. Values are exact
+ * (copied key values).
  */
-
 /*
  * psd_page_meta_update - recompute page statistics from the cached keys.
  *

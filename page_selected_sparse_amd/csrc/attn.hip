@@ -42,6 +42,8 @@ struct AttnArgs {
   float sl2;  // scale * log2(e)
 };
 
+constexpr int kMaxSplits = 16384;
+
 struct MergeArgs {
   const int32_t* lens;
   const int32_t* cnt;  // nullptr: dense
@@ -325,8 +327,31 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
   if (grp == 0 && hvalid) a.pml[(ubase + head) * a.nsplit + split] = make_float2(m_run, l_run);
 }
 
-__global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
-  extern __shared__ float wts[];  // [nsplit + 1]
+template <int NT>
+__device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) {
+  constexpr int NW = NT / 64;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float y = __shfl_xor(x, off, 64);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) x = is_max ? fmaxf(x, red[i]) : x + red[i];
+  __syncthreads();
+  return x;
+}
+
+// One workgroup per (query head, sequence). The split weights 2^(m_i - M) are computed
+// in parallel; the weighted sum of the partial accumulators is cut into slices of splits
+// (thread = (slice, 4 dims)), so that many independent loads are in flight, and the
+// slices are summed through LDS.
+template <int NT>
+__global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a) {
+  extern __shared__ float sh[];  // weights [nsplit] | slice sums [slices][Dv]
+  __shared__ float red[NT / 64];
   const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int g = h / a.G;
   const int L = a.lens[s];
@@ -334,30 +359,55 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
   const int count = a.cnt ? min(a.cnt[s * a.Hkv + g], a.b_max) : n;
   float* out = a.out + ((int64_t)s * a.Hq + h) * a.Dv;
   if (count <= 0) {
-    for (int d = tid; d < a.Dv; d += blockDim.x) out[d] = __builtin_nanf("");
+    for (int d = tid; d < a.Dv; d += NT) out[d] = __builtin_nanf("");
     return;
   }
   const int nsp = ceil_div(count, a.pps);
   const int64_t row = ((int64_t)s * a.Hq + h) * a.nsplit;
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int i = 0; i < nsp; ++i) M = fmaxf(M, a.pml[row + i].x);
-    float Ls = 0.f;
-    for (int i = 0; i < nsp; ++i) {
-      const float2 ml = a.pml[row + i];
-      const float w = exp2f(ml.x - M);
-      wts[i] = w;
-      Ls += ml.y * w;
+  float m = -INFINITY;
+  for (int i = tid; i < nsp; i += NT) m = fmaxf(m, a.pml[row + i].x);
+  const float M = block_reduce<NT>(m, red, true);
+  float* wts = sh;
+  float l = 0.f;
+  for (int i = tid; i < nsp; i += NT) {
+    const float2 ml = a.pml[row + i];
+    const float w = exp2f(ml.x - M);
+    wts[i] = w;
+    l += ml.y * w;
+  }
+  const float inv = 1.f / block_reduce<NT>(l, red, false);  // also publishes wts
+  const int v4 = a.Dv / 4;
+  const int slices = NT / v4;
+  const int slice = tid / v4, c = tid - slice * v4;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (slice < slices) {
+    const float4* acc = reinterpret_cast<const float4*>(a.pacc) + row * v4 + c;
+#pragma unroll 4
+    for (int i = slice; i < nsp; i += slices) {
+      const float4 x = acc[(int64_t)i * v4];
+      const float w = wts[i];
+      o.x += x.x * w;
+      o.y += x.y * w;
+      o.z += x.z * w;
+      o.w += x.w * w;
     }
-    wts[nsp] = 1.f / Ls;
   }
-  __syncthreads();
-  const float inv = wts[nsp];
-  for (int d = tid; d < a.Dv; d += blockDim.x) {
-    float o = 0.f;
-    for (int i = 0; i < nsp; ++i) o += a.pacc[(row + i) * a.Dv + d] * wts[i];
-    out[d] = o * inv;
+  float4* part = reinterpret_cast<float4*>(sh + ((a.nsplit + 3) & ~3));
+  if (slices > 1) {
+    if (slice < slices) part[slice * v4 + c] = o;
+    __syncthreads();
+    if (tid < v4) {
+      for (int j = 1; j < slices; ++j) {
+        const float4 x = part[j * v4 + tid];
+        o.x += x.x;
+        o.y += x.y;
+        o.z += x.z;
+        o.w += x.w;
+      }
+    }
   }
+  if (tid < v4)
+    reinterpret_cast<float4*>(out)[tid] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }
 
 template <bool BF16, int DQK, int DV>
@@ -388,6 +438,7 @@ bool plan_decode(const Geo& g, int max_pages_attended, DecodePlan* p) {
   pps = pps < lo ? lo : (pps > 64 ? 64 : pps);
   p->pps = (int)pps;
   p->nsplit = (max_pages_attended + p->pps - 1) / p->pps;
+  if (p->nsplit > kMaxSplits) return false;  // the merge keeps one weight per split in LDS
   const size_t parts = (size_t)g.B * g.Hq * p->nsplit;
   p->off_ml = (parts * g.Dv * sizeof(float) + 255) / 256 * 256;
   p->bytes = p->off_ml + parts * sizeof(float2) + 256;
@@ -418,9 +469,22 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
   if (e != hipSuccess) return e;
   MergeArgs m{lens, sel ? cnt : nullptr, a.pacc, a.pml, out, g.Hq, g.Hkv, g.G, p.pps,
               p.nsplit, g.Dv, b_max};
-  const int threads = g.Dv >= 256 ? 256 : g.Dv;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(g.Hq, g.B), dim3(threads),
-                     (p.nsplit + 1) * sizeof(float), st, m);
+  // wider workgroups when there are many splits to combine
+  const int nt = p.nsplit > 32 ? 1024 : 256;
+  const size_t lds = ((p.nsplit + 3) & ~3) * sizeof(float) + (size_t)nt * 4 * sizeof(float);
+  if (nt == 1024) {
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lse_merge_kernel<1024>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
+        hipSuccess)
+      return e;
+    hipLaunchKernelGGL(lse_merge_kernel<1024>, dim3(g.Hq, g.B), dim3(1024), lds, st, m);
+  } else {
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lse_merge_kernel<256>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
+        hipSuccess)
+      return e;
+    hipLaunchKernelGGL(lse_merge_kernel<256>, dim3(g.Hq, g.B), dim3(256), lds, st, m);
+  }
   return hipGetLastError();
 }
 

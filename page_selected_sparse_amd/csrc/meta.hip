@@ -6,9 +6,9 @@
 // thread owns 16 contiguous bytes of a row, requests all 16 rows at once and folds the
 // page's valid tokens. Loads are coalesced across the workgroup (consecutive threads read
 // consecutive 16-byte pieces of a token row) and each statistic is written once. Min/max
-// are exact, so the values written are key values themselves. The statistics are stored
-// chunk-major so that the min and max of 64 bytes' worth of dims of one (block, head) form
-// one 128-byte line (the unit the scoring kernel reads).
+// are exact, so the values written are key values themselves. The statistics of one
+// (block, head) are one contiguous record of 128-byte lines, each holding the min and the
+// max of 64 bytes' worth of dims (the unit the scoring kernel reads back).
 #include "psd_device.h"
 #include "psd_launch.h"
 
@@ -77,9 +77,9 @@ __global__ __launch_bounds__(256) void meta_kernel(MetaArgs a) {
         }
       }
     }
-    // chunk-major statistics: [D / CD][num_blocks][H_kv][2][CD], CD = 64 bytes of dims
+    // page-major statistics: [num_blocks][H_kv][D / CD][2][CD], CD = 64 bytes of dims
     constexpr int CD = BF16 ? 32 : 16;
-    const int64_t mrow = (((int64_t)(d / CD) * a.num_blocks + blk) * a.Hkv + h) * 2 * CD + d % CD;
+    const int64_t mrow = (((int64_t)blk * a.Hkv + h) * (a.D / CD) + d / CD) * 2 * CD + d % CD;
     if constexpr (BF16) {
       uint16_t* m = static_cast<uint16_t*>(a.meta);
       uint4 lo, hi;

@@ -37,6 +37,7 @@ __device__ __forceinline__ uint64_t score_key(double x) {
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int round_up(int a, int b) { return ceil_div(a, b) * b; }
 
 // Pages attended by a unit with n pages and the caller's budget.
 __device__ __forceinline__ int effective_budget(int n, int budget) {

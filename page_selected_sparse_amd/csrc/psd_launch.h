@@ -18,17 +18,20 @@ hipError_t launch_meta_update(const Geo& g, const void* k, void* meta, const int
                               const int32_t* lens, const int32_t* first_page, hipStream_t st);
 
 // ---- selection --------------------------------------------------------------------------
-// Chunking of the candidate pages 1..n-2 of a unit for the two-level top-b.
+// Chunking of the candidate pages 1..n-2 of a unit for the two-level top-b. A plan with
+// nchunk == 1 scores and ranks every unit in one workgroup and needs no merge.
 struct SelectPlan {
-  int chunk;       // candidate pages per scoring workgroup (threads * pages_per_thread)
+  int chunk;       // candidate pages per scoring workgroup (threads * ppt)
   int threads;     // threads per scoring workgroup
   int ppt;         // pages per thread
   int nchunk;      // chunks covering max_pages - 2 candidates
   int cap;         // candidate slots per chunk = min(chunk, b_max - 2)
+  int ustride;     // candidate slots per unit in the workspace
+  int cpl;         // statistics chunks per load group (DPP path)
+  int stages;      // load groups in flight per wave (DPP path)
   int head_block;  // query heads scored per pass (template width)
   int d_chunk;     // dims of q staged in LDS per pass (LDS q path)
   bool all_q;           // whole (q+, q-) table of the group in LDS
-  int pages_per_lane;   // pages scored together per thread (all_q plans)
   int merge_threads;  // threads of the per-unit merge workgroup
   size_t off_idx, off_cnt, bytes;  // workspace layout
   size_t merge_lds;  // LDS of a unit merge

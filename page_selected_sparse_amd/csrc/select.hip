@@ -16,18 +16,18 @@
 //
 // Selection (EntmaxKV README, top-k with the budget counting the always-kept tail page;
 // LOCKS README, introduction and "Results": sink and most-recent pages kept, counted
-// inside b) is two-level so that a unit with tens of thousands of pages still spreads
-// over many workgroups:
-//   1. score_kernel: a workgroup scores a chunk of candidate pages (1..n-2) of one
-//      (sequence, KV head) unit, finds the chunk's top-(b-2) by (score desc, page asc)
-//      with an LDS radix select on order-preserving 64-bit keys, and writes them in
-//      page order.
+// inside b) ranks pages by (score desc, page asc) with an LDS radix select on
+// order-preserving 64-bit keys. When there are enough (sequence, KV head) units to fill
+// the GPU and a unit has at most 2048 candidate pages, one workgroup scores all of a
+// unit's pages and writes its row directly. Otherwise selection is two-level, so that a
+// unit with tens of thousands of pages still spreads over many workgroups:
+//   1. score_kernel: a workgroup scores a chunk of candidate pages (1..n-2) of one unit,
+//      finds the chunk's top-(b-2) and writes them in page order to the workspace.
 //   2. merge_kernel: a workgroup per unit concatenates the chunk candidates (still in
-//      page order), radix-selects the global top-(b-2), and writes sink, the winners
-//      and the tail in ascending page order.
+//      page order), radix-selects the global top-(b-2), and writes them into the row.
 // The global top-(b-2) is contained in the union of the chunk top-(b-2) lists, since a
 // page outranked by fewer than b-2 pages overall is outranked by fewer than b-2 pages of
-// its own chunk.
+// its own chunk. Sink, tail, padding and counts are written by the scoring kernel.
 #include "psd_device.h"
 #include "psd_launch.h"
 
@@ -46,12 +46,13 @@ struct SelArgs {
   const int32_t* bt;
   const int32_t* lens;
   const int32_t* budgets;
-  uint64_t* ckey;    // [unit][nchunk][cap] chunk candidates (order-preserving keys)
-  int32_t* cidx;     // [unit][nchunk][cap] their logical pages
+  uint64_t* ckey;    // [unit][ustride] chunk candidates (order-preserving keys), chunk-major
+  int32_t* cidx;     // [unit][ustride] their logical pages
   int32_t* ccnt;     // [unit][nchunk] candidates written per chunk
   int32_t* sel;
   int32_t* cnt;
   int Hq, Hkv, G, D, max_pages, b_max, chunk, ppt, nchunk, cap, num_blocks;
+  int ustride;  // candidate slots per unit: nchunk * cap rounded up to 1 KB of keys
 };
 
 struct SelScratch {
@@ -69,32 +70,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
     if (lane >= off) x += y;
   }
   return x;
-}
-
-// Exclusive count of `flag` over the threads before this one (thread order), and the
-// total, for an NT-thread workgroup. Contains barriers: every thread must call it.
-template <int NT>
-__device__ __forceinline__ int block_excl_count(bool flag, SelScratch& sc, int& total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint64_t m = __ballot(flag);
-  const int below = __popcll(m & ((1ull << lane) - 1ull));
-  if constexpr (NW == 1) {
-    total = __popcll(m);
-    return below;
-  }
-  if (lane == 0) sc.wave_cnt[w] = __popcll(m);
-  __syncthreads();
-  int off = 0;
-  total = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int c = sc.wave_cnt[i];
-    off += i < w ? c : 0;
-    total += c;
-  }
-  __syncthreads();
-  return off + below;
 }
 
 // Finds the top K (1 <= K <= N) of keys[0..N) in LDS by radix select over 8-bit digits
@@ -172,27 +147,80 @@ __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch
   need = k;
 }
 
+// Exclusive prefix sum of x over the threads of an NT-thread workgroup (thread order),
+// and the total. Contains barriers: every thread must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_sum(int x, SelScratch& sc, int& total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = wave_inclusive_scan(x);
+  if constexpr (NW == 1) {
+    total = __shfl(incl, 63, 64);
+    return incl - x;
+  }
+  if (lane == 63) sc.wave_cnt[w] = incl;
+  __syncthreads();
+  int off = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int c = sc.wave_cnt[i];
+    off += i < w ? c : 0;
+    total += c;
+  }
+  __syncthreads();
+  return off + incl - x;
+}
+
 // Emits, in position order, every key with (key & M) > P and the first `need` keys with
-// (key & M) == P; calls out(rank, position) for each. Returns the number emitted. Every
-// thread must call it.
+// (key & M) == P; calls out(rank, position) for each. Each thread owns one contiguous
+// segment of positions: it counts its keys above and at the threshold, two block scans
+// give its first rank, and it writes its picks. Returns the number emitted. Every thread
+// must call it.
 template <int NT, typename Out>
 __device__ int block_emit_top(const uint64_t* keys, int N, uint64_t P, uint64_t M, int need,
                               SelScratch& sc, Out out) {
-  int run_eq = 0, run_out = 0;
-  for (int base = 0; base < N; base += NT) {
-    const int i = base + threadIdx.x;
-    const bool ok = i < N;
-    const uint64_t key = ok ? (keys[i] & M) : 0;
-    const bool gt = ok && key > P, eq = ok && key == P;
-    int tot_eq, tot_sel;
-    const int eq_rank = run_eq + block_excl_count<NT>(eq, sc, tot_eq);
-    const bool pick = gt || (eq && eq_rank < need);
-    const int pos = run_out + block_excl_count<NT>(pick, sc, tot_sel);
-    if (pick) out(pos, i);
-    run_eq += tot_eq;
-    run_out += tot_sel;
+  const int per = ceil_div(N, NT);
+  const int b0 = min((int)threadIdx.x * per, N), e0 = min(b0 + per, N);
+  int gt = 0, eq = 0;
+  for (int i = b0; i < e0; ++i) {
+    const uint64_t key = keys[i] & M;
+    gt += key > P;
+    eq += key == P;
   }
-  return run_out;
+  int tot;
+  const int eq_before = block_excl_sum<NT>(eq, sc, tot);
+  const int eq_take = min(max(need - eq_before, 0), eq);
+  int emitted;
+  int pos = block_excl_sum<NT>(gt + eq_take, sc, emitted);
+  int eq_seen = 0;
+  for (int i = b0; i < e0; ++i) {
+    const uint64_t key = keys[i] & M;
+    bool pick = key > P;
+    if (key == P) pick = eq_seen++ < eq_take;
+    if (pick) out(pos++, i);
+  }
+  return emitted;
+}
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8),
+// each waiting on one counter only.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Waits until at most 8 * n vector memory operations of this wave are outstanding.
+__device__ __forceinline__ void wait_vm8(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<8>(); break;
+    case 2: wait_vm<16>(); break;
+    case 3: wait_vm<24>(); break;
+    default: wait_vm<32>(); break;
+  }
 }
 
 template <bool BF16>
@@ -260,15 +288,16 @@ __device__ __forceinline__ double chunk_elem(const uint4* v, int j) {
   }
 }
 
-// Statistics are chunk-major: [D / CD][num_blocks][H_kv][2][CD] with CD = 64 bytes of
-// dims, so the minima and maxima of CD dims of one (block, head) are one 128-byte line.
+// Statistics are page-major: [num_blocks][H_kv][D / CD][2][CD] with CD = 64 bytes of
+// dims, so the minima and maxima of CD dims of one (block, head) form one 128-byte line
+// and the NCH = D / CD lines of a (block, head) record are contiguous.
 template <bool BF16>
 struct MetaGeo {
   static constexpr int ES = BF16 ? 2 : 4;
   static constexpr int CD = 64 / ES;  // dims per chunk
   // byte offset of chunk c of (block, head)
-  __device__ static int64_t piece(int c, int nb, int hkv, int blk, int g) {
-    return (((int64_t)c * nb + blk) * hkv + g) * 128;
+  __device__ static int64_t piece(int c, int nch, int hkv, int blk, int g) {
+    return (((int64_t)blk * hkv + g) * nch + c) * 128;
   }
 };
 
@@ -292,41 +321,79 @@ __device__ __forceinline__ void fma4_dpp(double& a0, double& a1, double& a2, dou
         "n"(B + 5), "n"(B + 6), "n"(B + 7));
 }
 
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// Reads one 128-byte statistics line of this lane's page back from the stage: piece k
+// (16 bytes) sits in slot (first + k) mod SL of the page's SL-slot region `page`. Waits
+// for the reads. Written as one asm block: the compiler would otherwise make every LDS
+// read wait for all loads still streaming into the stages.
+template <int SL>
+__device__ __forceinline__ void read_line(const uint4* page, int first, uint4 (&mv)[8]) {
+  const uint32_t b = (uint32_t)(uintptr_t)page;
+  uint32_t a[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = b + 16u * (uint32_t)((first + k) & (SL - 1));
+  u32x4 r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+  const u32x4 r[8] = {r0, r1, r2, r3, r4, r5, r6, r7};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) mv[k] = make_uint4(r[k].x, r[k].y, r[k].z, r[k].w);
+}
+
 // Bound of one page per lane for HB (4 or 8) heads. The group's (q+, q-) values for a
 // chunk of CD dims are spread over the lanes of each 16-lane row (value v of the chunk in
 // register v / 16 of lane v % 16, loaded from the LDS table once per chunk) and reach the
 // fp64 FMAs through DPP row broadcasts, so no per-dim operand traffic is needed.
-// Statistics lines (128 bytes per page and chunk) are loaded cooperatively and straight
-// into LDS: in each of 8 load instructions, 8 lanes read the 8 pieces of one page's line,
-// so every line is one coalesced request. The wave's `stage` (8 KB) holds its 64 lines
-// with each page's pieces rotated by the page index, so that each lane reads back its own
-// line without bank conflicts. The next chunk's lines land while the current one is
-// accumulated; dims ascend.
-template <bool BF16, int D, int HB>
-__device__ __forceinline__ void bound_dpp(const void* meta, int nb, int hkv, int blk, int g,
+// Statistics are loaded cooperatively and straight into LDS in groups of C chunks: each
+// load instruction moves 1 KB, 8 / C pages' C contiguous lines, so that each page's
+// record is fetched as one contiguous request. In a page's region of the stage its 8C
+// pieces are rotated by the page index, so that the 64 lanes read their own lines back
+// without bank conflicts. S groups are in flight while one is accumulated; dims ascend.
+template <bool BF16, int D, int HB, int CPL, int S>
+__device__ __forceinline__ void bound_dpp(const void* meta, int hkv, int blk, int g,
                                           const double* qv, uint4* stage, double* acc) {
   using M = MetaGeo<BF16>;
   constexpr int CD = M::CD;
   constexpr int NQ = CD * 2 * HB / 16;  // q registers per chunk
   constexpr int NCH = D / CD;
+  constexpr int C = CPL < NCH ? CPL : NCH;  // chunks per load group
+  constexpr int NG = NCH / C;               // load groups
+  constexpr int SS = S < NG ? S : NG;       // groups in flight
+  constexpr int SL = 8 * C;                 // 16-byte slots per page in a group
+  constexpr int NI = SL;                    // 1 KB load instructions per group
+  constexpr int PPI = 8 / C;                // pages per load instruction
+  constexpr int GB = 64 * SL;               // uint4 per group stage (64 pages)
+  static_assert(NCH % C == 0 && (SS == 1 || SS == 2), "load grouping");
   const int lane = threadIdx.x & 63, lane16 = lane & 15;
-  const int sub = lane & 7;  // which slot of its line this lane fills
   const unsigned char* base = static_cast<const unsigned char*>(meta);
-  // In load step i this lane fills slot `sub` of page 8i + lane / 8 with piece
-  // (sub + page) & 7 of that page's line.
-  int64_t src[8];
+  const uint32_t own = (uint32_t)blk * (uint32_t)hkv + (uint32_t)g;  // record of this page
+  // Load instruction i: this lane fetches piece (slot - page) mod SL of page
+  // i * PPI + lane / SL into slot lane % SL of that page's region.
+  uint32_t rec[NI];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int page = 8 * i + (lane >> 3);
-    src[i] = M::piece(0, nb, hkv, __shfl(blk, page, 64), g) + 16 * ((sub + page) & 7);
-  }
-  const int64_t cstride = (int64_t)nb * hkv * 128;  // bytes between chunks of one line
-  auto load = [&](int c) {
+  for (int i = 0; i < NI; ++i) rec[i] = __shfl(own, i * PPI + lane / SL, 64);
+  auto load = [&](int grp, uint4* st) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(base + src[i] + c * cstride,
-                                       (__attribute__((address_space(3))) void*)(stage + 64 * i),
+    for (int i = 0; i < NI; ++i) {
+      const int page = i * PPI + lane / SL;
+      const int piece = ((lane % SL) - page) & (SL - 1);
+      const unsigned char* src =
+          base + (uint64_t)rec[i] * (NCH * 128) + (grp * C * 128 + piece * 16);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(st + 64 * i),
                                        16, 0, 0);
+    }
   };
   auto accumulate = [&](int c, const uint4* mv) {
     double Q[NQ];
@@ -346,25 +413,28 @@ __device__ __forceinline__ void bound_dpp(const void* meta, int nb, int hkv, int
       }
     }
   };
-  load(0);
-  // kept rolled: the q reads and loads of one chunk stay inside their iteration
-#pragma unroll 1
-  for (int c = 0; c < NCH; ++c) {
-    __builtin_amdgcn_s_waitcnt(0);  // this chunk's lines have landed in LDS
-    uint4 mv[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) mv[k] = stage[lane * 8 + ((k - lane) & 7)];
-    __builtin_amdgcn_s_waitcnt(0);  // read back before the next lines overwrite the stage
-    if (c + 1 < NCH) load(c + 1);
-    accumulate(c, mv);
+  for (int j = 0; j < SS; ++j) load(j, stage + GB * j);
+  // kept rolled: the q reads and loads of one group stay inside their iteration
+#pragma unroll 1
+  for (int j = 0; j < NG; ++j) {
+    // group j has landed once only the groups issued after it are outstanding
+    wait_vm8(min(SS - 1, NG - 1 - j) * C);
+    uint4* st = stage + GB * (j & (SS - 1)) + lane * SL;  // this lane's page region
+#pragma unroll 1
+    for (int cc = 0; cc < C; ++cc) {
+      uint4 mv[8];
+      read_line<SL>(st, cc * 8 + lane, mv);
+      if (cc == C - 1 && j + SS < NG) load(j + SS, stage + GB * (j & (SS - 1)));
+      accumulate(j * C + cc, mv);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Bound contribution of dims [d0, d0 + DC) of one page for HB heads, with the (q+, q-)
 // table of those dims staged in LDS and read as broadcasts; dims ascend.
 template <bool BF16, int DC, int HB>
-__device__ __forceinline__ void bound_lds(const void* meta, int nb, int hkv, int blk, int g,
+__device__ __forceinline__ void bound_lds(const void* meta, int nch, int hkv, int blk, int g,
                                           int d0, const double2* qt, double* acc) {
   using M = MetaGeo<BF16>;
   constexpr int CD = M::CD;
@@ -373,7 +443,7 @@ __device__ __forceinline__ void bound_lds(const void* meta, int nb, int hkv, int
 #pragma unroll
   for (int dd = 0; dd < DC; dd += PER) {
     const int d = d0 + dd;
-    const unsigned char* pc = base + M::piece(d / CD, nb, hkv, blk, g) + (d % CD) * M::ES;
+    const unsigned char* pc = base + M::piece(d / CD, nch, hkv, blk, g) + (d % CD) * M::ES;
     const uint4 av = *reinterpret_cast<const uint4*>(pc);
     const uint4 bv = *reinterpret_cast<const uint4*>(pc + 64);
 #pragma unroll
@@ -389,6 +459,20 @@ __device__ __forceinline__ void bound_lds(const void* meta, int nb, int hkv, int
   }
 }
 
+// Copies `bytes` (a multiple of 16) from global memory to LDS with every load in flight at
+// once (loads straight into LDS, 16 bytes per lane), then waits for them.
+template <int NT>
+__device__ __forceinline__ void copy_to_lds(const void* src, void* dst, int bytes) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned char* g = static_cast<const unsigned char*>(src);
+  unsigned char* l = static_cast<unsigned char*>(dst);
+  for (int off = w * 1024; off < bytes; off += NT * 16) {
+    // a whole wave's 1 KB slice is in bounds: callers pad to 1 KB
+    __builtin_amdgcn_global_load_lds(g + off + lane * 16,
+                                     (__attribute__((address_space(3))) void*)(l + off), 16, 0, 0);
+  }
+}
+
 // Global top-kp of one unit from its chunk candidate lists, written to row[1 .. kp] in
 // ascending page order. The unit's slots are copied as one block (chunk-major, so in page
 // order); slots past a chunk's count get key 0, below every score key. When every chunk
@@ -401,16 +485,15 @@ __device__ void merge_unit(const SelArgs& a, int unit, int n, int kp, unsigned c
   const int nch = ceil_div(n - 2, a.chunk);
   const int total = nch * a.cap;
   const bool dense = a.cap == a.chunk;
+  const int ustride = a.ustride;
   uint64_t* keys = reinterpret_cast<uint64_t*>(lds);
-  int32_t* idx = reinterpret_cast<int32_t*>(lds + sizeof(uint64_t) * (size_t)a.nchunk * a.cap);
-  int* cnts = reinterpret_cast<int*>(idx + (size_t)a.nchunk * a.cap);
-  const int64_t src = (int64_t)unit * a.nchunk * a.cap;
+  int32_t* idx = reinterpret_cast<int32_t*>(lds + sizeof(uint64_t) * (size_t)ustride);
+  int* cnts = reinterpret_cast<int*>(idx + ustride);
+  const int64_t src = (int64_t)unit * ustride;
+  copy_to_lds<NT>(a.ckey + src, keys, round_up(total * 8, 1024));
+  if (!dense) copy_to_lds<NT>(a.cidx + src, idx, round_up(total * 4, 1024));
   for (int c = tid; c < nch; c += NT) cnts[c] = a.ccnt[(int64_t)unit * a.nchunk + c];
-#pragma unroll 4
-  for (int j = tid; j < total; j += NT) {
-    keys[j] = a.ckey[src + j];
-    if (!dense) idx[j] = a.cidx[src + j];
-  }
+  wait_vm<0>();
   __syncthreads();
   for (int j = tid; j < total; j += NT) {
     const int c = j / a.cap;
@@ -424,14 +507,20 @@ __device__ void merge_unit(const SelArgs& a, int unit, int n, int kp, unsigned c
                      [&](int pos, int i) { row[1 + pos] = dense ? i + 1 : idx[i]; });
 }
 
-// One workgroup scores one chunk of a unit's candidate pages 1..n-2, one page per thread.
-// DPP (groups of up to 8 heads, D <= 128): the whole (q+, q-) table in LDS, fed to the
-// FMAs by row broadcasts. Otherwise the table is staged 16 heads x DC dims at a time and
-// read as LDS broadcasts.
-template <bool BF16, int D, int HB, bool DPP, int NT>
+// One workgroup scores one chunk of a unit's candidate pages 1..n-2, one page per lane
+// and round (ppt rounds of NT pages). DPP (groups of up to 8 heads, D <= 128): the whole
+// (q+, q-) table in LDS, fed to the FMAs by row broadcasts, statistics staged S chunks
+// deep per wave. Otherwise the table is staged 16 heads x DC dims at a time and read as
+// LDS broadcasts. When a unit has a single chunk, its top-kp is final and goes straight
+// into the selection row; otherwise the chunk's candidates go to the workspace.
+template <bool BF16, int D, int HB, bool DPP, int NT, int CPL, int S>
 __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   constexpr int DC = DPP ? D : ((HB * D * 16 <= 32768) ? D : 32);
   constexpr int NDC = D / DC;
+  constexpr int NCH = D / MetaGeo<BF16>::CD;
+  constexpr int CC = CPL < NCH ? CPL : NCH;
+  constexpr int SS = S < NCH / CC ? S : NCH / CC;
+  constexpr int STAGE = 512 * CC * SS;  // uint4 per wave
   __shared__ double2 qlds[DC * HB];
   __shared__ SelScratch sc;
   extern __shared__ unsigned char lds[];
@@ -439,15 +528,15 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
 
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
+  const int unit = s * a.Hkv + g;
   const UnitInfo u = unit_info(a, s);
-  if (c == 0) write_row_header<NT>(a, s * a.Hkv + g, u);
+  if (c == 0) write_row_header<NT>(a, unit, u);
   if (u.trivial) return;
   const int kp = u.kp, n = u.n;
   const int lo = 1 + c * a.chunk;
   const int hi = min(lo + a.chunk, n - 1);
   if (lo >= hi) return;
   const int cnt = hi - lo;
-  const int unit = s * a.Hkv + g;
   const int nhp = ceil_div(a.G, HB);
 
   auto load_qlds = [&](int hp, int dc) {
@@ -466,16 +555,20 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   const int64_t bt0 = (int64_t)s * a.max_pages;
   for (int it = 0; it < a.ppt; ++it) {
     const int o = it * NT + tid;
+    if constexpr (DPP) {
+      // a wave with no page left in the chunk skips the round (no barrier inside)
+      if (it * NT + (tid & ~63) >= cnt) continue;
+    }
     const bool have = o < cnt;
-    const int blk = a.bt[bt0 + (have ? lo + o : 0)];
+    const int blk = a.bt[bt0 + (have ? lo + o : lo)];
     double best = -__builtin_inf();
     if constexpr (DPP) {
       double acc[HB];
 #pragma unroll
       for (int h = 0; h < HB; ++h) acc[h] = 0.0;
-      uint4* stage = reinterpret_cast<uint4*>(lds + a.chunk * sizeof(uint64_t)) + (tid >> 6) * 512;
-      bound_dpp<BF16, D, HB>(a.meta, a.num_blocks, a.Hkv, blk, g,
-                             reinterpret_cast<const double*>(qlds), stage, acc);
+      uint4* stage = reinterpret_cast<uint4*>(lds + a.chunk * sizeof(uint64_t)) + (tid >> 6) * STAGE;
+      bound_dpp<BF16, D, HB, CPL, S>(a.meta, a.Hkv, blk, g, reinterpret_cast<const double*>(qlds),
+                                     stage, acc);
 #pragma unroll
       for (int h = 0; h < HB; ++h)
         if (h < a.G && acc[h] > best) best = acc[h];
@@ -490,7 +583,7 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
             load_qlds(hp, dc);
             __syncthreads();
           }
-          bound_lds<BF16, DC, HB>(a.meta, a.num_blocks, a.Hkv, blk, g, dc * DC, qlds, acc);
+          bound_lds<BF16, DC, HB>(a.meta, NCH, a.Hkv, blk, g, dc * DC, qlds, acc);
         }
 #pragma unroll
         for (int h = 0; h < HB; ++h)
@@ -501,9 +594,17 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   }
   __syncthreads();
 
+  if (a.nchunk == 1) {  // the chunk is the whole unit: its top-kp is the selection
+    int32_t* row = a.sel + (int64_t)unit * a.b_max;
+    uint64_t P, M;
+    int need;
+    block_kth_largest<NT>(keys, cnt, kp, sc, P, M, need);
+    block_emit_top<NT>(keys, cnt, P, M, need, sc, [&](int pos, int i) { row[1 + pos] = 1 + i; });
+    return;
+  }
   // Chunk candidates: all pages when they fit in kp, else the chunk's top-kp.
-  uint64_t* okey = a.ckey + ((int64_t)unit * a.nchunk + c) * a.cap;
-  int32_t* oidx = a.cidx + ((int64_t)unit * a.nchunk + c) * a.cap;
+  uint64_t* okey = a.ckey + (int64_t)unit * a.ustride + c * a.cap;
+  int32_t* oidx = a.cidx + (int64_t)unit * a.ustride + c * a.cap;
   if (cnt <= kp || a.cap == a.chunk) {  // every page of the chunk is a candidate
     for (int o = tid; o < cnt; o += NT) {
       okey[o] = keys[o];
@@ -538,29 +639,62 @@ hipError_t set_lds(K kernel, size_t lds) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-template <bool BF16, int D, int HB, bool DPP, int NT>
+// Tuning of the scoring workgroups (defaults measured on MI355X): statistics chunks per
+// load group (CPL) and load groups in flight per wave (STAGES).
+#ifndef PSD_UNIT_THREADS
+#define PSD_UNIT_THREADS 1024  // whole-unit workgroups
+#endif
+#ifndef PSD_UNIT_CPL
+#define PSD_UNIT_CPL 2
+#endif
+#ifndef PSD_UNIT_STAGES
+#define PSD_UNIT_STAGES 1
+#endif
+#ifndef PSD_CHUNK_CPL
+#define PSD_CHUNK_CPL 1  // 256-thread chunk workgroups
+#endif
+#ifndef PSD_CHUNK_STAGES
+#define PSD_CHUNK_STAGES 1
+#endif
+#ifndef PSD_UNIT_MIN_UNITS
+#define PSD_UNIT_MIN_UNITS 128  // units that fill the GPU with one workgroup each
+#endif
+
+template <bool BF16, int D, int HB, bool DPP, int NT, int CPL, int S>
 hipError_t launch_score(const SelArgs& a, const SelectPlan& p, dim3 sgrid, hipStream_t st) {
-  hipError_t e = set_lds(&score_kernel<BF16, D, HB, DPP, NT>, p.score_lds);
+  hipError_t e = set_lds(&score_kernel<BF16, D, HB, DPP, NT, CPL, S>, p.score_lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((score_kernel<BF16, D, HB, DPP, NT>), sgrid, dim3(NT), p.score_lds, st, a);
+  hipLaunchKernelGGL((score_kernel<BF16, D, HB, DPP, NT, CPL, S>), sgrid, dim3(NT), p.score_lds,
+                     st, a);
   return hipGetLastError();
 }
 
-template <bool BF16, int D, int HB, bool DPP>
-hipError_t dispatch_nt(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStream_t st) {
-  return p.threads == 64 ? launch_score<BF16, D, HB, DPP, 64>(a, p, grid, st)
-                         : launch_score<BF16, D, HB, DPP, kThreads>(a, p, grid, st);
+// (threads, chunks per load group, groups in flight) triples the planner picks from;
+// (CPL, S) = (1, 1) is the fallback when the tuned staging does not fit in LDS.
+template <bool BF16, int D, int HB>
+hipError_t dispatch_dpp(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStream_t st) {
+  const bool tuned = p.cpl > 1 || p.stages > 1;
+  switch (p.threads) {
+    case 64: return launch_score<BF16, D, HB, true, 64, 4, 1>(a, p, grid, st);
+    case 256:
+      return tuned ? launch_score<BF16, D, HB, true, 256, PSD_CHUNK_CPL, PSD_CHUNK_STAGES>(a, p, grid, st)
+                   : launch_score<BF16, D, HB, true, 256, 1, 1>(a, p, grid, st);
+    case 512:
+      return tuned ? launch_score<BF16, D, HB, true, 512, PSD_UNIT_CPL, PSD_UNIT_STAGES>(a, p, grid, st)
+                   : launch_score<BF16, D, HB, true, 512, 1, 1>(a, p, grid, st);
+    default: return launch_score<BF16, D, HB, true, 1024, 1, 1>(a, p, grid, st);
+  }
 }
 
 template <bool BF16, int D>
 hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStream_t st) {
   if constexpr (D > 128) {
-    return launch_score<BF16, D, 16, false, kThreads>(a, p, grid, st);
+    return launch_score<BF16, D, 16, false, kThreads, 1, 1>(a, p, grid, st);
   } else {
     switch (p.head_block) {
-      case 4: return dispatch_nt<BF16, D, 4, true>(a, p, grid, st);
-      case 8: return dispatch_nt<BF16, D, 8, true>(a, p, grid, st);
-      default: return dispatch_nt<BF16, D, 16, false>(a, p, grid, st);
+      case 4: return dispatch_dpp<BF16, D, 4>(a, p, grid, st);
+      case 8: return dispatch_dpp<BF16, D, 8>(a, p, grid, st);
+      default: return launch_score<BF16, D, 16, false, kThreads, 1, 1>(a, p, grid, st);
     }
   }
 }
@@ -569,6 +703,7 @@ hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStre
 
 bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   if (b_max < 2) return false;
+  constexpr size_t kLdsLimit = 160 * 1024;
   const int kcap = b_max - 2;
   const int inner = g.max_pages > 2 ? g.max_pages - 2 : 1;
   const int64_t units = (int64_t)g.B * g.Hkv;
@@ -577,37 +712,85 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   p->all_q = g.G <= 16 && g.D <= 128;
   p->head_block = !p->all_q ? 16 : (g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16));
   p->d_chunk = p->all_q ? g.D : ((16 * g.D * 16 <= 32768) ? g.D : 32);
-  p->pages_per_lane = 1;
-  // one-wave workgroups when 256-thread ones would leave the GPU mostly idle
-  p->threads = (p->all_q && units * ((inner + kThreads - 1) / kThreads) < 512) ? 64 : kThreads;
-  const bool multi_pass = !p->all_q && (g.G > 16 || 16 * g.D * 16 > 32768);
+  const bool dpp = p->all_q && p->head_block <= 8;
+  const size_t static_lds = (size_t)p->d_chunk * p->head_block * 16 + 1536;
+  const int nch = g.D / (g.dtype == 1 ? 32 : 16);  // 64-byte statistics chunks per record
+  // LDS staging per wave for (chunks per group, groups in flight), as the kernel clamps them
+  auto stage_bytes = [&](int cpl, int st) {
+    const int c = cpl < nch ? cpl : nch;
+    const int ss = st < nch / c ? st : nch / c;
+    return (size_t)8192 * c * ss;
+  };
+  // the tuned staging of a workgroup size if it fits, else one chunk at a time
+  auto pick_staging = [&](int cpl, int st) {
+    const size_t keys = (size_t)p->chunk * 8;
+    if (cpl == 4 && p->threads == 64) st = 1;
+    if (static_lds + keys + (size_t)(p->threads / 64) * stage_bytes(cpl, st) <= kLdsLimit) {
+      p->cpl = cpl;
+      p->stages = st;
+    } else {
+      p->cpl = 1;
+      p->stages = 1;
+    }
+  };
   bool ok = false;
-  for (int ppt = 1; ppt <= 64; ppt *= 2) {
-    if (multi_pass && ppt > 1) break;
-    const int chunk = p->threads * p->pages_per_lane * ppt;
-    if (chunk * sizeof(uint64_t) > 65536) break;
-    const int nchunk = (inner + chunk - 1) / chunk;
-    if (nchunk > kMaxChunks) continue;
-    // Every page of a chunk is a candidate when they all fit in the merge; otherwise a
-    // chunk keeps only its own top b-2.
-    int cap = chunk;
-    if ((int64_t)nchunk * chunk > kMergeCap) cap = kcap < 1 ? 1 : (kcap < chunk ? kcap : chunk);
-    if ((int64_t)nchunk * cap <= kMergeCap) {
-      p->ppt = ppt;
-      p->chunk = chunk;
-      p->nchunk = nchunk;
-      p->cap = cap;
-      ok = true;
-      break;
+  if (dpp && inner <= 2048 && units >= PSD_UNIT_MIN_UNITS) {
+    // one workgroup per unit: scores every page and ranks them, no merge
+    p->threads = PSD_UNIT_THREADS;
+    p->ppt = (inner + p->threads - 1) / p->threads;
+    p->chunk = p->threads * p->ppt;
+    p->nchunk = 1;
+    p->cap = p->chunk;
+    if (p->threads == 512)
+      pick_staging(PSD_UNIT_CPL, PSD_UNIT_STAGES);
+    else if (p->threads == 256)
+      pick_staging(PSD_CHUNK_CPL, PSD_CHUNK_STAGES);
+    else
+      pick_staging(1, 1);
+    ok = true;
+  } else {
+    // one-wave workgroups when 256-thread ones would leave the GPU mostly idle
+    p->threads = (dpp && units * ((inner + kThreads - 1) / kThreads) < 512) ? 64 : kThreads;
+    const bool multi_pass = !p->all_q && (g.G > 16 || 16 * g.D * 16 > 32768);
+    for (int ppt = 1; ppt <= 64; ppt *= 2) {
+      if (multi_pass && ppt > 1) break;
+      const int chunk = p->threads * ppt;
+      if (chunk * sizeof(uint64_t) > 65536) break;
+      const int nchunk = (inner + chunk - 1) / chunk;
+      if (nchunk > kMaxChunks) continue;
+      // Every page of a chunk is a candidate when they all fit in the merge; otherwise a
+      // chunk keeps only its own top b-2.
+      int cap = chunk;
+      if ((int64_t)nchunk * chunk > kMergeCap) cap = kcap < 1 ? 1 : (kcap < chunk ? kcap : chunk);
+      if ((int64_t)nchunk * cap <= kMergeCap) {
+        p->ppt = ppt;
+        p->chunk = chunk;
+        p->nchunk = nchunk;
+        p->cap = cap;
+        ok = true;
+        break;
+      }
+    }
+    if (ok) {
+      if (!dpp) {
+        p->cpl = 1;
+        p->stages = 1;
+      } else if (p->threads == 64) {
+        pick_staging(4, 1);
+      } else {
+        pick_staging(PSD_CHUNK_CPL, PSD_CHUNK_STAGES);
+      }
     }
   }
   if (!ok) return false;
-  const size_t slots = (size_t)units * p->nchunk * p->cap;
-  p->merge_lds = (size_t)p->nchunk * p->cap * (sizeof(uint64_t) + sizeof(int32_t)) +
+  // candidate slots per unit, padded so that a merge copies whole 1 KB slices
+  p->ustride = p->nchunk == 1 ? 0 : (p->nchunk * p->cap + 255) / 256 * 256;
+  const size_t slots = (size_t)units * p->ustride;
+  p->merge_lds = (size_t)p->ustride * (sizeof(uint64_t) + sizeof(int32_t)) +
                  (size_t)p->nchunk * sizeof(int32_t);
   p->merge_threads = (int64_t)p->nchunk * p->cap <= 512 ? 64 : kThreads;
-  p->score_lds = p->chunk * sizeof(uint64_t);
-  if (p->head_block <= 8 && p->all_q) p->score_lds += (size_t)(p->threads / 64) * 8192;  // staging
+  p->score_lds = (size_t)p->chunk * sizeof(uint64_t);
+  if (dpp) p->score_lds += (size_t)(p->threads / 64) * stage_bytes(p->cpl, p->stages);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   p->off_idx = al(slots * sizeof(uint64_t));
   p->off_cnt = al(p->off_idx + slots * sizeof(int32_t));
@@ -623,7 +806,7 @@ static SelArgs make_args(const Geo& g, const SelectPlan& p, const void* q, const
                  reinterpret_cast<uint64_t*>(w), reinterpret_cast<int32_t*>(w + p.off_idx),
                  reinterpret_cast<int32_t*>(w + p.off_cnt), sel, cnt,
                  g.Hq, g.Hkv, g.G, g.D, g.max_pages, b_max, p.chunk, p.ppt, p.nchunk, p.cap,
-                 g.num_blocks};
+                 g.num_blocks, p.ustride};
 }
 
 hipError_t launch_select_score(const Geo& g, const SelectPlan& p, const void* q,
@@ -649,6 +832,7 @@ hipError_t launch_select_score(const Geo& g, const SelectPlan& p, const void* q,
 hipError_t launch_select_merge(const Geo& g, const SelectPlan& p, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, void* ws,
                                hipStream_t st) {
+  if (p.nchunk == 1) return hipSuccess;  // the scoring stage ranked every unit completely
   const SelArgs a = make_args(g, p, nullptr, nullptr, nullptr, lens, budgets, b_max, sel,
                               nullptr, ws);
   const dim3 ugrid(g.Hkv, g.B);

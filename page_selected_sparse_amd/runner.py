@@ -43,7 +43,7 @@ class DecodeStep:
         self.b_max = max(2, int(b_max))
         self.scale = 1.0 / float(D) ** 0.5
         cd = 32 if q.dtype == torch.bfloat16 else 16  # dims per 64-byte statistics chunk
-        self.meta = torch.empty((D // cd, NB, Hkv, 2, cd), dtype=q.dtype, device=dev)
+        self.meta = torch.empty((NB, Hkv, D // cd, 2, cd), dtype=q.dtype, device=dev)
         self.sel_pages = torch.empty((B, Hkv, self.b_max), dtype=torch.int32, device=dev)
         self.sel_count = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, Hq, head_dim_v), dtype=torch.float32, device=dev)

@@ -24,13 +24,13 @@ def run_gpu(w: synth.Workload, b_max=None, dense=True, cache=None):
     if dense:
         step.dense()
     torch.cuda.synchronize()
-    meta = step.meta.cpu()  # [D / CD, NB, H_kv, 2, CD]
+    meta = step.meta.cpu()  # [NB, H_kv, D / CD, 2, CD]
     if w.spec.dtype == "bf16":
         meta = synth.to_f64(meta.view(torch.int16).numpy().view(np.uint16), "bf16")
     else:
         meta = meta.numpy().astype(np.float64)
-    nc, nb, hkv, _, cd = meta.shape
-    meta = meta.transpose(1, 2, 3, 0, 4).reshape(nb, hkv, 2, nc * cd)  # [NB, H_kv, 2, D]
+    nb, hkv, nc, _, cd = meta.shape
+    meta = meta.transpose(0, 1, 3, 2, 4).reshape(nb, hkv, 2, nc * cd)  # [NB, H_kv, 2, D]
     res = dict(meta=meta, sel=step.sel_pages.cpu().numpy(), cnt=step.sel_count.cpu().numpy(),
                out=step.out.cpu().numpy().astype(np.float64), b_max=step.b_max)
     if dense:

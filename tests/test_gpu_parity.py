@@ -50,6 +50,12 @@ SMALL = {
     # enough units for the widest scoring workgroups
     "wide_batch": synth.small_spec(batch=64, num_q_heads=32, num_kv_heads=8, seq_lens=(),
                                    len_range=(3000, 9000), budget_percent=5, max_len=9008),
+    # one workgroup per unit with 8-head groups, and with fp32 statistics
+    "wide_group8": synth.small_spec(batch=32, num_q_heads=64, num_kv_heads=8, seq_lens=(),
+                                    len_range=(200, 6000), budget_percent=5, max_len=6000),
+    "wide_f32_d64": synth.small_spec(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=64,
+                                     head_dim_v=64, dtype="f32", seq_lens=(),
+                                     len_range=(1000, 20000), budget_percent=3, max_len=20000),
 }
 
 
