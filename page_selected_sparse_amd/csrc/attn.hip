@@ -101,9 +101,25 @@ __device__ __forceinline__ void load_frag8(const void* base, int64_t off, uint4&
   }
 }
 
+// Tuning (defaults measured on MI355X): software-pipelined page loads (bf16), and the
+// one-wave variant's occupancy target in waves per SIMD.
+#ifndef PSD_ATTN_PIPE
+#define PSD_ATTN_PIPE 0
+#endif
+#ifndef PSD_ATTN_W1
+#define PSD_ATTN_W1 4
+#endif
+#ifndef PSD_ATTN_TARGET
+#define PSD_ATTN_TARGET 4096  // sparse
+#endif
+#ifndef PSD_ATTN_TARGET_DENSE
+#define PSD_ATTN_TARGET_DENSE 2048
+#endif
+
 template <bool BF16, int DQK, int DV, int WAVES, int MIN_WAVES_PER_SIMD>
 __global__ __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnArgs a) {
+  constexpr bool PIPE = PSD_ATTN_PIPE != 0 && BF16;
   constexpr int NQ = DQK / 32;   // QK MFMAs per page (K = 32 dims each)
   constexpr int NC = DV / 16;    // PV MFMAs per page (16 output columns each)
   static_assert(NC % 4 == 0, "Dv must be a multiple of 64");
@@ -112,11 +128,16 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int p0 = split * a.pps;
+  // The selection entries of this split are requested together with the length and the
+  // count (the row holds b_max entries; lanes past it read its last entry), so that only
+  // the block-table lookup stands between them and the first K/V loads.
+  int sel_lp = p0 + lane;
+  if (a.sel) sel_lp = a.sel[(int64_t)(s * a.Hkv + g) * a.b_max + min(p0 + lane, a.b_max - 1)];
   const int L = a.lens[s];
   const int n = ceil_div(L, kPage);
   int count = a.sel ? min(a.cnt[s * a.Hkv + g], a.b_max) : n;
   if (count < 0) count = 0;  // flagged unit: the merge writes NaN
-  const int p0 = split * a.pps;
   if (p0 >= count) return;
   const int np = min(a.pps, count - p0);
 
@@ -124,8 +145,7 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
   // sequence's pages so that a malformed list can never address outside the table.
   int my_lp = 0, my_blk = 0;
   if (lane < np) {
-    my_lp = a.sel ? a.sel[(int64_t)(s * a.Hkv + g) * a.b_max + p0 + lane] : p0 + lane;
-    my_lp = min(max(my_lp, 0), n - 1);
+    my_lp = min(max(sel_lp, 0), n - 1);
     my_blk = a.bt[(int64_t)s * a.max_pages + my_lp];
     my_blk = min(max(my_blk, 0), a.num_blocks - 1);
   }
@@ -179,20 +199,25 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
     }
   };
 
-  for (int i = 0; i < np; ++i) {
-    const int lp = __builtin_amdgcn_readlane(my_lp, i);
-    const int blk = __builtin_amdgcn_readlane(my_blk, i);
-    const int valid = min(kPage, L - lp * kPage);  // tokens of this page before L
-
+  // K/V fragments of one page (EARLY: all of them, loaded ahead of use).
+  struct PageRegs {
     uint4 kr[EARLY ? NQ : 1][2], vr[EARLY ? NG : 1][4];
+  };
+  auto issue = [&](int i, PageRegs& R) {
     if constexpr (EARLY) {
+      const int blk = __builtin_amdgcn_readlane(my_blk, i);
 #pragma unroll
-      for (int c = 0; c < NQ; ++c) load_k(blk, c, kr[c][0], kr[c][1]);
+      for (int c = 0; c < NQ; ++c) load_k(blk, c, R.kr[c][0], R.kr[c][1]);
 #pragma unroll
       for (int w = 0; w < NG; ++w)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vr[w][j] = load_v(blk, w, j);
+        for (int j = 0; j < 4; ++j) R.vr[w][j] = load_v(blk, w, j);
     }
+  };
+  auto compute = [&](int i, const PageRegs& R) {
+    const int lp = __builtin_amdgcn_readlane(my_lp, i);
+    const int blk = __builtin_amdgcn_readlane(my_blk, i);
+    const int valid = min(kPage, L - lp * kPage);  // tokens of this page before L
 
     // ---- S^T = K Q^T -------------------------------------------------------------------
     float4v sacc = {0.f, 0.f, 0.f, 0.f};
@@ -200,8 +225,8 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
     for (int c = 0; c < NQ; ++c) {
       uint4 x0, x1, khi, klo, qh, ql;
       if constexpr (EARLY) {
-        x0 = kr[c][0];
-        x1 = kr[c][1];
+        x0 = R.kr[c][0];
+        x1 = R.kr[c][1];
       } else {
         load_k(blk, c, x0, x1);
       }
@@ -273,7 +298,7 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
       for (int j = 0; j < 4; ++j) {
         uint4 x;
         if constexpr (EARLY) {
-          x = vr[w][j];
+          x = R.vr[w][j];
         } else {
           x = load_v(blk, w, j);
         }
@@ -308,6 +333,25 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
           acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ph, Vl, acc[c], 0, 0, 0);
         }
       }
+    }
+  };
+
+  if constexpr (EARLY && PIPE) {
+    // Two register sets: page i + 1's loads are in flight while page i is computed.
+    PageRegs A, B;
+    issue(0, A);
+    for (int i = 0; i < np; i += 2) {
+      if (i + 1 < np) issue(i + 1, B);
+      compute(i, A);
+      if (i + 1 >= np) break;
+      if (i + 2 < np) issue(i + 2, A);
+      compute(i + 1, B);
+    }
+  } else {
+    PageRegs A;
+    for (int i = 0; i < np; ++i) {
+      issue(i, A);
+      compute(i, A);
     }
   }
 
@@ -413,7 +457,7 @@ __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a) {
 template <bool BF16, int DQK, int DV>
 hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) {
   // occupancy target per variant: the smallest register budget that does not spill
-  constexpr int W1 = DQK > 128 ? 1 : (BF16 ? 4 : 2);
+  constexpr int W1 = DQK > 128 ? 1 : (BF16 ? PSD_ATTN_W1 : 2);
   constexpr int W2 = DQK > 128 ? 1 : 2;
   if (waves == 1) {
     hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 1, W1>), grid, dim3(64), 0, st, a);
@@ -427,12 +471,13 @@ hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) 
 
 }  // namespace
 
-bool plan_decode(const Geo& g, int max_pages_attended, DecodePlan* p) {
+bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* p) {
   if (max_pages_attended < 1) return false;
   p->waves = (g.G + 15) / 16;
   const int64_t units = (int64_t)g.B * g.Hkv;
-  // Aim for ~2048 single-wave workgroups (fewer, larger ones for many-head groups).
-  const int64_t target = p->waves > 1 ? 512 : 8192;
+  // Aim for PSD_ATTN_TARGET single-wave workgroups (fewer, larger ones for many-head
+  // groups).
+  const int64_t target = p->waves > 1 ? 512 : (dense ? PSD_ATTN_TARGET_DENSE : PSD_ATTN_TARGET);
   int64_t pps = (units * max_pages_attended + target - 1) / target;
   const int64_t lo = p->waves > 1 ? 4 : 1;
   pps = pps < lo ? lo : (pps > 64 ? 64 : pps);

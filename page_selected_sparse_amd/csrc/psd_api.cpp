@@ -157,9 +157,12 @@ psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* m
 size_t psd_decode_workspace_bytes(const psd_shape* shape, int32_t max_pages_attended) {
   psd::Geo g;
   if (check_shape(shape, &g) != PSD_OK) return 0;
-  psd::DecodePlan p;
-  if (!psd::plan_decode(g, max_pages_attended, &p)) return 0;
-  return p.bytes;
+  // the same query serves the sparse and the dense call: room for either plan
+  psd::DecodePlan ps, pd;
+  if (!psd::plan_decode(g, max_pages_attended, false, &ps) ||
+      !psd::plan_decode(g, max_pages_attended, true, &pd))
+    return 0;
+  return ps.bytes > pd.bytes ? ps.bytes : pd.bytes;
 }
 
 static psd_status decode_common(const psd_shape* shape, const void* q, const void* k_cache,
@@ -177,7 +180,7 @@ static psd_status decode_common(const psd_shape* shape, const void* q, const voi
   if (!(scale > 0.f) || scale == __builtin_inff()) return PSD_ERR_INVALID_ARG;
   if ((st = check_strides(g, true)) != PSD_OK) return st;
   psd::DecodePlan p;
-  if (!psd::plan_decode(g, pages_cap, &p)) return PSD_ERR_INVALID_ARG;
+  if (!psd::plan_decode(g, pages_cap, sel_pages == nullptr, &p)) return PSD_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < p.bytes || !aligned16(workspace)) return PSD_ERR_WORKSPACE;
   return launched(psd::launch_decode(g, p, q, k_cache, v_cache, block_table, seq_lens, sel_pages,
                                      sel_count, b_max, scale, out, workspace, stream));

@@ -56,7 +56,8 @@ struct DecodePlan {
   int waves;   // waves per workgroup = ceil(G / 16) head tiles
   size_t off_ml, bytes;
 };
-bool plan_decode(const Geo& g, int max_pages_attended, DecodePlan* plan);
+// dense: every page of each sequence is attended (splits sized for long page walks).
+bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* plan);
 hipError_t launch_decode(const Geo& g, const DecodePlan& plan, const void* q, const void* k,
                          const void* v, const int32_t* bt, const int32_t* lens,
                          const int32_t* sel, const int32_t* cnt, int b_max, float scale,

@@ -58,6 +58,7 @@ struct SelArgs {
 struct SelScratch {
   uint32_t hist[256];
   int wave_cnt[16];
+  uint64_t wand[16], wor[16];
   int digit, k;
   bool done;
 };
@@ -72,26 +73,68 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
-// Finds the top K (1 <= K <= N) of keys[0..N) in LDS by radix select over 8-bit digits
-// from the most significant. Returns a prefix P over the bits covered by `mask` such that
-// every key with (key & mask) > P is in the top K and `need` of the keys with
-// (key & mask) == P complete it (the lowest positions among them). It stops as soon as all
-// keys of the chosen digit are needed; otherwise it ends with mask = all bits, P = the
-// K-th largest key. Equal digits met in a row by one thread are counted once.
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)x, m, 64), hi = __shfl_xor((uint32_t)(x >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Finds the top K (1 <= K <= N) of keys[0..N) in LDS by radix select over 8-bit digits.
+// Key 0 marks an empty slot: it never ranks (score keys of finite scores are nonzero and
+// far above it). The bits every nonzero key shares are skipped: the first digit starts at
+// the highest bit where two keys differ. Returns a prefix P over the bits covered by
+// `mask` such that every key with (key & mask) > P is in the top K and `need` of the keys
+// with (key & mask) == P complete it (the lowest positions among them). It stops as soon
+// as all keys of the chosen digit are needed; otherwise it ends with mask = all bits,
+// P = the K-th largest key. Equal digits met in a row by one thread are counted once.
 template <int NT>
 __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch& sc,
                                   uint64_t& P, uint64_t& M, int& need) {
-  const int tid = threadIdx.x;
-  uint64_t prefix = 0, mask = 0;
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint64_t kand = ~0ull, kor = 0;
+  for (int i = tid; i < N; i += NT) {
+    const uint64_t key = keys[i];
+    if (key) {
+      kand &= key;
+      kor |= key;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    kand &= shfl_xor64(kand, m);
+    kor |= shfl_xor64(kor, m);
+  }
+  if (lane == 0) {
+    sc.wand[w] = kand;
+    sc.wor[w] = kor;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    kand &= sc.wand[i];
+    kor |= sc.wor[i];
+  }
+  const uint64_t diff = kand ^ kor;
+  if (diff == 0) {  // every nonzero key is equal: the first K of them
+    P = kand;
+    M = ~0ull;
+    need = K;
+    return;
+  }
+  const int hb = 63 - __clzll(diff);
+  uint64_t mask = hb == 63 ? 0ull : ~((2ull << hb) - 1ull);  // bits above hb are shared
+  uint64_t prefix = kand & mask;
   int k = K;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (int sh = hb - 7;; sh -= 8) {
+    const int lo = sh > 0 ? sh : 0;
+    const uint64_t dmask = (1ull << (sh + 8 - lo)) - 1ull;
     for (int i = tid; i < 256; i += NT) sc.hist[i] = 0;
     __syncthreads();
     int run_d = -1, run_c = 0;
     for (int i = tid; i < N; i += NT) {
       const uint64_t key = keys[i];
       if ((key & mask) == prefix) {
-        const int dg = (int)((key >> shift) & 255u);
+        const int dg = (int)((key >> lo) & dmask);
         if (dg == run_d) {
           ++run_c;
         } else {
@@ -135,12 +178,12 @@ __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch
       }
     }
     __syncthreads();
-    prefix |= (uint64_t)sc.digit << shift;
-    mask |= 255ull << shift;
+    prefix |= (uint64_t)sc.digit << lo;
+    mask |= dmask << lo;
     k = sc.k;
     const bool done = sc.done;
     __syncthreads();  // sc is rewritten by the next pass
-    if (done) break;
+    if (done || lo == 0) break;
   }
   P = prefix;
   M = mask;
@@ -363,7 +406,7 @@ __device__ __forceinline__ void read_line(const uint4* page, int first, uint4 (&
 // without bank conflicts. S groups are in flight while one is accumulated; dims ascend.
 template <bool BF16, int D, int HB, int CPL, int S>
 __device__ __forceinline__ void bound_dpp(const void* meta, int hkv, int blk, int g,
-                                          const double* qv, uint4* stage, double* acc) {
+                                          const float* qv, uint4* stage, double* acc) {
   using M = MetaGeo<BF16>;
   constexpr int CD = M::CD;
   constexpr int NQ = CD * 2 * HB / 16;  // q registers per chunk
@@ -398,7 +441,7 @@ __device__ __forceinline__ void bound_dpp(const void* meta, int hkv, int blk, in
   auto accumulate = [&](int c, const uint4* mv) {
     double Q[NQ];
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) Q[m] = qv[c * CD * 2 * HB + 16 * m + lane16];
+    for (int m = 0; m < NQ; ++m) Q[m] = (double)qv[c * CD * 2 * HB + 16 * m + lane16];
 #pragma unroll
     for (int j = 0; j < CD; ++j) {
       const double kmn = chunk_elem<BF16>(mv, j), kmx = chunk_elem<BF16>(mv + 4, j);
@@ -521,7 +564,9 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   constexpr int CC = CPL < NCH ? CPL : NCH;
   constexpr int SS = S < NCH / CC ? S : NCH / CC;
   constexpr int STAGE = 512 * CC * SS;  // uint4 per wave
-  __shared__ double2 qlds[DC * HB];
+  // (q+, q-) table: fp32 for the DPP path (exact: q is bf16 or fp32), fp64 pairs otherwise
+  __shared__ float qf[DPP ? DC * HB * 2 : 1];
+  __shared__ double2 qlds[DPP ? 1 : DC * HB];
   __shared__ SelScratch sc;
   extern __shared__ unsigned char lds[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(lds);  // [chunk]
@@ -544,7 +589,12 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
       const int d = e / HB, h = e - d * HB, hh = hp * HB + h;
       double qv = 0.0;
       if (hh < a.G) qv = q_value<BF16>(a.q, ((int64_t)s * a.Hq + g * a.G + hh) * D + dc * DC + d);
-      qlds[e] = make_double2(qv >= 0.0 ? qv : 0.0, qv >= 0.0 ? 0.0 : qv);
+      if constexpr (DPP) {
+        qf[2 * e] = (float)(qv >= 0.0 ? qv : 0.0);
+        qf[2 * e + 1] = (float)(qv >= 0.0 ? 0.0 : qv);
+      } else {
+        qlds[e] = make_double2(qv >= 0.0 ? qv : 0.0, qv >= 0.0 ? 0.0 : qv);
+      }
     }
   };
   const bool once = nhp == 1 && NDC == 1;
@@ -567,8 +617,7 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
 #pragma unroll
       for (int h = 0; h < HB; ++h) acc[h] = 0.0;
       uint4* stage = reinterpret_cast<uint4*>(lds + a.chunk * sizeof(uint64_t)) + (tid >> 6) * STAGE;
-      bound_dpp<BF16, D, HB, CPL, S>(a.meta, a.Hkv, blk, g, reinterpret_cast<const double*>(qlds),
-                                     stage, acc);
+      bound_dpp<BF16, D, HB, CPL, S>(a.meta, a.Hkv, blk, g, qf, stage, acc);
 #pragma unroll
       for (int h = 0; h < HB; ++h)
         if (h < a.G && acc[h] > best) best = acc[h];
@@ -713,7 +762,7 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   p->head_block = !p->all_q ? 16 : (g.G <= 4 ? 4 : (g.G <= 8 ? 8 : 16));
   p->d_chunk = p->all_q ? g.D : ((16 * g.D * 16 <= 32768) ? g.D : 32);
   const bool dpp = p->all_q && p->head_block <= 8;
-  const size_t static_lds = (size_t)p->d_chunk * p->head_block * 16 + 1536;
+  const size_t static_lds = (size_t)p->d_chunk * p->head_block * (dpp ? 8 : 16) + 1536;
   const int nch = g.D / (g.dtype == 1 ? 32 : 16);  // 64-byte statistics chunks per record
   // LDS staging per wave for (chunks per group, groups in flight), as the kernel clamps them
   auto stage_bytes = [&](int cpl, int st) {
@@ -788,7 +837,8 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   const size_t slots = (size_t)units * p->ustride;
   p->merge_lds = (size_t)p->ustride * (sizeof(uint64_t) + sizeof(int32_t)) +
                  (size_t)p->nchunk * sizeof(int32_t);
-  p->merge_threads = (int64_t)p->nchunk * p->cap <= 512 ? 64 : kThreads;
+  const int64_t cands = (int64_t)p->nchunk * p->cap;
+  p->merge_threads = cands <= 512 ? 64 : (cands <= 4096 ? kThreads : 1024);
   p->score_lds = (size_t)p->chunk * sizeof(uint64_t);
   if (dpp) p->score_lds += (size_t)(p->threads / 64) * stage_bytes(p->cpl, p->stages);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -840,6 +890,9 @@ hipError_t launch_select_merge(const Geo& g, const SelectPlan& p, const int32_t*
   if (p.merge_threads == 64) {
     if ((e = set_lds(&merge_kernel<64>, p.merge_lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(merge_kernel<64>, ugrid, dim3(64), p.merge_lds, st, a);
+  } else if (p.merge_threads == 1024) {
+    if ((e = set_lds(&merge_kernel<1024>, p.merge_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_kernel<1024>, ugrid, dim3(1024), p.merge_lds, st, a);
   } else {
     if ((e = set_lds(&merge_kernel<kThreads>, p.merge_lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(merge_kernel<kThreads>, ugrid, dim3(kThreads), p.merge_lds, st, a);
