@@ -115,6 +115,9 @@ __device__ __forceinline__ void load_frag8(const void* base, int64_t off, uint4&
 #ifndef PSD_ATTN_TARGET_DENSE
 #define PSD_ATTN_TARGET_DENSE 2048
 #endif
+#ifndef PSD_ATTN_TARGET_WIDE
+#define PSD_ATTN_TARGET_WIDE 256  // workgroups of 2+ waves (groups over 16 heads)
+#endif
 
 template <bool BF16, int DQK, int DV, int WAVES, int MIN_WAVES_PER_SIMD>
 __global__ __launch_bounds__(64 * WAVES)
@@ -277,16 +280,19 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
       pl[j] = f2bf(p[j] - __uint_as_float(ph[j] << 16));
     }
     const short4v Ph = as_short4(pack2(ph[0], ph[1]), pack2(ph[2], ph[3]));
-    const short4v Pl = as_short4(pack2(pl[0], pl[1]), pack2(pl[2], pl[3]));
+    const bf16x8 PP = as_bf16x8(make_uint4(pack2(ph[0], ph[1]), pack2(ph[2], ph[3]),
+                                           pack2(pl[0], pl[1]), pack2(pl[2], pl[3])));
 
     // Rescale the output rows (heads 4grp + j) by their alpha.
     float al[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 4 * grp + j, 64);
+    if (__ballot(alpha != 1.f)) {  // skipped once no head's running max moves
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+      for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[c][j] *= al[j];
+        for (int j = 0; j < 4; ++j) acc[c][j] *= al[j];
+      }
     }
 
     // ---- O += P V ------------------------------------------------------------------------
@@ -322,9 +328,11 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
         uint32_t e[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) e[j] = hiw ? (vh[j][wd] >> 16) : (vh[j][wd] & 0xffffu);
-        const short4v Vb = as_short4(pack2(e[0], e[1]), pack2(e[2], e[3]));
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ph, Vb, acc[c], 0, 0, 0);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Pl, Vb, acc[c], 0, 0, 0);
+        // one K=32 MFMA: k = 8grp + i pairs token 4grp + (i & 3) with the hi (i < 4) or
+        // lo part of P, and V's 4 values repeat, so it adds (P_hi + P_lo) V
+        const uint32_t v01 = pack2(e[0], e[1]), v23 = pack2(e[2], e[3]);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(PP, as_bf16x8(make_uint4(v01, v23, v01, v23)),
+                                                         acc[c], 0, 0, 0);
         if constexpr (!BF16) {
           uint32_t f[4];
 #pragma unroll
@@ -366,6 +374,231 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
       for (int c = 0; c < NC; c += 4)
         *reinterpret_cast<float4*>(dst + c) =
             make_float4(acc[c][j], acc[c + 1][j], acc[c + 2][j], acc[c + 3][j]);
+    }
+  }
+  if (grp == 0 && hvalid) a.pml[(ubase + head) * a.nsplit + split] = make_float2(m_run, l_run);
+}
+
+// ---- latent (MLA-style) attention: K and V rows are one 576-dim latent row -------------
+//
+// For many-head groups (G = 16 * WAVES, up to 128) on a latent cache (V = first 512 dims of
+// each K row, same pointer and strides), a workgroup stages each 16-token page once in
+// LDS (direct-to-LDS loads, rows padded to 73 16-byte pieces so that fragment reads are
+// conflict-free), three pages deep, and every wave reads its MFMA fragments from there;
+// each wave keeps its 16 heads' q in registers. V columns map to MFMA columns as
+// d = 128 w + 8 lane_col + cc for tile 8 w + cc, so that a lane's 16-byte read serves
+// 8 tiles and the 16 lanes of a row read 16 consecutive pieces.
+constexpr int kLatRowPieces = 73;                 // 72 pieces of 16 B + 1 pad
+constexpr int kLatLoads = (16 * kLatRowPieces + 63) / 64;  // 1 KB loads per page: 19
+constexpr int kLatStage = kLatLoads * 64;         // uint4 per stage (tail slots unused)
+constexpr int kLatStages = 3;
+
+// Waits until at most n vector memory operations of this wave are outstanding, n <= 20.
+__device__ __forceinline__ void wait_vm_upto20(int n) {
+#define PSD_W(N) case N: __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70); break;
+  switch (n) {
+    PSD_W(0) PSD_W(1) PSD_W(2) PSD_W(3) PSD_W(4) PSD_W(5) PSD_W(6) PSD_W(7) PSD_W(8) PSD_W(9)
+    PSD_W(10) PSD_W(11) PSD_W(12) PSD_W(13) PSD_W(14) PSD_W(15) PSD_W(16) PSD_W(17)
+    PSD_W(18) PSD_W(19)
+    default: __builtin_amdgcn_s_waitcnt(0xF70); break;
+  }
+#undef PSD_W
+}
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4l;
+
+// Four 16-byte LDS reads in one asm block (with the wait for them), so that the compiler
+// does not make them wait for the loads still streaming into other stages.
+__device__ __forceinline__ void lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                          uint4& x0, uint4& x1, uint4& x2, uint4& x3) {
+  u32x4l r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+  x0 = make_uint4(r0.x, r0.y, r0.z, r0.w);
+  x1 = make_uint4(r1.x, r1.y, r1.z, r1.w);
+  x2 = make_uint4(r2.x, r2.y, r2.z, r2.w);
+  x3 = make_uint4(r3.x, r3.y, r3.z, r3.w);
+}
+
+__device__ __forceinline__ void lds_read2(uint32_t a0, uint32_t a1, uint4& x0, uint4& x1) {
+  u32x4l r0, r1;
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+  x0 = make_uint4(r0.x, r0.y, r0.z, r0.w);
+  x1 = make_uint4(r1.x, r1.y, r1.z, r1.w);
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void attn_latent_kernel(AttnArgs a) {
+  constexpr int DQK = 576, DV = 512, NQ = DQK / 32, NC = DV / 16;  // 18 and 32
+  __shared__ uint4 stage[kLatStages * kLatStage];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int p0 = split * a.pps;
+  int sel_lp = p0 + lane;
+  if (a.sel) sel_lp = a.sel[(int64_t)(s * a.Hkv + g) * a.b_max + min(p0 + lane, a.b_max - 1)];
+  const int L = a.lens[s];
+  const int n = ceil_div(L, kPage);
+  int count = a.sel ? min(a.cnt[s * a.Hkv + g], a.b_max) : n;
+  if (count < 0) count = 0;
+  if (p0 >= count) return;  // uniform over the workgroup
+  const int np = min(a.pps, count - p0);
+  int my_lp = 0, my_blk = 0;
+  if (lane < np) {
+    my_lp = min(max(sel_lp, 0), n - 1);
+    my_blk = a.bt[(int64_t)s * a.max_pages + my_lp];
+    my_blk = min(max(my_blk, 0), a.num_blocks - 1);
+  }
+
+  // this wave's 16 heads' q as B fragments: head r, dims 32c + 8grp .. +8
+  const int head = wave * 16 + r;
+  const bool hvalid = head < a.G;
+  const int64_t qrow = ((int64_t)s * a.Hq + g * a.G + (hvalid ? head : 0)) * DQK;
+  uint4 qf[NQ];
+#pragma unroll
+  for (int c = 0; c < NQ; ++c)
+    qf[c] = hvalid ? load16(static_cast<const uint16_t*>(a.q) + qrow + 32 * c + 8 * grp)
+                   : make_uint4(0, 0, 0, 0);
+
+  // Page loads: instruction i of a page is issued by wave i % WAVES; its lane l fills
+  // stage slot 64 i + l = (row, piece) of the padded layout, fetching piece 0 of the row
+  // for the pad slot and the tail slots (never read).
+  const uint16_t* kb = static_cast<const uint16_t*>(a.k);
+  const int my_loads = (kLatLoads - wave + WAVES - 1) / WAVES;
+  auto issue = [&](int i, int st) {
+    const int blk = __builtin_amdgcn_readlane(my_blk, i);
+    const uint16_t* pbase = kb + (int64_t)blk * a.kbs + (int64_t)g * a.khs;
+    for (int ins = wave; ins < kLatLoads; ins += WAVES) {
+      const int slot = ins * 64 + lane;
+      int row = slot / kLatRowPieces, piece = slot - row * kLatRowPieces;
+      if (row >= 16) {
+        row = 15;
+        piece = 0;
+      }
+      if (piece == kLatRowPieces - 1) piece = 0;
+      __builtin_amdgcn_global_load_lds(
+          pbase + (int64_t)row * a.kts + piece * 8,
+          (__attribute__((address_space(3))) void*)(stage + st * kLatStage + ins * 64), 16, 0,
+          0);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float4v acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t sbase = (uint32_t)(uintptr_t)stage;
+  issue(0, 0);
+  if (np > 1) issue(1, 1);
+  for (int i = 0; i < np; ++i) {
+    // page i has landed once only page i + 1's loads of this wave are outstanding
+    wait_vm_upto20(i + 1 < np ? my_loads : 0);
+    __syncthreads();  // every wave's share of page i is in; page i - 1 is read by all
+    if (i + 2 < np) issue(i + 2, (i + 2) % kLatStages);
+    const uint32_t st = sbase + (uint32_t)((i % kLatStages) * kLatStage * 16);
+    const int lp = __builtin_amdgcn_readlane(my_lp, i);
+    const int valid = min(kPage, L - lp * kPage);
+
+    // ---- S^T = K Q^T: K row r, dims 32c + 8grp (piece 4c + grp) ---------------------
+    float4v sacc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t krow = st + (uint32_t)(r * kLatRowPieces + grp) * 16;
+#pragma unroll
+    for (int c0 = 0; c0 < NQ; c0 += 2) {
+      uint4 k[2];
+      lds_read2(krow + 64 * c0, krow + 64 * (c0 + 1), k[0], k[1]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[c]), as_bf16x8(qf[c0 + c]),
+                                                       sacc, 0, 0, 0);
+    }
+
+    // ---- online softmax ------------------------------------------------------------------
+    float z[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = 4 * grp + j < valid ? sacc[j] * a.sl2 : -INFINITY;
+    const float m_loc = wave_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    const float m_new = fmaxf(m_run, m_loc);
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? exp2f(m_run - m_new) : 1.f;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = live ? exp2f(z[j] - m_new) : 0.f;
+    l_run = l_run * alpha + wave_sum4(p[0] + p[1] + p[2] + p[3]);
+    m_run = m_new;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ph[j] = f2bf(p[j]);
+      pl[j] = f2bf(p[j] - __uint_as_float(ph[j] << 16));
+    }
+    const bf16x8 PP = as_bf16x8(make_uint4(pack2(ph[0], ph[1]), pack2(ph[2], ph[3]),
+                                           pack2(pl[0], pl[1]), pack2(pl[2], pl[3])));
+    float al[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 4 * grp + j, 64);
+    if (__ballot(alpha != 1.f)) {  // skipped once no head's running max moves
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[c][j] *= al[j];
+    }
+
+    // ---- O += P V: V rows 4grp + j, piece 16w + r ---------------------------------------
+    const uint32_t vrow = st + (uint32_t)((4 * grp) * kLatRowPieces + r) * 16;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint4 x[4];
+      lds_read4(vrow + 16 * (0 * kLatRowPieces + 16 * w), vrow + 16 * (1 * kLatRowPieces + 16 * w),
+                vrow + 16 * (2 * kLatRowPieces + 16 * w), vrow + 16 * (3 * kLatRowPieces + 16 * w),
+                x[0], x[1], x[2], x[3]);
+      uint32_t vh[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (4 * grp + j >= valid) x[j] = make_uint4(0u, 0u, 0u, 0u);  // unwritten slots
+        vh[j][0] = x[j].x; vh[j][1] = x[j].y; vh[j][2] = x[j].z; vh[j][3] = x[j].w;
+      }
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const int wd = cc >> 1;
+        const bool hiw = cc & 1;
+        uint32_t e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[j] = hiw ? (vh[j][wd] >> 16) : (vh[j][wd] & 0xffffu);
+        const uint32_t v01 = pack2(e[0], e[1]), v23 = pack2(e[2], e[3]);
+        acc[8 * w + cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            PP, as_bf16x8(make_uint4(v01, v23, v01, v23)), acc[8 * w + cc], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- partials: rows are heads 4grp + j; tile 8w + cc column r is d = 128w + 8r + cc ---
+  const int64_t ubase = (int64_t)s * a.Hq + g * a.G;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int hh = wave * 16 + 4 * grp + j;
+    if (hh < a.G) {
+      float* dst = a.pacc + ((ubase + hh) * a.nsplit + split) * DV + 8 * r;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        *reinterpret_cast<float4*>(dst + 128 * w) =
+            make_float4(acc[8 * w][j], acc[8 * w + 1][j], acc[8 * w + 2][j], acc[8 * w + 3][j]);
+        *reinterpret_cast<float4*>(dst + 128 * w + 4) =
+            make_float4(acc[8 * w + 4][j], acc[8 * w + 5][j], acc[8 * w + 6][j], acc[8 * w + 7][j]);
+      }
     }
   }
   if (grp == 0 && hvalid) a.pml[(ubase + head) * a.nsplit + split] = make_float2(m_run, l_run);
@@ -469,6 +702,20 @@ hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) 
   return hipGetLastError();
 }
 
+hipError_t launch_latent(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) {
+  switch (waves) {
+    case 1: hipLaunchKernelGGL(attn_latent_kernel<1>, grid, dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(attn_latent_kernel<2>, grid, dim3(128), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(attn_latent_kernel<3>, grid, dim3(192), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(attn_latent_kernel<4>, grid, dim3(256), 0, st, a); break;
+    case 5: hipLaunchKernelGGL(attn_latent_kernel<5>, grid, dim3(320), 0, st, a); break;
+    case 6: hipLaunchKernelGGL(attn_latent_kernel<6>, grid, dim3(384), 0, st, a); break;
+    case 7: hipLaunchKernelGGL(attn_latent_kernel<7>, grid, dim3(448), 0, st, a); break;
+    default: hipLaunchKernelGGL(attn_latent_kernel<8>, grid, dim3(512), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* p) {
@@ -477,7 +724,8 @@ bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* p
   const int64_t units = (int64_t)g.B * g.Hkv;
   // Aim for PSD_ATTN_TARGET single-wave workgroups (fewer, larger ones for many-head
   // groups).
-  const int64_t target = p->waves > 1 ? 512 : (dense ? PSD_ATTN_TARGET_DENSE : PSD_ATTN_TARGET);
+  const int64_t target =
+      p->waves > 1 ? PSD_ATTN_TARGET_WIDE : (dense ? PSD_ATTN_TARGET_DENSE : PSD_ATTN_TARGET);
   int64_t pps = (units * max_pages_attended + target - 1) / target;
   const int64_t lo = p->waves > 1 ? 4 : 1;
   pps = pps < lo ? lo : (pps > 64 ? 64 : pps);
@@ -508,6 +756,8 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
   else if (g.D == 128)
     e = bf ? launch_attn<true, 128, 128>(a, grid, p.waves, st)
            : launch_attn<false, 128, 128>(a, grid, p.waves, st);
+  else if (bf && k == v && g.kbs == g.vbs && g.kts == g.vts && g.khs == g.vhs)
+    e = launch_latent(a, grid, p.waves, st);
   else
     e = bf ? launch_attn<true, 576, 512>(a, grid, p.waves, st)
            : launch_attn<false, 576, 512>(a, grid, p.waves, st);
