@@ -162,23 +162,27 @@ psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* m
 /*
  * The two stages of psd_select_pages, for callers that schedule or time them apart.
  * psd_select_pages(args) is exactly psd_select_score(args) followed, on the same stream,
- * by psd_select_merge with the same shape, seq_lens, budgets, b_max, sel_pages and
- * workspace.
+ * by psd_select_merge with the same shape, q, meta, block_table, seq_lens, budgets, b_max,
+ * sel_pages and workspace.
  *
- * psd_select_score scores every page and ranks each chunk of pages, leaving each chunk's
- * candidates in the workspace; it writes sel_count and every sel_pages entry except the
- * ranked winners (sink, tail and -1 padding; whole rows of units that keep every page or
- * exceed b_max). psd_select_merge reads the candidates back, takes the b-2 winners of
- * every ranking unit and writes them into sel_pages[..., 1 .. b-2] in ascending order.
- * The workspace must not be touched between the two calls. Arguments, errors and
- * sources as for psd_select_pages.
+ * psd_select_score scores the pages. It writes sel_count and every sel_pages entry except
+ * the ranked winners: the sink, the tail and the -1 padding, and the whole row of a unit
+ * that keeps every page or exceeds b_max. It leaves candidates in the workspace: either
+ * each chunk's top pages by exact score or, for groups of 16 or more bf16 heads,
+ * approximate scores with a proven error bound. psd_select_merge reads them back and
+ * writes the b-2 winners of every ranking unit into sel_pages[..., 1 .. b-2] in ascending
+ * order. For the approximate case it first rescores exactly the pages that the bound
+ * cannot decide, which is why it takes q, meta and block_table. The workspace must not be
+ * touched between the two calls. Arguments, errors and sources are as for
+ * psd_select_pages.
  */
 psd_status psd_select_score(const psd_shape* shape, const void* q, const void* meta,
                             const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
                             int32_t* sel_count, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
-psd_status psd_select_merge(const psd_shape* shape, const int32_t* seq_lens,
+psd_status psd_select_merge(const psd_shape* shape, const void* q, const void* meta,
+                            const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -23,8 +23,8 @@ SIGNATURES = {
                                  c_i32, c_void_p, c_void_p, c_void_p, c_size, c_void_p]),
     "psd_select_score": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_i32, c_void_p, c_void_p, c_void_p, c_size, c_void_p]),
-    "psd_select_merge": (c_i32, [c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p,
-                                 c_size, c_void_p]),
+    "psd_select_merge": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_i32, c_void_p, c_void_p, c_size, c_void_p]),
     "psd_decode_workspace_bytes": (c_size, [c_void_p, c_i32]),
     "psd_sparse_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_i32, c_float, c_void_p, c_void_p, c_size,

@@ -99,9 +99,10 @@ def select_score(shape: PsdShape, q, meta, block_table, seq_lens, budgets, b_max
                                        _stream(stream)), "psd_select_score")
 
 
-def select_merge(shape: PsdShape, seq_lens, budgets, b_max: int, sel_pages, workspace,
-                 stream=None):
-    _ok(_native.lib().psd_select_merge(ctypes.byref(shape), _ptr(seq_lens), _ptr(budgets), b_max,
+def select_merge(shape: PsdShape, q, meta, block_table, seq_lens, budgets, b_max: int, sel_pages,
+                 workspace, stream=None):
+    _ok(_native.lib().psd_select_merge(ctypes.byref(shape), _ptr(q), _ptr(meta),
+                                       _ptr(block_table), _ptr(seq_lens), _ptr(budgets), b_max,
                                        _ptr(sel_pages), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(),
                                        _stream(stream)), "psd_select_merge")

@@ -130,7 +130,8 @@ psd_status psd_select_score(const psd_shape* shape, const void* q, const void* m
                                            sel_pages, sel_count, workspace, stream));
 }
 
-psd_status psd_select_merge(const psd_shape* shape, const int32_t* seq_lens,
+psd_status psd_select_merge(const psd_shape* shape, const void* q, const void* meta,
+                            const int32_t* block_table, const int32_t* seq_lens,
                             const int32_t* budgets, int32_t b_max, int32_t* sel_pages,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   psd::Geo g;
@@ -138,8 +139,10 @@ psd_status psd_select_merge(const psd_shape* shape, const int32_t* seq_lens,
   psd_status st = select_common(shape, seq_lens, budgets, b_max, sel_pages, workspace,
                                 workspace_bytes, &g, &p);
   if (st != PSD_OK) return st;
-  return launched(psd::launch_select_merge(g, p, seq_lens, budgets, b_max, sel_pages, workspace,
-                                           stream));
+  if (!q || !meta || !block_table) return PSD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(meta)) return PSD_ERR_INVALID_ARG;
+  return launched(psd::launch_select_merge(g, p, q, meta, block_table, seq_lens, budgets, b_max,
+                                           sel_pages, workspace, stream));
 }
 
 psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* meta,
@@ -150,8 +153,8 @@ psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* m
   psd_status st = psd_select_score(shape, q, meta, block_table, seq_lens, budgets, b_max,
                                    sel_pages, sel_count, workspace, workspace_bytes, stream);
   if (st != PSD_OK) return st;
-  return psd_select_merge(shape, seq_lens, budgets, b_max, sel_pages, workspace,
-                          workspace_bytes, stream);
+  return psd_select_merge(shape, q, meta, block_table, seq_lens, budgets, b_max, sel_pages,
+                          workspace, workspace_bytes, stream);
 }
 
 size_t psd_decode_workspace_bytes(const psd_shape* shape, int32_t max_pages_attended) {

@@ -27,6 +27,7 @@ struct SelectPlan {
   int nchunk;      // chunks covering max_pages - 2 candidates
   int cap;         // candidate slots per chunk = min(chunk, b_max - 2)
   int ustride;     // candidate slots per unit in the workspace
+  bool prescore;   // many-head bf16 groups: certified MFMA pre-score + exact ranking
   int cpl;         // statistics chunks per load group (DPP path)
   int stages;      // load groups in flight per wave (DPP path)
   int head_block;  // query heads scored per pass (template width)
@@ -45,9 +46,23 @@ hipError_t launch_select_score(const Geo& g, const SelectPlan& plan, const void*
                                const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, int32_t* cnt,
                                void* ws, hipStream_t st);
-hipError_t launch_select_merge(const Geo& g, const SelectPlan& plan, const int32_t* lens,
+hipError_t launch_select_merge(const Geo& g, const SelectPlan& plan, const void* q,
+                               const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, void* ws,
                                hipStream_t st);
+
+// Certified many-head path (prescore.hip): the score stage is prescore_kernel (tiles of
+// `ppt` 16-page groups per workgroup, nchunk workgroups per unit), the merge stage is
+// certify_kernel. Workspace: approximate scores at 0, page maxima at off_idx.
+constexpr int kPreMaxInner = 7168;  // certify holds 21 bytes per candidate in LDS
+bool prescore_applies(const Geo& g);
+size_t prescore_lds(int max_inner);
+hipError_t launch_prescore(const Geo& g, const SelectPlan& plan, const void* q, const void* meta,
+                           const int32_t* bt, const int32_t* lens, const int32_t* budgets,
+                           int b_max, int32_t* sel, int32_t* cnt, void* ws, hipStream_t st);
+hipError_t launch_certify(const Geo& g, const SelectPlan& plan, const void* q, const void* meta,
+                          const int32_t* bt, const int32_t* lens, const int32_t* budgets,
+                          int b_max, int32_t* sel, void* ws, hipStream_t st);
 
 // ---- attention -------------------------------------------------------------------------
 struct DecodePlan {

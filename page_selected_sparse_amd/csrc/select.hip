@@ -752,6 +752,35 @@ hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStre
 
 bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   if (b_max < 2) return false;
+  p->prescore = false;
+  if (prescore_applies(g)) {
+    // certified MFMA pre-score: ~256 workgroups of up to 64 tiles of 16 pages
+    const int max_inner = g.max_pages > 2 ? g.max_pages - 2 : 1;
+    const int64_t tiles = (max_inner + 15) / 16;
+    const int64_t units = (int64_t)g.B * g.Hkv;
+    int64_t tpw = (units * tiles + 255) / 256;
+    tpw = tpw < 1 ? 1 : (tpw > 64 ? 64 : tpw);
+    p->prescore = true;
+    p->ppt = (int)tpw;
+    p->nchunk = (int)((tiles + tpw - 1) / tpw);
+    p->chunk = 16 * p->ppt;
+    p->threads = 64 * (g.G / 16);
+    p->cap = 0;
+    p->ustride = 0;
+    p->cpl = p->stages = 1;
+    p->head_block = 16;
+    p->d_chunk = g.D;
+    p->all_q = false;
+    p->merge_threads = 1024;
+    p->merge_lds = prescore_lds(max_inner);
+    p->score_lds = 0;
+    const size_t plane = ((size_t)units * max_inner * sizeof(float) + 255) / 256 * 256;
+    // planes: approximate group score, page maximum, runner-up, leading head; q norms
+    p->off_idx = plane;
+    p->off_cnt = 4 * plane;
+    p->bytes = 4 * plane + (size_t)units * sizeof(double) + 256;
+    return true;
+  }
   constexpr size_t kLdsLimit = 160 * 1024;
   const int kcap = b_max - 2;
   const int inner = g.max_pages > 2 ? g.max_pages - 2 : 1;
@@ -863,6 +892,8 @@ hipError_t launch_select_score(const Geo& g, const SelectPlan& p, const void* q,
                                const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, int32_t* cnt,
                                void* ws, hipStream_t st) {
+  if (p.prescore)
+    return launch_prescore(g, p, q, meta, bt, lens, budgets, b_max, sel, cnt, ws, st);
   const SelArgs a = make_args(g, p, q, meta, bt, lens, budgets, b_max, sel, cnt, ws);
   const dim3 sgrid(p.nchunk, g.Hkv, g.B);
   const bool bf = g.dtype == 1;
@@ -879,9 +910,11 @@ hipError_t launch_select_score(const Geo& g, const SelectPlan& p, const void* q,
 // The merge runs as its own launch: the kernel boundary makes every chunk's candidates
 // visible (a device-scope fence inside the scoring kernel writes back and invalidates
 // the L2).
-hipError_t launch_select_merge(const Geo& g, const SelectPlan& p, const int32_t* lens,
+hipError_t launch_select_merge(const Geo& g, const SelectPlan& p, const void* q,
+                               const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, void* ws,
                                hipStream_t st) {
+  if (p.prescore) return launch_certify(g, p, q, meta, bt, lens, budgets, b_max, sel, ws, st);
   if (p.nchunk == 1) return hipSuccess;  // the scoring stage ranked every unit completely
   const SelArgs a = make_args(g, p, nullptr, nullptr, nullptr, lens, budgets, b_max, sel,
                               nullptr, ws);

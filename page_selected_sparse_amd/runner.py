@@ -92,8 +92,8 @@ class DecodeStep:
 
     def select_merge(self, stream=None):
         """Second stage of ``select``: the winners of every unit from the candidates."""
-        api.select_merge(self.shape, self.seq_lens, self.budgets, self.b_max, self.sel_pages,
-                         self.ws_select, stream)
+        api.select_merge(self.shape, self.q, self.meta, self.block_table, self.seq_lens,
+                         self.budgets, self.b_max, self.sel_pages, self.ws_select, stream)
 
     def sparse(self, stream=None):
         api.sparse_decode(self.shape, self.q, self.k, self.v, self.block_table, self.seq_lens,

@@ -93,9 +93,13 @@ def test_null_and_workspace_errors(native):
     assert lib.psd_select_score(ctypes.byref(sh), f, f, f, f, f, 1, f, f, f, 1 << 30, None) == -1
     assert lib.psd_select_score(ctypes.byref(sh), f, None, f, f, f, 10, f, f, f, 1 << 30,
                                 None) == -1
-    assert lib.psd_select_merge(ctypes.byref(sh), f, f, 10, f, f, 8, None) == -3
-    assert lib.psd_select_merge(ctypes.byref(sh), None, f, 10, f, f, 1 << 30, None) == -1
-    assert lib.psd_select_merge(ctypes.byref(long), f, f, 60000, f, f, 1 << 40, None) == -4
+    assert lib.psd_select_merge(ctypes.byref(sh), f, f, f, f, f, 10, f, f, 8, None) == -3
+    assert lib.psd_select_merge(ctypes.byref(sh), f, f, f, None, f, 10, f, f, 1 << 30,
+                                None) == -1
+    assert lib.psd_select_merge(ctypes.byref(sh), None, f, f, f, f, 10, f, f, 1 << 30,
+                                None) == -1
+    assert lib.psd_select_merge(ctypes.byref(long), f, f, f, f, f, 60000, f, f, 1 << 40,
+                                None) == -4
     # misaligned pointer
     assert lib.psd_page_meta_update(ctypes.byref(sh), ctypes.c_void_p(18), f, f, f, None,
                                     None) == -1

@@ -188,3 +188,48 @@ def test_selection_stages_compose():
     step.select_merge()
     torch.cuda.synchronize()
     assert torch.equal(step.sel_pages, sel) and torch.equal(step.sel_count, cnt)
+
+
+@pytest.mark.parametrize("name", ["latent576", "group32", "mla_64k"])
+def test_prescore_error_bound_holds(name):
+    """The approximate many-head scores lie within the proven error bound of the exact fp64
+    group scores, and the page maxima are exact. Reads the scoring stage's workspace: the
+    approximate scores fill the first plane ([unit][max_pages - 2] fp32), the page maxima
+    the second, each plane padded to 256 bytes."""
+    from page_selected_sparse_amd import DecodeStep
+
+    spec = SMALL[name] if name in SMALL else synth.SPECS[name]
+    w = synth.make_workload(spec)
+    step = DecodeStep.from_arrays(w.q, w.cache, w.block_table, w.seq_lens, w.budgets,
+                                  w.spec.dtype, w.spec.head_dim_v, w.spec.latent)
+    step.build_meta()
+    step.select_score()
+    torch.cuda.synchronize()
+    B, Hkv, D = w.spec.batch, w.spec.num_kv_heads, w.spec.head_dim
+    G = w.spec.num_q_heads // Hkv
+    max_inner = w.block_table.shape[1] - 2
+    plane = (B * Hkv * max_inner * 4 + 255) // 256 * 256
+    ws = step.ws_select.cpu().numpy()
+    approx = ws[:B * Hkv * max_inner * 4].view(np.float32).reshape(B, Hkv, max_inner)
+    pmax = ws[plane:plane + B * Hkv * max_inner * 4].view(np.float32).reshape(B, Hkv, max_inner)
+    inp = synth.oracle_inputs(w)
+    worst = 0.0
+    for s in ([0, B - 1] if B > 2 else range(B)):
+        L = int(w.seq_lens[s])
+        n = O.pages_of(L)
+        b = O.effective_budget(n, int(w.budgets[s]))
+        if n <= b or b <= 2:  # nothing to rank: the scoring stage leaves no scores
+            continue
+        kmin, kmax = O.sequence_meta(inp["k_cache"], w.block_table[s], L)
+        for g in range(Hkv):
+            q = inp["q"][s, g * G:(g + 1) * G]
+            exact = O.group_scores(O.page_bounds(q, kmin[1:n - 1, g], kmax[1:n - 1, g]))
+            m = np.maximum(np.abs(kmin[1:n - 1, g]), np.abs(kmax[1:n - 1, g])).max(axis=1)
+            np.testing.assert_array_equal(pmax[s, g, :n - 2], m)
+            q1 = np.abs(q).sum(axis=1).max()
+            rel = 1.7e-5  # above the kernel's own factor for D <= 576 (about 1.64e-5)
+            e = rel * q1 * m + np.abs(exact) * 2.0 ** -40 + 1e-30
+            err = np.abs(approx[s, g, :n - 2].astype(np.float64) - exact)
+            worst = max(worst, float(np.max(err / e)))
+            assert np.all(err <= e), (s, g, float(np.max(err / e)))
+    print(f"[ok] {name}: worst error / bound = {worst:.3f}", flush=True)
