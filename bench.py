@@ -12,6 +12,8 @@ Prints one JSON line. Besides the contract fields it carries:
   cpu_baseline  the fp64 oracle's step on the host, on a bounded sample of sequences
   calls         per-call average durations (HIP events on the launch stream)
   dense         the dense baseline (psd_dense_decode) on the same inputs
+  graph_replay  the same step replayed from a captured HIP graph (launch cost removed),
+                with a bit-for-bit check against the eager outputs
 """
 from __future__ import annotations
 
@@ -141,6 +143,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step (reported beside the eager rate)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -195,6 +199,35 @@ def main():
 
     # The measured region: K whole steps, rotating copies.
     ms_step = timed(lambda st: st.step(), args.steps)
+
+    graph = None
+    if not args.no_graph:
+        # The same step replayed from a HIP graph (one captured step per rotated copy),
+        # checked bit for bit against the eager outputs.
+        for st in steps:
+            st.step()
+        torch.cuda.synchronize()
+        eager_out = [st.out.clone() for st in steps]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for st in steps:
+                st.step()
+        replays = max(1, args.steps // R)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(st.out, o) for st, o in zip(steps, eager_out))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        same = same and all(torch.equal(st.out, o) for st, o in zip(steps, eager_out))
+        ms_graph = e0.elapsed_time(e1) / (replays * R)
+        graph = {"ms_per_step": round(ms_graph, 5), "steps_per_s": round(1000.0 / ms_graph, 3),
+                 "matches_eager": bool(same)}
+        del g
 
     # Per-call averages, each call timed in its own loop with events on the stream the
     # kernels are launched on (torch's current stream). Every call below but sparse_decode
@@ -255,6 +288,8 @@ def main():
         "calls_ms": {k: round(v, 5) for k, v in calls.items()},
         "algorithmic_bytes": ab,
     }
+    if graph is not None:
+        result["graph_replay"] = graph
     if dense_ms is not None:
         result["dense"] = {"ms": round(dense_ms, 5),
                            "gbs": round(ab["dense_decode"] / (dense_ms * 1e-3) / 1e9, 1),

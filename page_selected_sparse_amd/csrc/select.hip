@@ -56,11 +56,9 @@ struct SelArgs {
 };
 
 struct SelScratch {
-  uint32_t hist[256];
-  int wave_cnt[16];
+  uint32_t hist[3][256];  // rotating: one barrier per radix pass
+  int wave_cnt[2][16];    // alternating between the two scans of an emission
   uint64_t wand[16], wor[16];
-  int digit, k;
-  bool done;
 };
 
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
@@ -86,11 +84,14 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
 // with (key & mask) == P complete it (the lowest positions among them). It stops as soon
 // as all keys of the chosen digit are needed; otherwise it ends with mask = all bits,
 // P = the K-th largest key. Equal digits met in a row by one thread are counted once.
+// One barrier per pass: histograms rotate over three buffers (a buffer is cleared two
+// passes before it is counted into) and every wave scans the histogram itself.
 template <int NT>
 __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch& sc,
                                   uint64_t& P, uint64_t& M, int& need) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < 2 * 256; i += NT) sc.hist[i >> 8][i & 255] = 0;
   uint64_t kand = ~0ull, kor = 0;
   for (int i = tid; i < N; i += NT) {
     const uint64_t key = keys[i];
@@ -125,11 +126,10 @@ __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch
   uint64_t mask = hb == 63 ? 0ull : ~((2ull << hb) - 1ull);  // bits above hb are shared
   uint64_t prefix = kand & mask;
   int k = K;
-  for (int sh = hb - 7;; sh -= 8) {
+  for (int pass = 0, sh = hb - 7;; ++pass, sh -= 8) {
     const int lo = sh > 0 ? sh : 0;
     const uint64_t dmask = (1ull << (sh + 8 - lo)) - 1ull;
-    for (int i = tid; i < 256; i += NT) sc.hist[i] = 0;
-    __syncthreads();
+    uint32_t* hist = sc.hist[pass % 3];
     int run_d = -1, run_c = 0;
     for (int i = tid; i < N; i += NT) {
       const uint64_t key = keys[i];
@@ -138,62 +138,59 @@ __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch
         if (dg == run_d) {
           ++run_c;
         } else {
-          if (run_c) atomicAdd(&sc.hist[run_d], (uint32_t)run_c);
+          if (run_c) atomicAdd(&hist[run_d], (uint32_t)run_c);
           run_d = dg;
           run_c = 1;
         }
       }
     }
-    if (run_c) atomicAdd(&sc.hist[run_d], (uint32_t)run_c);
+    if (run_c) atomicAdd(&hist[run_d], (uint32_t)run_c);
     __syncthreads();
-    if (tid < 64) {
-      // lane handles digits 255-4l .. 252-4l, i.e. descending digit order
-      const int base = 255 - 4 * tid;
-      const int c0 = sc.hist[base], c1 = sc.hist[base - 1], c2 = sc.hist[base - 2],
-                c3 = sc.hist[base - 3];
-      const int local = c0 + c1 + c2 + c3;
-      const int incl = wave_inclusive_scan(local);
-      const int excl = incl - local;
-      if (excl < k && k <= incl) {
-        int r = k - excl, dg, cnt;
-        if (r <= c0) {
-          dg = base;
-          cnt = c0;
-        } else if (r <= c0 + c1) {
-          r -= c0;
-          dg = base - 1;
-          cnt = c1;
-        } else if (r <= c0 + c1 + c2) {
-          r -= c0 + c1;
-          dg = base - 2;
-          cnt = c2;
-        } else {
-          r -= c0 + c1 + c2;
+    // every wave: lane l handles digits 255-4l .. 252-4l (descending digit order)
+    const int base = 255 - 4 * lane;
+    const int c0 = hist[base], c1 = hist[base - 1], c2 = hist[base - 2], c3 = hist[base - 3];
+    const int local = c0 + c1 + c2 + c3;
+    const int incl = wave_inclusive_scan(local);
+    const int excl = incl - local;
+    const bool mine = excl < k && k <= incl;
+    int r = k - excl, dg = base, cnt = c0;
+    if (r > c0) {
+      r -= c0;
+      dg = base - 1;
+      cnt = c1;
+      if (r > c1) {
+        r -= c1;
+        dg = base - 2;
+        cnt = c2;
+        if (r > c2) {
+          r -= c2;
           dg = base - 3;
           cnt = c3;
         }
-        sc.digit = dg;
-        sc.k = r;
-        sc.done = r == cnt;  // every key of this digit is in the top K
       }
     }
-    __syncthreads();
-    prefix |= (uint64_t)sc.digit << lo;
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    dg = __shfl(dg, src, 64);
+    r = __shfl(r, src, 64);
+    cnt = __shfl(cnt, src, 64);
+    // the buffer of the next pass but one was last read before this pass's barrier
+    for (int i = tid; i < 256; i += NT) sc.hist[(pass + 2) % 3][i] = 0;
+    prefix |= (uint64_t)dg << lo;
     mask |= dmask << lo;
-    k = sc.k;
-    const bool done = sc.done;
-    __syncthreads();  // sc is rewritten by the next pass
-    if (done || lo == 0) break;
+    k = r;
+    if (r == cnt || lo == 0) break;  // every key of this digit is needed, or all bits done
   }
+  __syncthreads();  // sc is reused by the next call
   P = prefix;
   M = mask;
   need = k;
 }
 
 // Exclusive prefix sum of x over the threads of an NT-thread workgroup (thread order),
-// and the total. Contains barriers: every thread must call it.
+// and the total, using wave-count buffer `buf`. One barrier; a buffer may be reused only
+// after another barrier.
 template <int NT>
-__device__ __forceinline__ int block_excl_sum(int x, SelScratch& sc, int& total) {
+__device__ __forceinline__ int block_excl_sum(int x, SelScratch& sc, int& total, int buf = 0) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int incl = wave_inclusive_scan(x);
@@ -201,17 +198,16 @@ __device__ __forceinline__ int block_excl_sum(int x, SelScratch& sc, int& total)
     total = __shfl(incl, 63, 64);
     return incl - x;
   }
-  if (lane == 63) sc.wave_cnt[w] = incl;
+  if (lane == 63) sc.wave_cnt[buf][w] = incl;
   __syncthreads();
   int off = 0;
   total = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const int c = sc.wave_cnt[i];
+    const int c = sc.wave_cnt[buf][i];
     off += i < w ? c : 0;
     total += c;
   }
-  __syncthreads();
   return off + incl - x;
 }
 
@@ -232,10 +228,10 @@ __device__ int block_emit_top(const uint64_t* keys, int N, uint64_t P, uint64_t 
     eq += key == P;
   }
   int tot;
-  const int eq_before = block_excl_sum<NT>(eq, sc, tot);
+  const int eq_before = block_excl_sum<NT>(eq, sc, tot, 0);
   const int eq_take = min(max(need - eq_before, 0), eq);
   int emitted;
-  int pos = block_excl_sum<NT>(gt + eq_take, sc, emitted);
+  int pos = block_excl_sum<NT>(gt + eq_take, sc, emitted, 1);
   int eq_seen = 0;
   for (int i = b0; i < e0; ++i) {
     const uint64_t key = keys[i] & M;
@@ -405,29 +401,36 @@ __device__ __forceinline__ void read_line(const uint4* page, int first, uint4 (&
 // pieces are rotated by the page index, so that the 64 lanes read their own lines back
 // without bank conflicts. S groups are in flight while one is accumulated; dims ascend.
 template <bool BF16, int D, int HB, int CPL, int S>
-__device__ __forceinline__ void bound_dpp(const void* meta, int hkv, int blk, int g,
-                                          const float* qv, uint4* stage, double* acc) {
+struct DppPage {
   using M = MetaGeo<BF16>;
-  constexpr int CD = M::CD;
-  constexpr int NQ = CD * 2 * HB / 16;  // q registers per chunk
-  constexpr int NCH = D / CD;
-  constexpr int C = CPL < NCH ? CPL : NCH;  // chunks per load group
-  constexpr int NG = NCH / C;               // load groups
-  constexpr int SS = S < NG ? S : NG;       // groups in flight
-  constexpr int SL = 8 * C;                 // 16-byte slots per page in a group
-  constexpr int NI = SL;                    // 1 KB load instructions per group
-  constexpr int PPI = 8 / C;                // pages per load instruction
-  constexpr int GB = 64 * SL;               // uint4 per group stage (64 pages)
+  static constexpr int CD = M::CD;
+  static constexpr int NQ = CD * 2 * HB / 16;  // q registers per chunk
+  static constexpr int NCH = D / CD;
+  static constexpr int C = CPL < NCH ? CPL : NCH;  // chunks per load group
+  static constexpr int NG = NCH / C;               // load groups
+  static constexpr int SS = S < NG ? S : NG;       // groups in flight
+  static constexpr int SL = 8 * C;                 // 16-byte slots per page in a group
+  static constexpr int NI = SL;                    // 1 KB load instructions per group
+  static constexpr int PPI = 8 / C;                // pages per load instruction
+  static constexpr int GB = 64 * SL;               // uint4 per group stage (64 pages)
   static_assert(NCH % C == 0 && (SS == 1 || SS == 2), "load grouping");
-  const int lane = threadIdx.x & 63, lane16 = lane & 15;
-  const unsigned char* base = static_cast<const unsigned char*>(meta);
-  const uint32_t own = (uint32_t)blk * (uint32_t)hkv + (uint32_t)g;  // record of this page
+
+  const unsigned char* base;
+  uint4* stage;
+  uint32_t rec[NI];
+
   // Load instruction i: this lane fetches piece (slot - page) mod SL of page
   // i * PPI + lane / SL into slot lane % SL of that page's region.
-  uint32_t rec[NI];
+  __device__ __forceinline__ void init(const void* meta, int hkv, int blk, int g, uint4* st) {
+    const int lane = threadIdx.x & 63;
+    base = static_cast<const unsigned char*>(meta);
+    stage = st;
+    const uint32_t own = (uint32_t)blk * (uint32_t)hkv + (uint32_t)g;  // record of this page
 #pragma unroll
-  for (int i = 0; i < NI; ++i) rec[i] = __shfl(own, i * PPI + lane / SL, 64);
-  auto load = [&](int grp, uint4* st) {
+    for (int i = 0; i < NI; ++i) rec[i] = __shfl(own, i * PPI + lane / SL, 64);
+  }
+  __device__ __forceinline__ void load(int grp, uint4* st) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int page = i * PPI + lane / SL;
@@ -437,41 +440,66 @@ __device__ __forceinline__ void bound_dpp(const void* meta, int hkv, int blk, in
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(st + 64 * i),
                                        16, 0, 0);
     }
-  };
-  auto accumulate = [&](int c, const uint4* mv) {
-    double Q[NQ];
+  }
+  // the first SS groups; may run before the q table is ready
+  __device__ __forceinline__ void issue_first() {
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) Q[m] = (double)qv[c * CD * 2 * HB + 16 * m + lane16];
+    for (int j = 0; j < SS; ++j) load(j, stage + GB * j);
+  }
+  // the rest of the pipeline and the accumulation, after issue_first()
+  __device__ __forceinline__ void finish(const float* qv, double* acc) {
+    const int lane = threadIdx.x & 63, lane16 = lane & 15;
+    auto accumulate = [&](int c, const uint4* mv) {
+      double Q[NQ];
 #pragma unroll
-    for (int j = 0; j < CD; ++j) {
-      const double kmn = chunk_elem<BF16>(mv, j), kmx = chunk_elem<BF16>(mv + 4, j);
-      if constexpr (HB == 4) {
-        if (j & 1)
-          fma4_dpp<8>(acc[0], acc[1], acc[2], acc[3], Q[j >> 1], kmx, kmn);
-        else
-          fma4_dpp<0>(acc[0], acc[1], acc[2], acc[3], Q[j >> 1], kmx, kmn);
-      } else {
-        fma4_dpp<0>(acc[0], acc[1], acc[2], acc[3], Q[j], kmx, kmn);
-        fma4_dpp<8>(acc[4], acc[5], acc[6], acc[7], Q[j], kmx, kmn);
+      for (int m = 0; m < NQ; ++m) Q[m] = (double)qv[c * CD * 2 * HB + 16 * m + lane16];
+#pragma unroll
+      for (int j = 0; j < CD; ++j) {
+        const double kmn = chunk_elem<BF16>(mv, j), kmx = chunk_elem<BF16>(mv + 4, j);
+        if constexpr (HB == 4) {
+          if (j & 1)
+            fma4_dpp<8>(acc[0], acc[1], acc[2], acc[3], Q[j >> 1], kmx, kmn);
+          else
+            fma4_dpp<0>(acc[0], acc[1], acc[2], acc[3], Q[j >> 1], kmx, kmn);
+        } else {
+          fma4_dpp<0>(acc[0], acc[1], acc[2], acc[3], Q[j], kmx, kmn);
+          fma4_dpp<8>(acc[4], acc[5], acc[6], acc[7], Q[j], kmx, kmn);
+        }
+      }
+    };
+    // kept rolled: the q reads and loads of one group stay inside their iteration
+#pragma unroll 1
+    for (int j = 0; j < NG; ++j) {
+      // group j has landed once only the groups issued after it are outstanding
+      wait_vm8(min(SS - 1, NG - 1 - j) * C);
+      uint4* st = stage + GB * (j & (SS - 1)) + lane * SL;  // this lane's page region
+#pragma unroll 1
+      for (int cc = 0; cc < C; ++cc) {
+        uint4 mv[8];
+        read_line<SL>(st, cc * 8 + lane, mv);
+        if (cc == C - 1 && j + SS < NG) load(j + SS, stage + GB * (j & (SS - 1)));
+        accumulate(j * C + cc, mv);
       }
     }
-  };
-#pragma unroll
-  for (int j = 0; j < SS; ++j) load(j, stage + GB * j);
-  // kept rolled: the q reads and loads of one group stay inside their iteration
-#pragma unroll 1
-  for (int j = 0; j < NG; ++j) {
-    // group j has landed once only the groups issued after it are outstanding
-    wait_vm8(min(SS - 1, NG - 1 - j) * C);
-    uint4* st = stage + GB * (j & (SS - 1)) + lane * SL;  // this lane's page region
-#pragma unroll 1
-    for (int cc = 0; cc < C; ++cc) {
-      uint4 mv[8];
-      read_line<SL>(st, cc * 8 + lane, mv);
-      if (cc == C - 1 && j + SS < NG) load(j + SS, stage + GB * (j & (SS - 1)));
-      accumulate(j * C + cc, mv);
-    }
   }
+};
+
+// Bound of one page per lane for HB (4 or 8) heads. The group's (q+, q-) values for a
+// chunk of CD dims are spread over the lanes of each 16-lane row (value v of the chunk in
+// register v / 16 of lane v % 16, loaded from the LDS table once per chunk) and reach the
+// fp64 FMAs through DPP row broadcasts, so no per-dim operand traffic is needed.
+// Statistics are loaded cooperatively and straight into LDS in groups of C chunks: each
+// load instruction moves 1 KB, 8 / C pages' C contiguous lines, so that each page's
+// record is fetched as one contiguous request. In a page's region of the stage its 8C
+// pieces are rotated by the page index, so that the 64 lanes read their own lines back
+// without bank conflicts. S groups are in flight while one is accumulated; dims ascend.
+template <bool BF16, int D, int HB, int CPL, int S>
+__device__ __forceinline__ void bound_dpp(const void* meta, int hkv, int blk, int g,
+                                          const float* qv, uint4* stage, double* acc) {
+  DppPage<BF16, D, HB, CPL, S> pg;
+  pg.init(meta, hkv, blk, g, stage);
+  pg.issue_first();
+  pg.finish(qv, acc);
 }
 
 // Bound contribution of dims [d0, d0 + DC) of one page for HB heads, with the (q+, q-)
@@ -598,11 +626,32 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
     }
   };
   const bool once = nhp == 1 && NDC == 1;
+  const int64_t bt0 = (int64_t)s * a.max_pages;
+  uint4* stage = reinterpret_cast<uint4*>(lds + a.chunk * sizeof(uint64_t)) + (tid >> 6) * STAGE;
+  // DPP path: the first page set's block ids and statistics loads go out before the q
+  // table is built, and the table's barrier waits only for LDS writes, so that the table
+  // is built while those loads are in flight.
+  // Only the block id stays live across the barrier; the record offsets are recomputed
+  // after it (the empty asm keeps the compiler from reusing the first ones).
+  const bool pre = DPP && (tid & ~63) < cnt;
+  int blk0 = 0;
+  if constexpr (DPP) {
+    if (pre) {
+      blk0 = a.bt[bt0 + (tid < cnt ? lo + tid : lo)];
+      DppPage<BF16, D, HB, CPL, S> first;
+      first.init(a.meta, a.Hkv, blk0, g, stage);
+      first.issue_first();
+    }
+  }
   if (once) {
     load_qlds(0, 0);
-    __syncthreads();
+    if constexpr (DPP) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's table writes are done
+      __builtin_amdgcn_s_barrier();
+    } else {
+      __syncthreads();
+    }
   }
-  const int64_t bt0 = (int64_t)s * a.max_pages;
   for (int it = 0; it < a.ppt; ++it) {
     const int o = it * NT + tid;
     if constexpr (DPP) {
@@ -610,18 +659,25 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
       if (it * NT + (tid & ~63) >= cnt) continue;
     }
     const bool have = o < cnt;
-    const int blk = a.bt[bt0 + (have ? lo + o : lo)];
     double best = -__builtin_inf();
     if constexpr (DPP) {
       double acc[HB];
 #pragma unroll
       for (int h = 0; h < HB; ++h) acc[h] = 0.0;
-      uint4* stage = reinterpret_cast<uint4*>(lds + a.chunk * sizeof(uint64_t)) + (tid >> 6) * STAGE;
-      bound_dpp<BF16, D, HB, CPL, S>(a.meta, a.Hkv, blk, g, qf, stage, acc);
+      if (it == 0) {
+        asm volatile("" : "+v"(blk0));
+        DppPage<BF16, D, HB, CPL, S> first;
+        first.init(a.meta, a.Hkv, blk0, g, stage);
+        first.finish(qf, acc);
+      } else {
+        const int blk = a.bt[bt0 + (have ? lo + o : lo)];
+        bound_dpp<BF16, D, HB, CPL, S>(a.meta, a.Hkv, blk, g, qf, stage, acc);
+      }
 #pragma unroll
       for (int h = 0; h < HB; ++h)
         if (h < a.G && acc[h] > best) best = acc[h];
     } else {
+      const int blk = a.bt[bt0 + (have ? lo + o : lo)];
       for (int hp = 0; hp < nhp; ++hp) {
         double acc[HB];
 #pragma unroll
