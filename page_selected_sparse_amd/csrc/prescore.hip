@@ -147,7 +147,10 @@ __device__ __forceinline__ void wait_vm_upto40(int n) {
 #undef PSD_W
 }
 
-constexpr int kPreStages = 3;
+#ifndef PSD_PRE_STAGES
+#define PSD_PRE_STAGES 3
+#endif
+constexpr int kPreStages = PSD_PRE_STAGES;
 #ifndef PSD_PRE_CHAIN
 #define PSD_PRE_CHAIN 4
 #endif
@@ -302,16 +305,21 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
     }
   };
 
+  // tiles in flight ahead of the one computed (bounded so that the vmcnt wait fits)
+  constexpr int MLW = (NLD + WAVES - 1) / WAVES;  // most loads one wave issues per tile
+  constexpr int AH0 = 39 / MLW < 1 ? 1 : 39 / MLW;
+  constexpr int AH = kPreStages - 1 < AH0 ? kPreStages - 1 : AH0;
+  constexpr int NST = AH + 1;  // stages used
   const uint32_t sbase = (uint32_t)(uintptr_t)stage;
-  issue(0, 0);
-  if (T > 1) issue(1, 1);
+  for (int j = 0; j < AH && j < T; ++j) issue(j, j);
   for (int t = 0; t < T; ++t) {
-    wait_vm_upto40(t + 1 < T ? my_loads : 0);
+    // tile t has landed once only the tiles issued after it are outstanding
+    wait_vm_upto40(min(AH - 1, T - 1 - t) * my_loads);
     __syncthreads();  // tile t is in; tile t - 1 is read by every wave; its maxima are in
-    if (t + 2 < T) issue(t + 2, (t + 2) % kPreStages);
+    if (t + AH < T) issue(t + AH, (t + AH) % NST);
     if (t > 0) finish(t - 1);
     const uint32_t row =
-        sbase + (uint32_t)((t % kPreStages) * STG + r * SLP + grp) * 16 + 64 * kb0;
+        sbase + (uint32_t)((t % NST) * STG + r * SLP + grp) * 16 + 64 * kb0;
     float sum[4] = {0.f, 0.f, 0.f, 0.f};
     float4v chain = {0.f, 0.f, 0.f, 0.f};
     u16x2 amax = {0, 0};
@@ -512,12 +520,14 @@ __device__ uint64_t kth_key(const uint64_t* keys, int N, int K, SelScr& sc) {
   return prefix;
 }
 
-// The KA-th largest of keysA and the KB-th largest of keysB (same length N), exactly, in
-// one radix sweep with two histograms: digits start at the highest bit where any two keys
-// of either array differ.
+// The KA-th largest of keysA and the KB-th largest of keysB (same length N) in one radix
+// sweep with two histograms: digits start at the highest bit where any two keys of either
+// array differ. After max_passes digits it stops with a lower bound of A's and an upper
+// bound of B's (exact when every bit was resolved).
 template <int NT>
 __device__ void kth_key2(const uint64_t* keysA, int KA, const uint64_t* keysB, int KB, int N,
-                         SelScr& sc, uint32_t* histB, uint64_t& outA, uint64_t& outB) {
+                         SelScr& sc, uint32_t* histB, uint64_t& outA, uint64_t& outB,
+                         int max_passes = 8) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   uint64_t kand = ~0ull, kor = 0;
@@ -551,7 +561,7 @@ __device__ void kth_key2(const uint64_t* keysA, int KA, const uint64_t* keysB, i
   uint64_t pa = kand & mask, pb = pa;
   int ka = KA, kb = KB;
   __shared__ int res[4];
-  for (int sh = hb - 7;; sh -= 8) {
+  for (int sh = hb - 7, pass = 0;; sh -= 8, ++pass) {
     const int lo = sh > 0 ? sh : 0;
     const uint64_t dmask = (1ull << (sh + 8 - lo)) - 1ull;
     for (int i = tid; i < 256; i += NT) {
@@ -621,6 +631,13 @@ __device__ void kth_key2(const uint64_t* keysA, int KA, const uint64_t* keysB, i
     kb = res[3];
     __syncthreads();
     if (lo == 0) break;
+    if (pass + 1 == max_passes) {
+      // stop early: A is bounded below by its prefix with zero low bits, B above by its
+      // prefix with all low bits set
+      outA = pa;
+      outB = pb | ~mask;
+      return;
+    }
   }
   outA = pa;
   outB = pb;
@@ -729,10 +746,12 @@ __global__ __launch_bounds__(NT) void certify_kernel(PreArgs a) {
     kU[i] = score_key(U);
   }
   __syncthreads();
-  // T: the (b-2)-th largest lower bound; V: the (b-1)-th largest upper bound
+  // T: the (b-2)-th largest lower bound or less; V: the (b-1)-th largest upper bound or
+  // more (two digits below the first differing bit; looser bounds only leave more pages
+  // undecided)
   __shared__ uint32_t histB[256];
   uint64_t T, V;
-  kth_key2<NT>(kL, kp, kU, kp + 1, cnt, sc, histB, T, V);
+  kth_key2<NT>(kL, kp, kU, kp + 1, cnt, sc, histB, T, V, 2);
   for (int i = tid; i < cnt; i += NT) flag[i] = kL[i] > V ? 1 : (kU[i] >= T ? 2 : 0);
   __syncthreads();
 
