@@ -65,7 +65,23 @@ def algorithmic_bytes(w, sel_counts: np.ndarray) -> dict:
 
 
 KERNEL_SOURCES = {"score_kernel": "select.hip", "merge_kernel": "select.hip",
-                  "meta_kernel": "meta.hip", "attn_kernel": "attn.hip"}
+                  "prescore_kernel": "prescore.hip", "certify_kernel": "prescore.hip",
+                  "meta_kernel": "meta.hip", "attn_kernel": "attn.hip",
+                  "attn_latent_kernel": "attn.hip", "lse_merge_kernel": "attn.hip"}
+
+
+def selection_kernels(w) -> tuple:
+    """Names of the kernels behind select_score and select_merge for a workload. Follows
+    the library's planning rule: bf16 groups of 16..128 query heads (a multiple of 16)
+    with D of 64, 128 or 576 take the certified MFMA pre-score and its certify stage;
+    everything else the exact bound kernel and the chunk merge."""
+    sp = w.spec
+    G = sp.num_q_heads // sp.num_kv_heads
+    max_pages = int(np.max((w.seq_lens + 15) // 16))
+    if (sp.dtype == "bf16" and 16 <= G <= 128 and G % 16 == 0 and
+            sp.head_dim in (64, 128, 576) and max_pages - 2 <= 7168):
+        return "prescore_kernel", "certify_kernel"
+    return "score_kernel", "merge_kernel"
 
 
 def source_digest(kernel: str) -> str:
@@ -231,7 +247,8 @@ def main():
 
     # Per-call averages, each call timed in its own loop with events on the stream the
     # kernels are launched on (torch's current stream). Every call below but sparse_decode
-    # is a single kernel; sparse_decode is the attention kernel plus the split merge.
+    # is a single kernel (select_merge launches none when each scoring workgroup ranked a
+    # whole unit); sparse_decode is the attention kernel plus the split merge.
     calls = {"page_meta_update": timed(lambda st: st.refresh_tail(), args.steps),
              "select_score": timed(lambda st: st.select_score(), args.steps),
              "select_merge": timed(lambda st: st.select_merge(), args.steps),
@@ -248,8 +265,9 @@ def main():
     sel_counts = steps[0].sel_count.cpu().numpy()
     ab = algorithmic_bytes(w, sel_counts)
     # The dominant single-kernel call and its achieved algorithmic bandwidth.
-    kernel_of = {"select_score": ("score_kernel", ab["select_score"]),
-                 "select_merge": ("merge_kernel", ab["select_merge"]),
+    score_k, merge_k = selection_kernels(w)
+    kernel_of = {"select_score": (score_k, ab["select_score"]),
+                 "select_merge": (merge_k, ab["select_merge"]),
                  "page_meta_update": ("meta_kernel", ab["meta_update"])}
     dom = max(kernel_of, key=lambda k: calls[k])
     kname, dom_bytes = kernel_of[dom]
@@ -286,6 +304,9 @@ def main():
                      "algorithmic_bytes": dom_bytes, "ms": round(calls[dom], 5),
                      "traffic": traffic},
         "calls_ms": {k: round(v, 5) for k, v in calls.items()},
+        # algorithmic GB/s of every call (sparse_decode: attention plus the split merge)
+        "calls_gbs": {k: round(ab[{"page_meta_update": "meta_update"}.get(k, k)] /
+                               (v * 1e-3) / 1e9, 1) for k, v in calls.items()},
         "algorithmic_bytes": ab,
     }
     if graph is not None:

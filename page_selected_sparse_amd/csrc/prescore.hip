@@ -395,16 +395,6 @@ struct SelScr {
   double red[16];
 };
 
-__device__ __forceinline__ int wave_scan_incl(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
 template <int NT>
 __device__ __forceinline__ int excl_sum(int x, SelScr& sc, int& total) {
   constexpr int NW = NT / 64;
@@ -424,11 +414,6 @@ __device__ __forceinline__ int excl_sum(int x, SelScr& sc, int& total) {
   return off + incl - x;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)x, m, 64), hi = __shfl_xor((uint32_t)(x >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // The K-th largest key (1 <= K <= N) of keys[0..N), exactly: radix select over 8-bit
 // digits, starting at the highest bit where two keys differ (the bits every key shares
 // are skipped) and resolving every bit below it. Equal digits met in a row by one thread
@@ -442,11 +427,7 @@ __device__ uint64_t kth_key(const uint64_t* keys, int N, int K, SelScr& sc) {
     kand &= keys[i];
     kor |= keys[i];
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    kand &= shfl_xor_u64(kand, m);
-    kor |= shfl_xor_u64(kor, m);
-  }
+  wave_and_or64(kand, kor);
   if (lane == 0) {
     sc.wand[w] = kand;
     sc.wor[w] = kor;
@@ -535,11 +516,7 @@ __device__ void kth_key2(const uint64_t* keysA, int KA, const uint64_t* keysB, i
     kand &= keysA[i] & keysB[i];
     kor |= keysA[i] | keysB[i];
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    kand &= shfl_xor_u64(kand, m);
-    kor |= shfl_xor_u64(kor, m);
-  }
+  wave_and_or64(kand, kor);
   if (lane == 0) {
     sc.wand[w] = kand;
     sc.wor[w] = kor;

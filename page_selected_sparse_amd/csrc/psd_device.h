@@ -46,6 +46,59 @@ __device__ __forceinline__ int effective_budget(int n, int budget) {
   return b < n ? b : n;
 }
 
+// ---- wave-wide primitives on DPP row moves and lane reads (no LDS round trips) ----
+// DPP control codes: row_shr:n = 0x110 + n, row_ror:n = 0x120 + n, row_bcast:15 = 0x142
+// (lane 15 of each row to the next row), row_bcast:31 = 0x143 (lane 31 to rows 2 and 3).
+// Lanes without a source, or in rows outside ROW_MASK, read 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_move(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts within each 16-lane row, then the row
+// totals carried into the rows above.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += dpp_move<0x111>(x);
+  x += dpp_move<0x112>(x);
+  x += dpp_move<0x114>(x);
+  x += dpp_move<0x118>(x);
+  x += dpp_move<0x142, 0xa>(x);
+  x += dpp_move<0x143, 0xc>(x);
+  return x;
+}
+
+// AND and OR of a 64-bit value over the 64 lanes (uniform results): rotations within
+// each row, then the four row results read out of lanes 0, 16, 32 and 48.
+__device__ __forceinline__ void wave_and_or64(uint64_t& a, uint64_t& o) {
+  int al = (int)(uint32_t)a, ah = (int)(uint32_t)(a >> 32);
+  int ol = (int)(uint32_t)o, oh = (int)(uint32_t)(o >> 32);
+#define PSD_ROT_STEP(C)      \
+  al &= dpp_move<C>(al);     \
+  ah &= dpp_move<C>(ah);     \
+  ol |= dpp_move<C>(ol);     \
+  oh |= dpp_move<C>(oh);
+  PSD_ROT_STEP(0x121)
+  PSD_ROT_STEP(0x122)
+  PSD_ROT_STEP(0x124)
+  PSD_ROT_STEP(0x128)
+#undef PSD_ROT_STEP
+  uint32_t ra = ~0u, rb = ~0u, rc = 0u, rd = 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    ra &= (uint32_t)__builtin_amdgcn_readlane(al, 16 * r);
+    rb &= (uint32_t)__builtin_amdgcn_readlane(ah, 16 * r);
+    rc |= (uint32_t)__builtin_amdgcn_readlane(ol, 16 * r);
+    rd |= (uint32_t)__builtin_amdgcn_readlane(oh, 16 * r);
+  }
+  a = ((uint64_t)rb << 32) | ra;
+  o = ((uint64_t)rd << 32) | rc;
+}
+
+// Value of x in lane `src` (a wave-uniform lane index).
+__device__ __forceinline__ int lane_value(int x, int src) {
+  return __builtin_amdgcn_readlane(x, src);
+}
+
 template <typename T>
 __device__ __forceinline__ uint4 load16(const T* p) {
   return *reinterpret_cast<const uint4*>(p);

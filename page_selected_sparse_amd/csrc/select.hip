@@ -61,21 +61,6 @@ struct SelScratch {
   uint64_t wand[16], wor[16];
 };
 
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)x, m, 64), hi = __shfl_xor((uint32_t)(x >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // Finds the top K (1 <= K <= N) of keys[0..N) in LDS by radix select over 8-bit digits.
 // Key 0 marks an empty slot: it never ranks (score keys of finite scores are nonzero and
 // far above it). The bits every nonzero key shares are skipped: the first digit starts at
@@ -100,11 +85,7 @@ __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch
       kor |= key;
     }
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    kand &= shfl_xor64(kand, m);
-    kor |= shfl_xor64(kor, m);
-  }
+  wave_and_or64(kand, kor);
   if (lane == 0) {
     sc.wand[w] = kand;
     sc.wor[w] = kor;
@@ -150,7 +131,7 @@ __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch
     const int base = 255 - 4 * lane;
     const int c0 = hist[base], c1 = hist[base - 1], c2 = hist[base - 2], c3 = hist[base - 3];
     const int local = c0 + c1 + c2 + c3;
-    const int incl = wave_inclusive_scan(local);
+    const int incl = wave_scan_incl(local);
     const int excl = incl - local;
     const bool mine = excl < k && k <= incl;
     int r = k - excl, dg = base, cnt = c0;
@@ -170,9 +151,9 @@ __device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch
       }
     }
     const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-    dg = __shfl(dg, src, 64);
-    r = __shfl(r, src, 64);
-    cnt = __shfl(cnt, src, 64);
+    dg = lane_value(dg, src);
+    r = lane_value(r, src);
+    cnt = lane_value(cnt, src);
     // the buffer of the next pass but one was last read before this pass's barrier
     for (int i = tid; i < 256; i += NT) sc.hist[(pass + 2) % 3][i] = 0;
     prefix |= (uint64_t)dg << lo;
@@ -193,9 +174,9 @@ template <int NT>
 __device__ __forceinline__ int block_excl_sum(int x, SelScratch& sc, int& total, int buf = 0) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int incl = wave_inclusive_scan(x);
+  const int incl = wave_scan_incl(x);
   if constexpr (NW == 1) {
-    total = __shfl(incl, 63, 64);
+    total = lane_value(incl, 63);
     return incl - x;
   }
   if (lane == 63) sc.wave_cnt[buf][w] = incl;
@@ -627,7 +608,8 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   };
   const bool once = nhp == 1 && NDC == 1;
   const int64_t bt0 = (int64_t)s * a.max_pages;
-  uint4* stage = reinterpret_cast<uint4*>(lds + a.chunk * sizeof(uint64_t)) + (tid >> 6) * STAGE;
+  // one key slot per lane and round (a one-wave chunk may be narrower than the wave)
+  uint4* stage = reinterpret_cast<uint4*>(lds + NT * a.ppt * sizeof(uint64_t)) + (tid >> 6) * STAGE;
   // DPP path: the first page set's block ids and statistics loads go out before the q
   // table is built, and the table's barrier waits only for LDS writes, so that the table
   // is built while those loads are in flight.
@@ -761,6 +743,12 @@ hipError_t set_lds(K kernel, size_t lds) {
 #ifndef PSD_CHUNK_STAGES
 #define PSD_CHUNK_STAGES 1
 #endif
+#ifndef PSD_WAVE_CHUNK
+#define PSD_WAVE_CHUNK 64  // pages of a one-wave chunk workgroup
+#endif
+#ifndef PSD_MERGE_BIG
+#define PSD_MERGE_BIG 4096  // candidates above which a unit merge takes 1024 threads
+#endif
 #ifndef PSD_UNIT_MIN_UNITS
 #define PSD_UNIT_MIN_UNITS 128  // units that fill the GPU with one workgroup each
 #endif
@@ -857,7 +845,7 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   };
   // the tuned staging of a workgroup size if it fits, else one chunk at a time
   auto pick_staging = [&](int cpl, int st) {
-    const size_t keys = (size_t)p->chunk * 8;
+    const size_t keys = (size_t)p->threads * p->ppt * 8;
     if (cpl == 4 && p->threads == 64) st = 1;
     if (static_lds + keys + (size_t)(p->threads / 64) * stage_bytes(cpl, st) <= kLdsLimit) {
       p->cpl = cpl;
@@ -888,7 +876,8 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
     const bool multi_pass = !p->all_q && (g.G > 16 || 16 * g.D * 16 > 32768);
     for (int ppt = 1; ppt <= 64; ppt *= 2) {
       if (multi_pass && ppt > 1) break;
-      const int chunk = p->threads * ppt;
+      // a one-wave workgroup may take fewer pages than lanes: more waves share a unit
+      const int chunk = p->threads == 64 && ppt == 1 ? PSD_WAVE_CHUNK : p->threads * ppt;
       if (chunk * sizeof(uint64_t) > 65536) break;
       const int nchunk = (inner + chunk - 1) / chunk;
       if (nchunk > kMaxChunks) continue;
@@ -923,8 +912,8 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   p->merge_lds = (size_t)p->ustride * (sizeof(uint64_t) + sizeof(int32_t)) +
                  (size_t)p->nchunk * sizeof(int32_t);
   const int64_t cands = (int64_t)p->nchunk * p->cap;
-  p->merge_threads = cands <= 512 ? 64 : (cands <= 4096 ? kThreads : 1024);
-  p->score_lds = (size_t)p->chunk * sizeof(uint64_t);
+  p->merge_threads = cands <= 512 ? 64 : (cands <= PSD_MERGE_BIG ? kThreads : 1024);
+  p->score_lds = (size_t)p->threads * p->ppt * sizeof(uint64_t);
   if (dpp) p->score_lds += (size_t)(p->threads / 64) * stage_bytes(p->cpl, p->stages);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   p->off_idx = al(slots * sizeof(uint64_t));
