@@ -583,13 +583,36 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
   const int unit = s * a.Hkv + g;
+  const int lo = 1 + c * a.chunk;
+  const int64_t bt0 = (int64_t)s * a.max_pages;
+  // one key slot per lane and round (a one-wave chunk may be narrower than the wave)
+  uint4* stage = reinterpret_cast<uint4*>(lds + NT * a.ppt * sizeof(uint64_t)) + (tid >> 6) * STAGE;
+  // DPP path: the first page set's block ids and statistics loads go out before the
+  // sequence length is known and before the q table is built. The block-table index is
+  // clamped to the row and the block id to the pool, so that these loads stay in bounds
+  // whatever the row holds past the sequence; lanes past the chunk's pages load a record
+  // they never use. A wave that issued them waits for them before it exits.
+  // Only the block id stays live across the barrier; the record offsets are recomputed
+  // after it (the empty asm keeps the compiler from reusing the first ones).
+  const bool pre = DPP && lo + (tid & ~63) < a.max_pages - 1;
+  int blk0 = 0;
+  if constexpr (DPP) {
+    if (pre) {
+      blk0 = a.bt[bt0 + min(lo + tid, a.max_pages - 1)];
+      blk0 = min(max(blk0, 0), a.num_blocks - 1);
+      DppPage<BF16, D, HB, CPL, S> first;
+      first.init(a.meta, a.Hkv, blk0, g, stage);
+      first.issue_first();
+    }
+  }
   const UnitInfo u = unit_info(a, s);
   if (c == 0) write_row_header<NT>(a, unit, u);
-  if (u.trivial) return;
   const int kp = u.kp, n = u.n;
-  const int lo = 1 + c * a.chunk;
   const int hi = min(lo + a.chunk, n - 1);
-  if (lo >= hi) return;
+  if (u.trivial || lo >= hi) {
+    if (pre) wait_vm<0>();
+    return;
+  }
   const int cnt = hi - lo;
   const int nhp = ceil_div(a.G, HB);
 
@@ -607,24 +630,7 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
     }
   };
   const bool once = nhp == 1 && NDC == 1;
-  const int64_t bt0 = (int64_t)s * a.max_pages;
-  // one key slot per lane and round (a one-wave chunk may be narrower than the wave)
-  uint4* stage = reinterpret_cast<uint4*>(lds + NT * a.ppt * sizeof(uint64_t)) + (tid >> 6) * STAGE;
-  // DPP path: the first page set's block ids and statistics loads go out before the q
-  // table is built, and the table's barrier waits only for LDS writes, so that the table
-  // is built while those loads are in flight.
-  // Only the block id stays live across the barrier; the record offsets are recomputed
-  // after it (the empty asm keeps the compiler from reusing the first ones).
-  const bool pre = DPP && (tid & ~63) < cnt;
-  int blk0 = 0;
-  if constexpr (DPP) {
-    if (pre) {
-      blk0 = a.bt[bt0 + (tid < cnt ? lo + tid : lo)];
-      DppPage<BF16, D, HB, CPL, S> first;
-      first.init(a.meta, a.Hkv, blk0, g, stage);
-      first.issue_first();
-    }
-  }
+  // the table's barrier waits only for LDS writes: it is built while the loads fly
   if (once) {
     load_qlds(0, 0);
     if constexpr (DPP) {
@@ -678,6 +684,9 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
       }
     }
     keys[o] = score_key(best);  // every slot written; slots past cnt are never read
+  }
+  if constexpr (DPP) {
+    if (pre) wait_vm<0>();  // a wave that skipped every round still has its first loads
   }
   __syncthreads();
 
@@ -748,6 +757,12 @@ hipError_t set_lds(K kernel, size_t lds) {
 #endif
 #ifndef PSD_MERGE_BIG
 #define PSD_MERGE_BIG 4096  // candidates above which a unit merge takes 1024 threads
+#endif
+#ifndef PSD_WAVE_WG_MAX
+#define PSD_WAVE_WG_MAX 512  // one-wave chunk workgroups below this many 256-page chunks
+#endif
+#ifndef PSD_MIN_PPT
+#define PSD_MIN_PPT 1
 #endif
 #ifndef PSD_UNIT_MIN_UNITS
 #define PSD_UNIT_MIN_UNITS 128  // units that fill the GPU with one workgroup each
@@ -872,9 +887,9 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
     ok = true;
   } else {
     // one-wave workgroups when 256-thread ones would leave the GPU mostly idle
-    p->threads = (dpp && units * ((inner + kThreads - 1) / kThreads) < 512) ? 64 : kThreads;
+    p->threads = (dpp && units * ((inner + kThreads - 1) / kThreads) < PSD_WAVE_WG_MAX) ? 64 : kThreads;
     const bool multi_pass = !p->all_q && (g.G > 16 || 16 * g.D * 16 > 32768);
-    for (int ppt = 1; ppt <= 64; ppt *= 2) {
+    for (int ppt = PSD_MIN_PPT; ppt <= 64; ppt *= 2) {
       if (multi_pass && ppt > 1) break;
       // a one-wave workgroup may take fewer pages than lanes: more waves share a unit
       const int chunk = p->threads == 64 && ppt == 1 ? PSD_WAVE_CHUNK : p->threads * ppt;
