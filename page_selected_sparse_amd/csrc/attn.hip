@@ -37,6 +37,7 @@ struct AttnArgs {
   const int32_t* cnt;
   float* pacc;  // [B, Hq, nsplit, Dv]
   float2* pml;  // [B, Hq, nsplit]
+  float* out;   // [B, Hq, Dv]: written directly when one workgroup holds a whole unit
   int Hq, Hkv, G, max_pages, b_max, pps, nsplit, num_blocks;
   int64_t kbs, kts, khs, vbs, vts, vhs;
   float sl2;  // scale * log2(e)
@@ -118,10 +119,24 @@ __device__ __forceinline__ void load_frag8(const void* base, int64_t off, uint4&
 #ifndef PSD_ATTN_TARGET_WIDE
 #define PSD_ATTN_TARGET_WIDE 256  // workgroups of 2+ waves (groups over 16 heads)
 #endif
+#ifndef PSD_ATTN_UNIT_WAVES
+#define PSD_ATTN_UNIT_WAVES 16  // waves of a whole-unit workgroup
+#endif
+#ifndef PSD_ATTN_UNIT_MIN
+#define PSD_ATTN_UNIT_MIN 128  // units that fill the GPU with one workgroup each
+#endif
+#ifndef PSD_ATTN_UNIT_DENSE
+#define PSD_ATTN_UNIT_DENSE 0  // whole-unit workgroups for the dense walk too
+#endif
 
-template <bool BF16, int DQK, int DV, int WAVES, int MIN_WAVES_PER_SIMD>
-__global__ __launch_bounds__(64 * WAVES)
+// NWS > 0: one workgroup per unit (groups of up to 16 heads), its NWS waves being the
+// splits: wave w takes the unit's list entries w, w + NWS, w + 2 NWS, ..., and the waves'
+// partials are combined in LDS at the end, so that no partial leaves the workgroup.
+template <bool BF16, int DQK, int DV, int WAVES, int MIN_WAVES_PER_SIMD, int NWS = 0>
+__global__ __launch_bounds__(64 * (NWS > 0 ? NWS : WAVES))
 __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnArgs a) {
+  constexpr bool UNIT = NWS > 0;
+  static_assert(!UNIT || (WAVES == 1 && DQK <= 128), "unit workgroups: one head tile");
   constexpr bool PIPE = PSD_ATTN_PIPE != 0 && BF16;
   constexpr int NQ = DQK / 32;   // QK MFMAs per page (K = 32 dims each)
   constexpr int NC = DV / 16;    // PV MFMAs per page (16 output columns each)
@@ -130,31 +145,41 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
-  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int p0 = split * a.pps;
-  // The selection entries of this split are requested together with the length and the
-  // count (the row holds b_max entries; lanes past it read its last entry), so that only
-  // the block-table lookup stands between them and the first K/V loads.
-  int sel_lp = p0 + lane;
-  if (a.sel) sel_lp = a.sel[(int64_t)(s * a.Hkv + g) * a.b_max + min(p0 + lane, a.b_max - 1)];
+  const int split = UNIT ? wave : blockIdx.x;
+  const int g = UNIT ? blockIdx.x : blockIdx.y, s = UNIT ? blockIdx.y : blockIdx.z;
+  const int hw = UNIT ? 0 : wave;  // head tile of this wave
+  // List entries of this split: first + stride * i.
+  const int first = UNIT ? wave : split * a.pps;
+  const int stride = UNIT ? NWS : 1;
+  const int64_t srow = (int64_t)(s * a.Hkv + g) * a.b_max;
+  // The first selection entries are requested together with the length and the count
+  // (the row holds b_max entries; lanes past it read its last entry), so that only the
+  // block-table lookup stands between them and the first K/V loads.
+  int sel_lp = first + stride * lane;
+  if (a.sel) sel_lp = a.sel[srow + min(sel_lp, a.b_max - 1)];
   const int L = a.lens[s];
   const int n = ceil_div(L, kPage);
   int count = a.sel ? min(a.cnt[s * a.Hkv + g], a.b_max) : n;
-  if (count < 0) count = 0;  // flagged unit: the merge writes NaN
-  if (p0 >= count) return;
-  const int np = min(a.pps, count - p0);
+  if (count < 0) count = 0;  // flagged unit: its output is NaN
+  const int total = first >= count ? 0
+                    : (UNIT ? ceil_div(count - first, stride) : min(a.pps, count - first));
+  if (!UNIT && total == 0) return;
 
-  // Page list of this split: lane i holds entry p0 + i. Entries are clamped to the
-  // sequence's pages so that a malformed list can never address outside the table.
+  // Page list of a batch of up to 64 entries: lane i holds entry first + stride * (b0 + i).
+  // Entries are clamped to the sequence's pages so that a malformed list can never
+  // address outside the table.
   int my_lp = 0, my_blk = 0;
-  if (lane < np) {
-    my_lp = min(max(sel_lp, 0), n - 1);
-    my_blk = a.bt[(int64_t)s * a.max_pages + my_lp];
-    my_blk = min(max(my_blk, 0), a.num_blocks - 1);
-  }
+  auto set_batch = [&](int np) {
+    my_lp = my_blk = 0;
+    if (lane < np) {
+      my_lp = min(max(sel_lp, 0), n - 1);
+      my_blk = a.bt[(int64_t)s * a.max_pages + my_lp];
+      my_blk = min(max(my_blk, 0), a.num_blocks - 1);
+    }
+  };
 
   // Q tile as the B operand of S^T = K Q^T: lane holds head r, dims 32c + 8grp .. +8.
-  const int head = wave * 16 + r;  // within the group
+  const int head = hw * 16 + r;  // within the group
   const bool hvalid = head < a.G;
   const int64_t qrow = ((int64_t)s * a.Hq + g * a.G + (hvalid ? head : 0)) * DQK;
   uint4 qhi[QREG ? NQ : 1], qlo[QREG ? NQ : 1];
@@ -344,30 +369,79 @@ __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnAr
     }
   };
 
-  if constexpr (EARLY && PIPE) {
-    // Two register sets: page i + 1's loads are in flight while page i is computed.
-    PageRegs A, B;
-    issue(0, A);
-    for (int i = 0; i < np; i += 2) {
-      if (i + 1 < np) issue(i + 1, B);
-      compute(i, A);
-      if (i + 1 >= np) break;
-      if (i + 2 < np) issue(i + 2, A);
-      compute(i + 1, B);
+  for (int b0 = 0; b0 < total; b0 += 64) {
+    const int np = min(64, total - b0);
+    if (b0 > 0) {
+      const int e = first + stride * (b0 + lane);
+      sel_lp = a.sel ? a.sel[srow + min(e, a.b_max - 1)] : e;
     }
-  } else {
-    PageRegs A;
-    for (int i = 0; i < np; ++i) {
-      issue(i, A);
-      compute(i, A);
+    set_batch(np);
+    if constexpr (EARLY && PIPE) {
+      // Two register sets: page i + 1's loads are in flight while page i is computed.
+      PageRegs A, B;
+      issue(0, A);
+      for (int i = 0; i < np; i += 2) {
+        if (i + 1 < np) issue(i + 1, B);
+        compute(i, A);
+        if (i + 1 >= np) break;
+        if (i + 2 < np) issue(i + 2, A);
+        compute(i + 1, B);
+      }
+    } else {
+      PageRegs A;
+      for (int i = 0; i < np; ++i) {
+        issue(i, A);
+        compute(i, A);
+      }
     }
+  }
+
+  if constexpr (UNIT) {
+    // Combine the waves: M = max m_w, out = sum acc_w 2^(m_w - M) / sum l_w 2^(m_w - M).
+    // A wave without pages has m = -inf, l = 0 and acc = 0 and weighs nothing.
+    extern __shared__ float ush[];  // acc [NWS][G][DV] | (m, l) [NWS][16]
+    float2* lml = reinterpret_cast<float2*>(ush + NWS * a.G * DV);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hh = 4 * grp + j;
+      if (hh < a.G) {
+        float* dst = ush + (wave * a.G + hh) * DV + r * NC;
+#pragma unroll
+        for (int c = 0; c < NC; c += 4)
+          *reinterpret_cast<float4*>(dst + c) =
+              make_float4(acc[c][j], acc[c + 1][j], acc[c + 2][j], acc[c + 3][j]);
+      }
+    }
+    if (grp == 0 && hvalid) lml[wave * 16 + head] = make_float2(m_run, l_run);
+    __syncthreads();
+    float* out = a.out + ((int64_t)s * a.Hq + g * a.G) * DV;
+    for (int t = threadIdx.x; t < a.G * DV; t += 64 * NWS) {
+      const int h = t / DV, d = t - h * DV;
+      if (count == 0) {
+        out[t] = __builtin_nanf("");
+        continue;
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWS; ++w) M = fmaxf(M, lml[w * 16 + h].x);
+      float l = 0.f, o = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWS; ++w) {
+        const float2 ml = lml[w * 16 + h];
+        const float wt = exp2f(ml.x - M);
+        l += ml.y * wt;
+        o += ush[(w * a.G + h) * DV + d] * wt;
+      }
+      out[t] = o / l;
+    }
+    return;
   }
 
   // ---- partials: acc rows are heads 4grp + j, columns d = r*NC + c ----------------------
   const int64_t ubase = (int64_t)s * a.Hq + g * a.G;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int hh = wave * 16 + 4 * grp + j;
+    const int hh = hw * 16 + 4 * grp + j;
     if (hh < a.G) {
       float* dst = a.pacc + ((ubase + hh) * a.nsplit + split) * DV + r * NC;
 #pragma unroll
@@ -702,6 +776,17 @@ hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) 
   return hipGetLastError();
 }
 
+template <bool BF16, int D>
+hipError_t launch_unit(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr int NW = PSD_ATTN_UNIT_WAVES;
+  auto kern = &attn_kernel<BF16, D, D, 1, (NW + 3) / 4, NW>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_latent(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) {
   switch (waves) {
     case 1: hipLaunchKernelGGL(attn_latent_kernel<1>, grid, dim3(64), 0, st, a); break;
@@ -722,6 +807,16 @@ bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* p
   if (max_pages_attended < 1) return false;
   p->waves = (g.G + 15) / 16;
   const int64_t units = (int64_t)g.B * g.Hkv;
+  p->unit = 0;
+  if (g.G <= 16 && g.D <= 128 && units >= PSD_ATTN_UNIT_MIN && (!dense || PSD_ATTN_UNIT_DENSE)) {
+    // one workgroup per unit, its waves the splits, combined in LDS: no partials
+    p->unit = PSD_ATTN_UNIT_WAVES;
+    p->pps = (max_pages_attended + p->unit - 1) / p->unit;
+    p->nsplit = 1;
+    p->off_ml = 0;
+    p->bytes = 256;
+    return true;
+  }
   // Aim for PSD_ATTN_TARGET single-wave workgroups (fewer, larger ones for many-head
   // groups).
   const int64_t target =
@@ -744,12 +839,20 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
                          float* out, void* ws, hipStream_t st) {
   unsigned char* w = static_cast<unsigned char*>(ws);
   AttnArgs a{q, k, v, bt, lens, sel, cnt,
-             reinterpret_cast<float*>(w), reinterpret_cast<float2*>(w + p.off_ml),
+             reinterpret_cast<float*>(w), reinterpret_cast<float2*>(w + p.off_ml), out,
              g.Hq, g.Hkv, g.G, g.max_pages, b_max, p.pps, p.nsplit, g.num_blocks,
              g.kbs, g.kts, g.khs, g.vbs, g.vts, g.vhs, scale * 1.4426950408889634f};
   const dim3 grid(p.nsplit, g.Hkv, g.B);
   hipError_t e;
   const bool bf = g.dtype == 1;
+  if (p.unit) {
+    const size_t lds = (size_t)PSD_ATTN_UNIT_WAVES * g.G * g.Dv * sizeof(float) +
+                       (size_t)PSD_ATTN_UNIT_WAVES * 16 * sizeof(float2);
+    const dim3 ugrid(g.Hkv, g.B);
+    if (g.D == 64)
+      return bf ? launch_unit<true, 64>(a, ugrid, lds, st) : launch_unit<false, 64>(a, ugrid, lds, st);
+    return bf ? launch_unit<true, 128>(a, ugrid, lds, st) : launch_unit<false, 128>(a, ugrid, lds, st);
+  }
   if (g.D == 64)
     e = bf ? launch_attn<true, 64, 64>(a, grid, p.waves, st)
            : launch_attn<false, 64, 64>(a, grid, p.waves, st);

@@ -66,9 +66,10 @@ hipError_t launch_certify(const Geo& g, const SelectPlan& plan, const void* q, c
 
 // ---- attention -------------------------------------------------------------------------
 struct DecodePlan {
-  int pps;     // pages per split (one workgroup)
+  int pps;     // pages per split (one workgroup, or one wave of a whole-unit workgroup)
   int nsplit;  // splits per unit
   int waves;   // waves per workgroup = ceil(G / 16) head tiles
+  int unit;    // > 0: one workgroup of `unit` waves per unit, combined in LDS (no merge)
   size_t off_ml, bytes;
 };
 // dense: every page of each sequence is attended (splits sized for long page walks).

@@ -90,6 +90,15 @@ def test_capacity_flag_not_truncation():
     assert np.all(np.isnan(res["out"][0]))
 
 
+def test_capacity_flag_whole_unit_attention():
+    # 128 units: each takes one whole-unit attention workgroup; flagged units give NaN
+    w = synth.make_workload(synth.small_spec(batch=64, seq_lens=(1000, 100) * 32,
+                                             budget_pages=20, max_len=1008))
+    res = run_gpu(w, b_max=10, dense=False)
+    assert np.all(res["cnt"][0::2] == -1) and np.all(np.isnan(res["out"][0::2]))
+    check_workload(w, res, seqs=list(range(1, 64, 2)), dense_seqs=[])
+
+
 def test_tie_break_across_chunks():
     # 40 pages spread over several 256-page chunks get identical keys that beat every
     # other page; with 25 free slots the 25 lowest-index copies must win.
