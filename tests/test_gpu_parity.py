@@ -99,6 +99,16 @@ def test_capacity_flag_whole_unit_attention():
     check_workload(w, res, seqs=list(range(1, 64, 2)), dense_seqs=[])
 
 
+def test_whole_unit_attention_long_lists():
+    # 128 units whose kept lists exceed 64 entries per wave of a whole-unit attention
+    # workgroup (1,100 of 1,150 pages), so that each wave walks its list in batches
+    lens = tuple(16 * 1150 - 3 * i for i in range(64))
+    w = synth.make_workload(synth.small_spec(batch=64, seq_lens=lens, budget_pages=1100,
+                                             needles=2, max_len=16 * 1150))
+    res = run_gpu(w, dense=False)
+    check_workload(w, res, seqs=[0, 37, 63], dense_seqs=[])
+
+
 def test_tie_break_across_chunks():
     # 40 pages spread over several 256-page chunks get identical keys that beat every
     # other page; with 25 free slots the 25 lowest-index copies must win.
