@@ -125,6 +125,24 @@ __device__ __forceinline__ void lds2i(uint32_t base, uint4& x0, uint4& x1) {
   x1 = make_uint4(r1.x, r1.y, r1.z, r1.w);
 }
 
+// The same two reads without the wait: the registers are defined once a later
+// lgkm_wait2 on them has run (LDS reads complete in order).
+template <int O0, int O1>
+__device__ __forceinline__ void lds2i_issue(uint32_t base, u32x4p& r0, u32x4p& r1) {
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:%3\n\t"
+      "ds_read_b128 %1, %2 offset:%4"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(base), "n"(O0), "n"(O1)
+      : "memory");
+}
+// Waits until at most N LDS / scalar-memory operations are outstanding; r0 and r1 are
+// tied to the wait so that no use of them can move above it.
+template <int N>
+__device__ __forceinline__ void lgkm_wait2(u32x4p& r0, u32x4p& r1) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r0), "+v"(r1) : "n"(N));
+}
+
 template <int KB, int KPW, typename F>
 __device__ __forceinline__ void for_kb(F&& f) {
   if constexpr (KB < KPW) {
@@ -323,10 +341,20 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
     float sum[4] = {0.f, 0.f, 0.f, 0.f};
     float4v chain = {0.f, 0.f, 0.f, 0.f};
     u16x2 amax = {0, 0};
+    // the reads of step kb + 2 are in flight while step kb's MFMAs run
+    u32x4p ra[2][2];
+    lds2i_issue<0, 64>(row, ra[0][0], ra[0][1]);
     for_kb<0, KPW>([&](auto kbc) {
       constexpr int kb = decltype(kbc)::value;
-      uint4 x0, x1;
-      lds2i<64 * kb, 64 * (kb + 1)>(row, x0, x1);
+      constexpr int cur = (kb / 2) & 1;
+      if constexpr (kb + 2 < KPW) {
+        lds2i_issue<64 * (kb + 2), 64 * (kb + 3)>(row, ra[cur ^ 1][0], ra[cur ^ 1][1]);
+        lgkm_wait2<2>(ra[cur][0], ra[cur][1]);
+      } else {
+        lgkm_wait2<0>(ra[cur][0], ra[cur][1]);
+      }
+      const uint4 x0 = make_uint4(ra[cur][0].x, ra[cur][0].y, ra[cur][0].z, ra[cur][0].w);
+      const uint4 x1 = make_uint4(ra[cur][1].x, ra[cur][1].y, ra[cur][1].z, ra[cur][1].w);
       // a chain of kPreChain k blocks accumulates in the MFMA, then joins the fp32 sum
       if constexpr (kb % kPreChain == 0) chain = float4v{0.f, 0.f, 0.f, 0.f};
       chain = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(x0), as_bf8(qf[kb]), chain, 0, 0, 0);
