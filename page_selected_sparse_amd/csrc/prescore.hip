@@ -10,10 +10,12 @@
 //   UB_h(p) = sum_d q+_hd kmax_pd + q-_hd kmin_pd = [Q+ | Q-] . [Kmax ; Kmin]
 //
 // is a contraction over k = 2D whose operands are bf16 values: every product is exact in
-// fp32. A chain of C MFMAs (32 products each) accumulates from zero, and the chain's fp32
-// result is added into a running fp32 sum (one sum per (head, page)), so every product
-// passes a bounded number of roundings: at most 33 C inside the chain (any summation
-// order inside an MFMA, faithful rounding: unit 2^-23) and K/C + 1 in the sum (2^-24):
+// fp32. Chains of at most C MFMAs (32 products each; the even and the odd k blocks of
+// each run of 2C form two chains) accumulate from zero, and each chain's fp32 result is
+// added into a running fp32 sum (one sum per (head, page)). With K k blocks there are at
+// most 2 ceil(K / 2C) <= K/C + 1 chains, so every product passes a bounded number of
+// roundings: at most 33 C inside its chain (any summation order inside an MFMA, faithful
+// rounding: unit 2^-23) and K/C + 1 in the sum (2^-24):
 //   |UB~ - UB| <= (gamma_33C(2^-23) + gamma_{K/C+1}(2^-24)(1 + ...)) sum_d |q_hd||c_pd|
 //              <= 1.6e-5 * ||q_h||_1 * M_p + tiny          (C = 4, K <= 36 k blocks)
 // with M_p the largest |statistic| of the page record and gamma_n(u) = n u / (1 - n u).
@@ -273,20 +275,32 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
 
   const int64_t rec_bytes = NCH * 128;
   const int my_loads = (NLD - wave + WAVES - 1) / WAVES;
+  constexpr int MLW0 = (NLD + WAVES - 1) / WAVES;  // most load instructions per wave and tile
   auto issue = [&](int t, int st) {
-    for (int ins = wave; ins < NLD; ins += WAVES) {
+    // every block id first (one LDS round trip), then the loads
+    int blk[MLW0], piece[MLW0];
+#pragma unroll
+    for (int j = 0; j < MLW0; ++j) {
+      const int ins = wave + j * WAVES;
       const int slot = ins * 64 + lane;
-      int row = slot / SLP, piece = slot - row * SLP;
+      int row = slot / SLP, pc = slot - row * SLP;
       if (row >= 16) {
         row = 15;
-        piece = 0;
+        pc = 0;
       }
-      if (piece == SLP - 1) piece = 0;
-      const int blk = blk_of[16 * t + row];
-      const unsigned char* src =
-          a.meta + ((int64_t)blk * a.Hkv + g) * rec_bytes + (int64_t)piece * 16;
-      __builtin_amdgcn_global_load_lds(
-          src, (__attribute__((address_space(3))) void*)(stage + st * STG + ins * 64), 16, 0, 0);
+      if (pc == SLP - 1) pc = 0;
+      piece[j] = pc;
+      blk[j] = ins < NLD ? blk_of[16 * t + row] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < MLW0; ++j) {
+      const int ins = wave + j * WAVES;
+      if (ins < NLD) {
+        const unsigned char* src =
+            a.meta + ((int64_t)blk[j] * a.Hkv + g) * rec_bytes + (int64_t)piece[j] * 16;
+        __builtin_amdgcn_global_load_lds(
+            src, (__attribute__((address_space(3))) void*)(stage + st * STG + ins * 64), 16, 0, 0);
+      }
     }
   };
   // combines tile t's per-wave head maxima and writes its pages' results
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
   float* second = a.second + (int64_t)unit * a.max_inner;
   int32_t* best = a.best + (int64_t)unit * a.max_inner;
   auto finish = [&](int t) {
-    if (tid < 16) {
+    if (tid < 16) {  // wave 0 (the record maxima come from the last head tile's waves)
       const int i = 16 * (t0 + t) + tid;  // inner page index
       if (i < inner) {
         // the leading 16-head tile and the best of the other tiles
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
     const uint32_t row =
         sbase + (uint32_t)((t % NST) * STG + r * SLP + grp) * 16 + 64 * kb0;
     float sum[4] = {0.f, 0.f, 0.f, 0.f};
-    float4v chain = {0.f, 0.f, 0.f, 0.f};
+    float4v chain = {0.f, 0.f, 0.f, 0.f}, chain2 = {0.f, 0.f, 0.f, 0.f};
     u16x2 amax = {0, 0};
     // the reads of step kb + 2 are in flight while step kb's MFMAs run
     u32x4p ra[2][2];
@@ -355,15 +369,23 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
       }
       const uint4 x0 = make_uint4(ra[cur][0].x, ra[cur][0].y, ra[cur][0].z, ra[cur][0].w);
       const uint4 x1 = make_uint4(ra[cur][1].x, ra[cur][1].y, ra[cur][1].z, ra[cur][1].w);
-      // a chain of kPreChain k blocks accumulates in the MFMA, then joins the fp32 sum
-      if constexpr (kb % kPreChain == 0) chain = float4v{0.f, 0.f, 0.f, 0.f};
+      // two independent chains (even and odd k blocks), each of up to kPreChain MFMAs,
+      // so that consecutive MFMAs do not wait on each other; each chain then joins the
+      // fp32 sum (the same number of additions as one chain per kPreChain k blocks)
+      if constexpr (kb % (2 * kPreChain) == 0) {
+        chain = float4v{0.f, 0.f, 0.f, 0.f};
+        chain2 = float4v{0.f, 0.f, 0.f, 0.f};
+      }
       chain = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(x0), as_bf8(qf[kb]), chain, 0, 0, 0);
-      chain = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(x1), as_bf8(qf[kb + 1]), chain, 0, 0, 0);
-      if constexpr ((kb + 2) % kPreChain == 0 || kb + 2 >= KPW) {
+      chain2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(x1), as_bf8(qf[kb + 1]), chain2, 0, 0, 0);
+      if constexpr ((kb + 2) % (2 * kPreChain) == 0 || kb + 2 >= KPW) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sum[i] += chain[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[i] += chain2[i];
       }
-      // every wave tracks it (no branch in the MFMA stream); head tile 0 reports it. The
+      // every wave tracks it (no branch in the MFMA stream); the last head tile reports
+      // it (wave 0 already finishes the previous tile). The
       // empty asm pins the running max each step, so that the max is not reassociated
       // into a tree that would keep every fragment alive to the end.
       const uint32_t ws[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -376,7 +398,7 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
       // keep each step's reads, MFMAs and adds together (short register live ranges)
       __builtin_amdgcn_sched_barrier(0);
     });
-    if (ht == 0) {
+    if (ht == HT - 1) {
       // page r's record (this wave's k blocks) spans the four grp lanes of row r
       uint32_t m = amax.x > amax.y ? amax.x : amax.y;
       m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
@@ -402,8 +424,7 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
       for (int i = 0; i < 4; ++i) {
         float v = sum[i];
         if (!__builtin_isfinite(v)) v = __builtin_inff();
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+        v = row_max16(v);
         if (r == 0) wmax[t & 1][ht][4 * grp + i] = v;
       }
     }

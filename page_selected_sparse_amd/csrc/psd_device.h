@@ -94,6 +94,16 @@ __device__ __forceinline__ void wave_and_or64(uint64_t& a, uint64_t& o) {
   o = ((uint64_t)rd << 32) | rc;
 }
 
+// Maximum over the 16 lanes of each row, in every lane of the row (rotations by 1, 2, 4
+// and 8 within the row).
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, __int_as_float(dpp_move<0x121>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<0x122>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<0x124>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<0x128>(__float_as_int(v))));
+  return v;
+}
+
 // Value of x in lane `src` (a wave-uniform lane index).
 __device__ __forceinline__ int lane_value(int x, int src) {
   return __builtin_amdgcn_readlane(x, src);
