@@ -840,7 +840,18 @@ __global__ __launch_bounds__(NT) void certify_kernel(PreArgs a) {
 
   // the remaining slots go to the best undecided pages, ties to the lower page
   const int need = kp - total_i;
-  if (need > 0) {
+  if (need > 0 && total_r <= 64) {
+    // few undecided pages: one wave ranks them directly by (key desc, page asc)
+    if (tid < total_r) {
+      const uint64_t key = kL[tid];
+      int rank = 0;
+      for (int j = 0; j < total_r; ++j) {
+        const uint64_t kj = kL[j];
+        rank += kj > key || (kj == key && j < tid);
+      }
+      if (rank < need) flag[rlist[tid]] = 1;
+    }
+  } else if (need > 0) {
     const uint64_t P = kth_key<NT>(kL, total_r, need, sc);
     // pages strictly above P, then the first `need - above` at P in page order
     int above = 0, at = 0;
