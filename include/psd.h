@@ -167,12 +167,15 @@ psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* m
  *
  * psd_select_score scores the pages. It writes sel_count and every sel_pages entry except
  * the ranked winners: the sink, the tail and the -1 padding, and the whole row of a unit
- * that keeps every page or exceeds b_max. It leaves candidates in the workspace: either
- * each chunk's top pages by exact score or, for groups of 16 or more bf16 heads,
- * approximate scores with a proven error bound. psd_select_merge reads them back and
- * writes the b-2 winners of every ranking unit into sel_pages[..., 1 .. b-2] in ascending
- * order. For the approximate case it first rescores exactly the pages that the bound
- * cannot decide, which is why it takes q, meta and block_table. The workspace must not be
+ * that keeps every page or exceeds b_max. When one workgroup scores a whole unit (batches
+ * of at least 128 units of at most 2050 pages, groups of up to 8 heads) it also writes
+ * the winners, and psd_select_merge then launches nothing. Otherwise it leaves
+ * candidates in the workspace: either each chunk's top pages by exact score or, for
+ * groups of 16 or more bf16 heads, approximate scores with a proven error bound.
+ * psd_select_merge reads them back and writes the b-2 winners of every ranking unit into
+ * sel_pages[..., 1 .. b-2] in ascending order. For the approximate case it first rescores
+ * exactly the pages that the bound cannot decide, which is why it takes q, meta and
+ * block_table. The workspace must not be
  * touched between the two calls. Arguments, errors and sources are as for
  * psd_select_pages.
  */
@@ -196,8 +199,11 @@ size_t psd_decode_workspace_bytes(const psd_shape* shape, int32_t max_pages_atte
  * psd_sparse_decode - softmax attention over the kept pages only.
  *
  * out[s, h, :] = sum_t softmax_t(scale * q[s,h] . K_t) V_t[:D_v] over the valid tokens t
- * of the pages sel_pages[s, h / G, 0 .. sel_count - 1]. Accumulation is fp32 with
- * split-K partials merged by log-sum-exp. Units whose sel_count is negative get NaN.
+ * of the pages sel_pages[s, h / G, 0 .. sel_count - 1]. Accumulation is fp32; the page
+ * splits of a unit are combined by log-sum-exp, inside the workgroup when one workgroup
+ * holds a whole unit (batches of at least 128 units, groups of up to 16 heads, D <= 128),
+ * else by a second launch over partials in the workspace. Units whose sel_count is
+ * negative get NaN.
  *
  *   q, k_cache, v_cache, block_table, seq_lens as above (device, read)
  *   sel_pages, sel_count, b_max   as written by psd_select_pages (device, read)
