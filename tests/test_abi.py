@@ -111,3 +111,30 @@ def test_null_and_workspace_errors(native):
     assert lib.psd_dense_decode(ctypes.byref(sh), f, f, f, f, f, 0.1, f, f, 4, None) == -3
     assert lib.psd_sparse_decode(ctypes.byref(sh), f, f, f, f, f, None, f, 10, 0.1, f, f,
                                  1 << 30, None) == -1
+
+
+def test_plans_follow_the_batch_shape(native):
+    """Host planning, through the workspace queries: whole-unit scoring needs no candidate
+    area; small batches keep chunk candidates and split partials; many-head bf16 groups
+    keep the certified planes."""
+    lib = native.lib()
+    q = lambda sh, b: (lib.psd_select_workspace_bytes(ctypes.byref(sh), b),
+                       lib.psd_decode_workspace_bytes(ctypes.byref(sh), b))
+    ragged = _shape(native, batch=32, max_pages_per_seq=2048, num_blocks=65536)
+    sel, dec = q(ragged, 102)
+    assert 0 < sel <= 256 * 4 + 512  # 256 units: one scoring workgroup each, no candidates
+    assert dec > 0  # sized for the dense walk too (split partials)
+    one = _shape(native, batch=1, max_pages_per_seq=2048, num_blocks=2048)
+    sel, dec = q(one, 102)
+    assert sel >= 8 * 2046 * 12  # every page of the 8 units is a candidate
+    assert dec >= 32 * 2 * 128 * 4  # at least two splits of fp32 partials per head
+    mla = _shape(native, batch=16, num_q_heads=128, num_kv_heads=1, head_dim=576,
+                 head_dim_v=512, max_pages_per_seq=4096, num_blocks=65536,
+                 k_block_stride=16 * 576, k_token_stride=576, k_head_stride=576,
+                 v_block_stride=16 * 576, v_token_stride=576, v_head_stride=576)
+    sel, dec = q(mla, 205)
+    assert sel >= 4 * 16 * 4094 * 4  # approximate score, maxima, runner-up, leading tile
+    assert dec > 0
+    # a wider budget never needs a smaller workspace
+    for sh in (one, mla):
+        assert q(sh, 400)[0] >= q(sh, 100)[0]
