@@ -1,7 +1,8 @@
 """Benchmark: page-selected sparse decode attention steps/s on one MI355X.
 
-A step is one layer's decode for the whole batch through the three C-ABI calls:
-page_meta_update (tail page) -> select_pages -> sparse_decode. The default workload is the
+A step is one layer's decode for the whole batch through the C-ABI: page_meta_update
+(tail page) -> select_sparse_decode (select_pages and sparse_decode in one call, a single
+launch when one workgroup ranks and attends each unit). The default workload is the
 ragged batch: B=32 sequences of 16K..32K tokens, 32 query / 8 KV heads, D=128, bf16,
 5% page budget (sink and tail included). Inputs are resident in HBM before timing; steps
 rotate over --rotate device copies of (cache, statistics, q) so that consecutive steps
@@ -11,6 +12,7 @@ Prints one JSON line. Besides the contract fields it carries:
   roofline      achieved algorithmic GB/s of the dominant kernel against 8 TB/s
   cpu_baseline  the fp64 oracle's step on the host, on a bounded sample of sequences
   calls         per-call average durations (HIP events on the launch stream)
+  separate      the same step with select_pages and sparse_decode as two calls
   dense         the dense baseline (psd_dense_decode) on the same inputs
   graph_replay  the same step replayed from a captured HIP graph (launch cost removed),
                 with a bit-for-bit check against the eager outputs
@@ -64,10 +66,33 @@ def algorithmic_bytes(w, sel_counts: np.ndarray) -> dict:
                 dense_decode=dense_b, score_stats=int(np.sum(scored) * Hkv * 2 * D * es))
 
 
-KERNEL_SOURCES = {"score_kernel": "select.hip", "merge_kernel": "select.hip",
-                  "prescore_kernel": "prescore.hip", "certify_kernel": "prescore.hip",
-                  "meta_kernel": "meta.hip", "attn_kernel": "attn.hip",
-                  "attn_latent_kernel": "attn.hip", "lse_merge_kernel": "attn.hip"}
+KERNEL_SOURCES = {"score_kernel": ("select.hip",), "merge_kernel": ("select.hip",),
+                  "select_attn_kernel": ("select.hip", "attn_core.h"),
+                  "prescore_kernel": ("prescore.hip",), "certify_kernel": ("prescore.hip",),
+                  "meta_kernel": ("meta.hip",), "attn_kernel": ("attn.hip", "attn_core.h"),
+                  "attn_latent_kernel": ("attn.hip", "attn_core.h"),
+                  "lse_merge_kernel": ("attn.hip", "attn_core.h")}
+
+
+def one_call_kernel(w):
+    """The kernel behind select_sparse_decode when it is a single launch, else None.
+    Follows the library's planning rule: at least 128 (sequence, KV head) units, at most
+    2048 candidate pages per unit, groups of up to 8 query heads, D = D_v <= 128, and no
+    certified pre-score."""
+    sp = w.spec
+    G = sp.num_q_heads // sp.num_kv_heads
+    units = sp.batch * sp.num_kv_heads
+    if (G <= 8 and sp.head_dim <= 128 and sp.head_dim_v == sp.head_dim and units >= 128 and
+            w.block_table.shape[1] - 2 <= 2048):
+        return "select_attn_kernel"
+    return None
+
+
+def call_bytes(ab: dict, call: str) -> int:
+    """Algorithmic bytes of one C-ABI call."""
+    if call == "select_sparse_decode":
+        return ab["select"] + ab["sparse_decode"]
+    return ab[{"page_meta_update": "meta_update"}.get(call, call)]
 
 
 def selection_kernels(w) -> tuple:
@@ -85,12 +110,12 @@ def selection_kernels(w) -> tuple:
 
 
 def source_digest(kernel: str) -> str:
-    """sha256 of the HIP source a kernel is built from (with the shared device header)."""
+    """sha256 of the HIP sources a kernel is built from (with the shared device header)."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "page_selected_sparse_amd", "csrc")
-    for f in (KERNEL_SOURCES[kernel], "psd_device.h"):
+    for f in (*KERNEL_SOURCES[kernel], "psd_device.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -246,13 +271,17 @@ def main():
         del g
 
     # Per-call averages, each call timed in its own loop with events on the stream the
-    # kernels are launched on (torch's current stream). Every call below but sparse_decode
-    # is a single kernel (select_merge launches none when each scoring workgroup ranked a
-    # whole unit); sparse_decode is the attention kernel plus the split merge.
+    # kernels are launched on (torch's current stream). page_meta_update, select_score and
+    # select_merge are single kernels (select_merge launches none when each scoring
+    # workgroup ranked a whole unit); sparse_decode is the attention kernel, plus the split
+    # merge unless one workgroup attends each unit; select_sparse_decode is one kernel where
+    # one_call_kernel() names it, else the launches of the two calls.
     calls = {"page_meta_update": timed(lambda st: st.refresh_tail(), args.steps),
+             "select_sparse_decode": timed(lambda st: st.select_sparse(), args.steps),
              "select_score": timed(lambda st: st.select_score(), args.steps),
              "select_merge": timed(lambda st: st.select_merge(), args.steps),
              "sparse_decode": timed(lambda st: st.sparse(), args.steps)}
+    ms_separate = timed(lambda st: st.step_separate(), args.steps)
     dense_ms = timed(lambda st: st.dense(), max(10, args.steps // 4)) if not args.no_dense else None
 
     if args.calibrate_copy:
@@ -269,6 +298,10 @@ def main():
     kernel_of = {"select_score": (score_k, ab["select_score"]),
                  "select_merge": (merge_k, ab["select_merge"]),
                  "page_meta_update": ("meta_kernel", ab["meta_update"])}
+    fused_k = one_call_kernel(w)
+    if fused_k:
+        kernel_of = {"select_sparse_decode": (fused_k, ab["select"] + ab["sparse_decode"]),
+                     "page_meta_update": ("meta_kernel", ab["meta_update"])}
     dom = max(kernel_of, key=lambda k: calls[k])
     kname, dom_bytes = kernel_of[dom]
     achieved = dom_bytes / (calls[dom] * 1e-3) / 1e9
@@ -305,8 +338,10 @@ def main():
                      "traffic": traffic},
         "calls_ms": {k: round(v, 5) for k, v in calls.items()},
         # algorithmic GB/s of every call (sparse_decode: attention plus the split merge)
-        "calls_gbs": {k: round(ab[{"page_meta_update": "meta_update"}.get(k, k)] /
-                               (v * 1e-3) / 1e9, 1) for k, v in calls.items()},
+        "calls_gbs": {k: round(call_bytes(ab, k) / (v * 1e-3) / 1e9, 1)
+                      for k, v in calls.items()},
+        "separate": {"ms_per_step": round(ms_separate, 5),
+                     "steps_per_s": round(1000.0 / ms_separate, 3)},
         "algorithmic_bytes": ab,
     }
     if graph is not None:

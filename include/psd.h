@@ -221,6 +221,39 @@ psd_status psd_sparse_decode(const psd_shape* shape, const void* q, const void* 
                              const int32_t* sel_count, int32_t b_max, float scale, float* out,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes psd_select_sparse_decode needs for this shape and b_max. 0 if
+ * unsupported. */
+size_t psd_select_sparse_decode_workspace_bytes(const psd_shape* shape, int32_t b_max);
+
+/*
+ * psd_select_sparse_decode - psd_select_pages followed by psd_sparse_decode, as one call.
+ *
+ * Writes exactly what psd_select_pages(shape, q, meta, block_table, seq_lens, budgets,
+ * b_max, sel_pages, sel_count, ...) and then psd_sparse_decode(shape, q, k_cache, v_cache,
+ * block_table, seq_lens, sel_pages, sel_count, b_max, scale, out, ...) write, bit for bit.
+ * When one workgroup can both rank and attend a whole unit (batches of at least 128
+ * units of at most 2050 pages, groups of up to 8 heads, D <= 128) it is a single launch:
+ * each workgroup scores and ranks its unit's pages, keeps the page list on chip and
+ * attends over it, so that no unit waits for the slowest ranking of the batch before its
+ * attention starts. Otherwise the call enqueues the two calls' launches in turn, sharing
+ * the workspace. sel_pages and sel_count are still written in full.
+ *
+ *   arguments   as for psd_select_pages and psd_sparse_decode
+ *   workspace   >= psd_select_sparse_decode_workspace_bytes(shape, b_max) bytes (scratch)
+ *
+ * Errors as for the two calls (PSD_ERR_CAPACITY when b_max is beyond what the selection
+ * holds). Source: EntmaxKV README, "Two selection strategies" and package tree (select,
+ * then decode over the selection); LOCKS README, "How it works" (scores, static top-b,
+ * then a paged attention kernel over the selected pages, within one decode step).
+ */
+psd_status psd_select_sparse_decode(const psd_shape* shape, const void* q, const void* meta,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* budgets, int32_t b_max, float scale,
+                                    int32_t* sel_pages, int32_t* sel_count, float* out,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
 /*
  * psd_dense_decode - the same attention over every page of each sequence (baseline).
  *

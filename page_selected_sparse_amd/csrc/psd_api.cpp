@@ -209,6 +209,53 @@ psd_status psd_dense_decode(const psd_shape* shape, const void* q, const void* k
                        stream);
 }
 
+size_t psd_select_sparse_decode_workspace_bytes(const psd_shape* shape, int32_t b_max) {
+  const size_t sel = psd_select_workspace_bytes(shape, b_max);
+  psd::Geo g;
+  psd::DecodePlan p;
+  if (sel == 0 || check_shape(shape, &g) != PSD_OK || !psd::plan_decode(g, b_max, false, &p))
+    return 0;
+  // the selection's workspace is dead once its merge stage has run: the attention reuses it
+  return sel > p.bytes ? sel : p.bytes;
+}
+
+psd_status psd_select_sparse_decode(const psd_shape* shape, const void* q, const void* meta,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* budgets, int32_t b_max, float scale,
+                                    int32_t* sel_pages, int32_t* sel_count, float* out,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  psd::Geo g;
+  psd::SelectPlan sp;
+  psd_status st = select_common(shape, seq_lens, budgets, b_max, sel_pages, workspace,
+                                workspace_bytes, &g, &sp);
+  if (st != PSD_OK) return st;
+  if (!q || !meta || !block_table || !sel_count || !k_cache || !v_cache || !out)
+    return PSD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(meta) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(out))
+    return PSD_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == __builtin_inff()) return PSD_ERR_INVALID_ARG;
+  if ((st = check_strides(g, true)) != PSD_OK) return st;
+  psd::DecodePlan dp;
+  if (!psd::plan_decode(g, b_max, false, &dp)) return PSD_ERR_INVALID_ARG;
+  if (workspace_bytes < dp.bytes) return PSD_ERR_WORKSPACE;
+  if (psd::fused_applies(g, sp, dp, b_max))
+    return launched(psd::launch_select_decode(g, sp, dp, q, meta, k_cache, v_cache, block_table,
+                                              seq_lens, budgets, b_max, scale, sel_pages,
+                                              sel_count, out, workspace, stream));
+  hipError_t e = psd::launch_select_score(g, sp, q, meta, block_table, seq_lens, budgets, b_max,
+                                          sel_pages, sel_count, workspace, stream);
+  if (e == hipSuccess)
+    e = psd::launch_select_merge(g, sp, q, meta, block_table, seq_lens, budgets, b_max,
+                                 sel_pages, workspace, stream);
+  if (e == hipSuccess)
+    e = psd::launch_decode(g, dp, q, k_cache, v_cache, block_table, seq_lens, sel_pages,
+                           sel_count, b_max, scale, out, workspace, stream);
+  return launched(e);
+}
+
 const char* psd_status_string(psd_status s) {
   switch (s) {
     case PSD_OK: return "ok";

@@ -79,4 +79,15 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& plan, const void* q, co
                          const int32_t* sel, const int32_t* cnt, int b_max, float scale,
                          float* out, void* ws, hipStream_t st);
 
+// ---- selection and attention in one launch -------------------------------------------------
+// Applies when both plans take one workgroup per unit (DPP scoring of groups of up to 8
+// heads, whole-unit attention): each workgroup scores, ranks and attends its unit, the page
+// list passing through LDS. Writes the selection rows and counts as the separate calls do.
+bool fused_applies(const Geo& g, const SelectPlan& sp, const DecodePlan& dp, int b_max);
+hipError_t launch_select_decode(const Geo& g, const SelectPlan& sp, const DecodePlan& dp,
+                                const void* q, const void* meta, const void* k, const void* v,
+                                const int32_t* bt, const int32_t* lens, const int32_t* budgets,
+                                int b_max, float scale, int32_t* sel, int32_t* cnt, float* out,
+                                void* ws, hipStream_t st);
+
 }  // namespace psd

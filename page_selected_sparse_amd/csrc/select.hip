@@ -28,6 +28,7 @@
 // The global top-(b-2) is contained in the union of the chunk top-(b-2) lists, since a
 // page outranked by fewer than b-2 pages overall is outranked by fewer than b-2 pages of
 // its own chunk. Sink, tail, padding and counts are written by the scoring kernel.
+#include "attn_core.h"
 #include "psd_device.h"
 #include "psd_launch.h"
 
@@ -291,6 +292,25 @@ __device__ void write_row_header(const SelArgs& a, int unit, const UnitInfo& u) 
     row[0] = 0;
     row[u.b - 1] = u.n - 1;
   }
+}
+
+// The same entries as write_row_header, into a unit's page list in LDS. Returns the
+// list's entry count: b for units that rank, n for units that keep every page, -1 for
+// units over capacity (no entries). The list may overlap the statistics staging area:
+// call it only after a barrier that follows every wave's wait for its loads.
+template <int NT>
+__device__ int write_list_header(int32_t* list, const UnitInfo& u, int b_max) {
+  const int tid = threadIdx.x;
+  if (u.b > b_max) return -1;
+  if (u.n <= u.b) {
+    for (int i = tid; i < u.n; i += NT) list[i] = i;
+    return u.n;
+  }
+  if (tid == 0) {
+    list[0] = 0;
+    list[u.b - 1] = u.n - 1;
+  }
+  return u.b;
 }
 
 // Element j of a chunk held as 16-byte vectors, widened exactly to fp64.
@@ -565,8 +585,11 @@ __device__ void merge_unit(const SelArgs& a, int unit, int n, int kp, unsigned c
 // deep per wave. Otherwise the table is staged 16 heads x DC dims at a time and read as
 // LDS broadcasts. When a unit has a single chunk, its top-kp is final and goes straight
 // into the selection row; otherwise the chunk's candidates go to the workspace.
+//
+// With `list` (whole-unit plans only, chunk 0) the ranked winners also go to list[1..b-2]
+// in LDS; write_list_header completes the list once the workgroup has passed a barrier.
 template <bool BF16, int D, int HB, bool DPP, int NT, int CPL, int S>
-__global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
+__device__ __forceinline__ void score_body(const SelArgs& a, int c, int g, int s, int32_t* list) {
   constexpr int DC = DPP ? D : ((HB * D * 16 <= 32768) ? D : 32);
   constexpr int NDC = D / DC;
   constexpr int NCH = D / MetaGeo<BF16>::CD;
@@ -580,7 +603,6 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   extern __shared__ unsigned char lds[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(lds);  // [chunk]
 
-  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
   const int unit = s * a.Hkv + g;
   const int lo = 1 + c * a.chunk;
@@ -695,7 +717,10 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
     uint64_t P, M;
     int need;
     block_kth_largest<NT>(keys, cnt, kp, sc, P, M, need);
-    block_emit_top<NT>(keys, cnt, P, M, need, sc, [&](int pos, int i) { row[1 + pos] = 1 + i; });
+    block_emit_top<NT>(keys, cnt, P, M, need, sc, [&](int pos, int i) {
+      row[1 + pos] = 1 + i;
+      if (list) list[1 + pos] = 1 + i;
+    });
     return;
   }
   // Chunk candidates: all pages when they fit in kp, else the chunk's top-kp.
@@ -717,6 +742,11 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
     });
     if (tid == 0) a.ccnt[(int64_t)unit * a.nchunk + c] = emitted;
   }
+}
+
+template <bool BF16, int D, int HB, bool DPP, int NT, int CPL, int S>
+__global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
+  score_body<BF16, D, HB, DPP, NT, CPL, S>(a, blockIdx.x, blockIdx.y, blockIdx.z, nullptr);
 }
 
 template <int NT>
@@ -805,6 +835,47 @@ hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStre
       default: return launch_score<BF16, D, 16, false, kThreads, 1, 1>(a, p, grid, st);
     }
   }
+}
+
+// One workgroup per (sequence, KV head) unit does the whole sparse decode of the unit:
+// it scores and ranks the unit's pages as score_kernel does for a whole-unit plan (and
+// writes the selection row and count the same way), keeps the page list in LDS at
+// `list_off`, and then attends over it as the whole-unit attention kernel does, its 16
+// waves being the splits. The list lies past both the ranking keys and the attention's
+// closing combine area, inside the statistics staging area: its winners are written by
+// the emission, which follows the last staged load, and its sink, tail or identity
+// entries after the barrier that follows the scoring.
+template <bool BF16, int D, int HB>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
+void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off) {
+  static_assert(PSD_ATTN_UNIT_WAVES == 16, "one attention split per wave of the workgroup");
+  extern __shared__ unsigned char lds[];
+  int32_t* list = reinterpret_cast<int32_t*>(lds + list_off);
+  const int g = blockIdx.x, s = blockIdx.y;
+  score_body<BF16, D, HB, true, 1024, 1, 1>(a, 0, g, s, list);
+  __syncthreads();  // every staged load has landed; the ranking keys are no longer read
+  const int count = write_list_header<1024>(list, unit_info(a, s), a.b_max);
+  __syncthreads();
+  attn_body<BF16, D, D, 1, 16>(aa, 0, g, s, list, count);
+}
+
+template <bool BF16, int D>
+hipError_t launch_fused(const SelArgs& a, const AttnArgs& aa, int head_block, dim3 grid,
+                        size_t lds, int list_off, hipStream_t st) {
+  auto kern = head_block == 4 ? &select_attn_kernel<BF16, D, 4> : &select_attn_kernel<BF16, D, 8>;
+  hipError_t e = set_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(1024), lds, st, a, aa, list_off);
+  return hipGetLastError();
+}
+
+// Byte offset of the page list and dynamic LDS of the fused launch.
+void fused_layout(const Geo& g, const SelectPlan& sp, int b_max, size_t* list_off, size_t* lds) {
+  const size_t keys = (size_t)sp.threads * sp.ppt * sizeof(uint64_t);
+  const size_t combine = unit_combine_lds(g);
+  *list_off = ((keys > combine ? keys : combine) + 255) / 256 * 256;
+  const size_t end = *list_off + (size_t)b_max * sizeof(int32_t);
+  *lds = end > sp.score_lds ? end : sp.score_lds;
 }
 
 }  // namespace
@@ -991,6 +1062,36 @@ hipError_t launch_select_merge(const Geo& g, const SelectPlan& p, const void* q,
     hipLaunchKernelGGL(merge_kernel<kThreads>, ugrid, dim3(kThreads), p.merge_lds, st, a);
   }
   return hipGetLastError();
+}
+
+bool fused_applies(const Geo& g, const SelectPlan& sp, const DecodePlan& dp, int b_max) {
+  if (sp.prescore || sp.nchunk != 1 || sp.threads != 1024 || !sp.all_q) return false;
+  if (sp.head_block != 4 && sp.head_block != 8) return false;
+  if (sp.cpl != 1 || sp.stages != 1) return false;
+  if (dp.unit != 16 || g.D > 128 || g.Dv != g.D) return false;
+  size_t list_off, lds;
+  fused_layout(g, sp, b_max, &list_off, &lds);
+  const size_t static_lds = (size_t)g.D * sp.head_block * 2 * sizeof(float) + sizeof(double2) +
+                            sizeof(SelScratch);
+  return static_lds + lds <= 160 * 1024;
+}
+
+hipError_t launch_select_decode(const Geo& g, const SelectPlan& sp, const DecodePlan& dp,
+                                const void* q, const void* meta, const void* k, const void* v,
+                                const int32_t* bt, const int32_t* lens, const int32_t* budgets,
+                                int b_max, float scale, int32_t* sel, int32_t* cnt, float* out,
+                                void* ws, hipStream_t st) {
+  const SelArgs a = make_args(g, sp, q, meta, bt, lens, budgets, b_max, sel, cnt, ws);
+  const AttnArgs aa = make_attn_args(g, dp, q, k, v, bt, lens, sel, cnt, b_max, scale, out, ws);
+  size_t list_off, lds;
+  fused_layout(g, sp, b_max, &list_off, &lds);
+  const dim3 grid(g.Hkv, g.B);
+  const bool bf = g.dtype == 1;
+  if (g.D == 64)
+    return bf ? launch_fused<true, 64>(a, aa, sp.head_block, grid, lds, (int)list_off, st)
+              : launch_fused<false, 64>(a, aa, sp.head_block, grid, lds, (int)list_off, st);
+  return bf ? launch_fused<true, 128>(a, aa, sp.head_block, grid, lds, (int)list_off, st)
+            : launch_fused<false, 128>(a, aa, sp.head_block, grid, lds, (int)list_off, st);
 }
 
 }  // namespace psd

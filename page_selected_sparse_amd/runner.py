@@ -1,12 +1,13 @@
-"""Device buffers for one layer's decode step and the three-call step itself.
+"""Device buffers for one layer's decode step and the decode step itself.
 
-``DecodeStep`` owns (as torch tensors) the page statistics, the selection rows, the two
+``DecodeStep`` owns (as torch tensors) the page statistics, the selection rows, the
 workspaces and the output for a fixed batch geometry, and issues
 
-    page_meta_update (tail page) -> select_pages -> sparse_decode
+    page_meta_update (tail page) -> select_sparse_decode
 
-on one stream. ``dense()`` runs the dense baseline on the same inputs. Nothing here
-computes: it sizes buffers and forwards pointers to the C-ABI.
+on one stream; ``step_separate`` issues select_pages and sparse_decode as two calls
+instead. ``dense()`` runs the dense baseline on the same inputs. Nothing here computes:
+it sizes buffers and forwards pointers to the C-ABI.
 """
 from __future__ import annotations
 
@@ -56,6 +57,10 @@ class DecodeStep:
         self.ws_select = torch.empty(sel_ws, dtype=torch.uint8, device=dev)
         self.ws_decode = torch.empty(dec_ws, dtype=torch.uint8, device=dev)
         self.ws_dense = torch.empty(den_ws, dtype=torch.uint8, device=dev)
+        fused_ws = api.select_sparse_decode_workspace_bytes(self.shape, self.b_max)
+        if fused_ws == 0:
+            raise api.PsdError(-2, "workspace query")
+        self.ws_fused = torch.empty(fused_ws, dtype=torch.uint8, device=dev)
         self.first_page_zero = torch.zeros(B, dtype=torch.int32, device=dev)
 
     @classmethod
@@ -100,12 +105,24 @@ class DecodeStep:
                           self.sel_pages, self.sel_count, self.b_max, self.scale, self.out,
                           self.ws_decode, stream)
 
+    def select_sparse(self, stream=None):
+        """``select`` then ``sparse`` as one call (one launch where a workgroup holds a unit)."""
+        api.select_sparse_decode(self.shape, self.q, self.meta, self.k, self.v, self.block_table,
+                                 self.seq_lens, self.budgets, self.b_max, self.scale,
+                                 self.sel_pages, self.sel_count, self.out, self.ws_fused, stream)
+
     def dense(self, stream=None):
         api.dense_decode(self.shape, self.q, self.k, self.v, self.block_table, self.seq_lens,
                          self.scale, self.out_dense, self.ws_dense, stream)
 
     def step(self, stream=None):
-        """One sparse decode step: tail refresh, selection, attention over kept pages."""
+        """One sparse decode step: tail refresh, then selection and attention over the kept
+        pages in one call."""
+        self.refresh_tail(stream)
+        self.select_sparse(stream)
+
+    def step_separate(self, stream=None):
+        """The same step with selection and attention as separate calls."""
         self.refresh_tail(stream)
         self.select(stream)
         self.sparse(stream)

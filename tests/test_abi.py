@@ -113,6 +113,33 @@ def test_null_and_workspace_errors(native):
                                  1 << 30, None) == -1
 
 
+def test_one_call_step_checks(native):
+    """psd_select_sparse_decode: workspace covers both stages; the checks of the two calls
+    it stands for apply before anything launches."""
+    lib = native.lib()
+    sh = _shape(native)
+    f = ctypes.c_void_p(16)
+    ws = lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(sh), 10)
+    assert ws >= lib.psd_select_workspace_bytes(ctypes.byref(sh), 10)
+    assert ws >= lib.psd_decode_workspace_bytes(ctypes.byref(sh), 10)
+    assert lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(sh), 1) == 0
+    long = _shape(native, batch=1, max_pages_per_seq=65536, num_blocks=65536)
+    assert lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(long), 60000) == 0
+    call = lambda shp, q, k, b_max, scale, out, nbytes: lib.psd_select_sparse_decode(
+        shp, q, f, k, f, f, f, f, b_max, scale, f, f, out, f, nbytes, None)
+    big = 1 << 30
+    assert call(None, f, f, 10, 0.1, f, big) == -1
+    assert call(ctypes.byref(sh), None, f, 10, 0.1, f, big) == -1
+    assert call(ctypes.byref(sh), f, None, 10, 0.1, f, big) == -1
+    assert call(ctypes.byref(sh), f, f, 10, 0.1, None, big) == -1
+    assert call(ctypes.byref(sh), f, f, 1, 0.1, f, big) == -1
+    assert call(ctypes.byref(sh), f, f, 10, 0.0, f, big) == -1
+    assert call(ctypes.byref(sh), f, f, 10, 0.1, f, 8) == -3
+    assert call(ctypes.byref(long), f, f, 60000, 0.1, f, 1 << 40) == -4
+    assert call(ctypes.byref(_shape(native, head_dim=96, head_dim_v=96)), f, f, 10, 0.1, f,
+                big) == -2
+
+
 def test_plans_follow_the_batch_shape(native):
     """Host planning, through the workspace queries: whole-unit scoring needs no candidate
     area; small batches keep chunk candidates and split partials; many-head bf16 groups

@@ -209,6 +209,55 @@ def test_selection_stages_compose():
     assert torch.equal(step.sel_pages, sel) and torch.equal(step.sel_count, cnt)
 
 
+def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """Bit-equal, NaN included."""
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# Batches where one workgroup ranks and attends each unit (bf16 and fp32, 4- and 8-head
+# groups, D 64 and 128, a flagged unit), and batches where the one call falls back to the
+# separate launches.
+ONE_CALL = ["wide_batch", "wide_group8", "wide_f32_d64", "ragged_b32_32k", "ragged_default",
+            "group16", "latent576", "flagged_units"]
+
+
+@pytest.mark.parametrize("name", ONE_CALL)
+def test_one_call_step_matches_separate_calls(name):
+    """psd_select_sparse_decode writes what psd_select_pages then psd_sparse_decode write,
+    bit for bit: rows, counts and outputs."""
+    from page_selected_sparse_amd import DecodeStep
+
+    b_max = None
+    if name == "flagged_units":
+        spec = synth.small_spec(batch=64, seq_lens=(1000, 100) * 32, budget_pages=20,
+                                max_len=1008)
+        b_max = 10
+    elif name in SMALL:
+        spec = SMALL[name]
+    else:
+        spec = name
+    w = synth.make_workload(spec)
+    print(f"[gpu] one-call step {name}", flush=True)
+    step = DecodeStep.from_arrays(w.q, w.cache, w.block_table, w.seq_lens, w.budgets,
+                                  w.spec.dtype, w.spec.head_dim_v, w.spec.latent, b_max=b_max)
+    step.build_meta()
+    step.select()
+    step.sparse()
+    torch.cuda.synchronize()
+    sel, cnt, out = step.sel_pages.clone(), step.sel_count.clone(), step.out.clone()
+    for rep in range(2):  # the second call runs over the first call's results
+        if rep == 0:
+            step.sel_pages.fill_(-7)
+            step.sel_count.fill_(-7)
+            step.out.fill_(123.0)
+        step.select_sparse()
+        torch.cuda.synchronize()
+        assert _same(step.sel_pages, sel) and _same(step.sel_count, cnt)
+        assert _same(step.out, out)
+    del step
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["latent576", "group32", "mla_64k"])
 def test_prescore_error_bound_holds(name):
     """The approximate many-head scores lie within the proven error bound of the exact fp64
