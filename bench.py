@@ -1,8 +1,8 @@
 """Benchmark: page-selected sparse decode attention steps/s on one MI355X.
 
-A step is one layer's decode for the whole batch through the C-ABI: page_meta_update
-(tail page) -> select_sparse_decode (select_pages and sparse_decode in one call, a single
-launch when one workgroup ranks and attends each unit). The default workload is the
+A step is one layer's decode for the whole batch through one C-ABI call, decode_step:
+page_meta_update (tail page), select_pages and sparse_decode, as a single launch when one
+workgroup refreshes, ranks and attends each unit. The default workload is the
 ragged batch: B=32 sequences of 16K..32K tokens, 32 query / 8 KV heads, D=128, bf16,
 5% page budget (sink and tail included). Inputs are resident in HBM before timing; steps
 rotate over --rotate device copies of (cache, statistics, q) so that consecutive steps
@@ -12,7 +12,8 @@ Prints one JSON line. Besides the contract fields it carries:
   roofline      achieved algorithmic GB/s of the dominant kernel against 8 TB/s
   cpu_baseline  the fp64 oracle's step on the host, on a bounded sample of sequences
   calls         per-call average durations (HIP events on the launch stream)
-  separate      the same step with select_pages and sparse_decode as two calls
+  separate      the same step as three calls (page_meta_update, select_pages,
+                sparse_decode)
   dense         the dense baseline (psd_dense_decode) on the same inputs
   graph_replay  the same step replayed from a captured HIP graph (launch cost removed),
                 with a bit-for-bit check against the eager outputs
@@ -75,7 +76,8 @@ KERNEL_SOURCES = {"score_kernel": ("select.hip",), "merge_kernel": ("select.hip"
 
 
 def one_call_kernel(w):
-    """The kernel behind select_sparse_decode when it is a single launch, else None.
+    """The kernel behind decode_step and select_sparse_decode when each is a single launch,
+    else None.
     Follows the library's planning rule: at least 128 (sequence, KV head) units, at most
     2048 candidate pages per unit, groups of up to 8 query heads, D = D_v <= 128, and no
     certified pre-score."""
@@ -92,6 +94,8 @@ def call_bytes(ab: dict, call: str) -> int:
     """Algorithmic bytes of one C-ABI call."""
     if call == "select_sparse_decode":
         return ab["select"] + ab["sparse_decode"]
+    if call == "decode_step":
+        return ab["step"]
     return ab[{"page_meta_update": "meta_update"}.get(call, call)]
 
 
@@ -274,9 +278,10 @@ def main():
     # kernels are launched on (torch's current stream). page_meta_update, select_score and
     # select_merge are single kernels (select_merge launches none when each scoring
     # workgroup ranked a whole unit); sparse_decode is the attention kernel, plus the split
-    # merge unless one workgroup attends each unit; select_sparse_decode is one kernel where
-    # one_call_kernel() names it, else the launches of the two calls.
-    calls = {"page_meta_update": timed(lambda st: st.refresh_tail(), args.steps),
+    # merge unless one workgroup attends each unit; decode_step and select_sparse_decode are
+    # one kernel each where one_call_kernel() names it, else the launches of their calls.
+    calls = {"decode_step": timed(lambda st: st.step(), args.steps),
+             "page_meta_update": timed(lambda st: st.refresh_tail(), args.steps),
              "select_sparse_decode": timed(lambda st: st.select_sparse(), args.steps),
              "select_score": timed(lambda st: st.select_score(), args.steps),
              "select_merge": timed(lambda st: st.select_merge(), args.steps),
@@ -300,8 +305,7 @@ def main():
                  "page_meta_update": ("meta_kernel", ab["meta_update"])}
     fused_k = one_call_kernel(w)
     if fused_k:
-        kernel_of = {"select_sparse_decode": (fused_k, ab["select"] + ab["sparse_decode"]),
-                     "page_meta_update": ("meta_kernel", ab["meta_update"])}
+        kernel_of = {"decode_step": (fused_k, ab["step"])}
     dom = max(kernel_of, key=lambda k: calls[k])
     kname, dom_bytes = kernel_of[dom]
     achieved = dom_bytes / (calls[dom] * 1e-3) / 1e9

@@ -255,6 +255,29 @@ psd_status psd_select_sparse_decode(const psd_shape* shape, const void* q, const
                                     hipStream_t stream);
 
 /*
+ * psd_decode_step - one decode step: psd_page_meta_update with first_page == NULL (the
+ * tail page of every sequence, every KV head), then psd_select_sparse_decode.
+ *
+ * Writes exactly what those two calls write, bit for bit (statistics, rows, counts,
+ * outputs). Where psd_select_sparse_decode is a single launch, the tail refresh runs
+ * inside it: the tail page is never a ranking candidate, so its statistics are not read
+ * by the same step's scoring. This needs one more device precondition than the two calls:
+ * the block holding a sequence's tail page is not an earlier page of any sequence in the
+ * batch (true of a paged cache whose partly filled blocks each belong to one sequence).
+ *
+ *   meta        statistics [num_blocks, H_kv, D / CD, 2, CD] (device, read and written)
+ *   others      as for psd_select_sparse_decode, with the same workspace query
+ *
+ * Source: EntmaxKV README, package tree (per-page k_min / k_max refresh at append time,
+ * then selection and decode over the selected pages); LOCKS README, "How it works".
+ */
+psd_status psd_decode_step(const psd_shape* shape, const void* q, void* meta, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* seq_lens, const int32_t* budgets, int32_t b_max,
+                           float scale, int32_t* sel_pages, int32_t* sel_count, float* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * psd_dense_decode - the same attention over every page of each sequence (baseline).
  *
  * workspace >= psd_decode_workspace_bytes(shape, shape->max_pages_per_seq) bytes.

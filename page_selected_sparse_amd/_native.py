@@ -33,6 +33,9 @@ SIGNATURES = {
     "psd_select_sparse_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_i32, c_float, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_size, c_void_p]),
+    "psd_decode_step": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_i32, c_float, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_size, c_void_p]),
     "psd_dense_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_float, c_void_p, c_void_p, c_size, c_void_p]),
     "psd_status_string": (ctypes.c_char_p, [c_i32]),

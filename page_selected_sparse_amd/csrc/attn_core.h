@@ -145,10 +145,16 @@ __device__ __forceinline__ void load_frag8(const void* base, int64_t off, uint4&
 // The body of one workgroup: split `split` of unit (s, g), or, with NWS > 0, the whole
 // unit. When `list` is given it replaces the selection row and count in memory (a list
 // in LDS written by the same workgroup: ascending pages, list_count entries, negative for
-// a flagged unit).
-template <bool BF16, int DQK, int DV, int WAVES, int NWS>
+// a flagged unit). A whole-unit workgroup calls `before_combine()` in every thread once
+// its wave has attended all of its pages, before the waves are combined.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+template <bool BF16, int DQK, int DV, int WAVES, int NWS, typename Hook = NoHook>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g, int s,
-                                          const int32_t* list, int list_count) {
+                                          const int32_t* list, int list_count,
+                                          const Hook& before_combine = Hook()) {
   constexpr bool UNIT = NWS > 0;
   static_assert(!UNIT || (WAVES == 1 && DQK <= 128), "unit workgroups: one head tile");
   constexpr bool PIPE = PSD_ATTN_PIPE != 0 && BF16;
@@ -415,6 +421,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
   if constexpr (UNIT) {
     // Combine the waves: M = max m_w, out = sum acc_w 2^(m_w - M) / sum l_w 2^(m_w - M).
     // A wave without pages has m = -inf, l = 0 and acc = 0 and weighs nothing.
+    before_combine();
     extern __shared__ float ush[];  // acc [NWS][G][DV] | (m, l) [NWS][16]
     float2* lml = reinterpret_cast<float2*>(ush + NWS * a.G * DV);
 #pragma unroll

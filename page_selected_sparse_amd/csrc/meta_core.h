@@ -1,0 +1,74 @@
+// Page statistics of VEC consecutive dims (16 bytes) of one KV head of one page: the min
+// and max over the page's valid tokens, written to the page-major statistics layout
+// [num_blocks][H_kv][D / CD][2][CD] (CD = 64 bytes of dims). Shared by the statistics
+// kernel and the one-launch decode step.
+#pragma once
+
+#include "psd_device.h"
+
+namespace psd {
+namespace {
+
+// All 16 token rows are requested at once; rows past `valid` are not used. Min/max are
+// exact, so the values written are key values themselves.
+template <bool BF16>
+__device__ __forceinline__ void refresh_stats(const void* k, void* meta, int blk, int valid, int h,
+                                              int d, int Hkv, int D, int64_t kbs, int64_t kts,
+                                              int64_t khs) {
+  constexpr int VEC = BF16 ? 8 : 4;  // elements per 16 bytes
+  const int64_t base = (int64_t)blk * kbs + (int64_t)h * khs + d;
+  float v[kPage][VEC];
+#pragma unroll
+  for (int t = 0; t < kPage; ++t) {
+    const int tt = t < valid ? t : 0;
+    if constexpr (BF16) {
+      const uint4 w = load16(static_cast<const uint16_t*>(k) + base + (int64_t)tt * kts);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[t][2 * i] = bf_lo(ws[i]);
+        v[t][2 * i + 1] = bf_hi(ws[i]);
+      }
+    } else {
+      const float4 w =
+          *reinterpret_cast<const float4*>(static_cast<const float*>(k) + base + (int64_t)tt * kts);
+      v[t][0] = w.x; v[t][1] = w.y; v[t][2] = w.z; v[t][3] = w.w;
+    }
+  }
+  float mn[VEC], mx[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) mn[i] = mx[i] = v[0][i];
+#pragma unroll
+  for (int t = 1; t < kPage; ++t) {
+    if (t < valid) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        mn[i] = v[t][i] < mn[i] ? v[t][i] : mn[i];
+        mx[i] = v[t][i] > mx[i] ? v[t][i] : mx[i];
+      }
+    }
+  }
+  constexpr int CD = BF16 ? 32 : 16;
+  const int64_t mrow = (((int64_t)blk * Hkv + h) * (D / CD) + d / CD) * 2 * CD + d % CD;
+  if constexpr (BF16) {
+    uint16_t* m = static_cast<uint16_t*>(meta);
+    uint4 lo, hi;
+    lo.x = pack2(__float_as_uint(mn[0]) >> 16, __float_as_uint(mn[1]) >> 16);
+    lo.y = pack2(__float_as_uint(mn[2]) >> 16, __float_as_uint(mn[3]) >> 16);
+    lo.z = pack2(__float_as_uint(mn[4]) >> 16, __float_as_uint(mn[5]) >> 16);
+    lo.w = pack2(__float_as_uint(mn[6]) >> 16, __float_as_uint(mn[7]) >> 16);
+    hi.x = pack2(__float_as_uint(mx[0]) >> 16, __float_as_uint(mx[1]) >> 16);
+    hi.y = pack2(__float_as_uint(mx[2]) >> 16, __float_as_uint(mx[3]) >> 16);
+    hi.z = pack2(__float_as_uint(mx[4]) >> 16, __float_as_uint(mx[5]) >> 16);
+    hi.w = pack2(__float_as_uint(mx[6]) >> 16, __float_as_uint(mx[7]) >> 16);
+    *reinterpret_cast<uint4*>(m + mrow) = lo;
+    *reinterpret_cast<uint4*>(m + mrow + CD) = hi;
+  } else {
+    float* m = static_cast<float*>(meta);
+    *reinterpret_cast<float4*>(m + mrow) = make_float4(mn[0], mn[1], mn[2], mn[3]);
+    *reinterpret_cast<float4*>(m + mrow + CD) = make_float4(mx[0], mx[1], mx[2], mx[3]);
+  }
+}
+
+}  // namespace
+}  // namespace psd

@@ -209,6 +209,49 @@ psd_status psd_dense_decode(const psd_shape* shape, const void* q, const void* k
                        stream);
 }
 
+// select_pages then sparse_decode, as one launch when the plans allow; with `refresh`,
+// the tail-page statistics refresh of page_meta_update (no first_page) comes first.
+static psd_status step_common(const psd_shape* shape, const void* q, const void* meta,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              const int32_t* budgets, int32_t b_max, float scale,
+                              int32_t* sel_pages, int32_t* sel_count, float* out, void* workspace,
+                              size_t workspace_bytes, bool refresh, hipStream_t stream) {
+  psd::Geo g;
+  psd::SelectPlan sp;
+  psd_status st = select_common(shape, seq_lens, budgets, b_max, sel_pages, workspace,
+                                workspace_bytes, &g, &sp);
+  if (st != PSD_OK) return st;
+  if (!q || !meta || !block_table || !sel_count || !k_cache || !v_cache || !out)
+    return PSD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(meta) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(out))
+    return PSD_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == __builtin_inff()) return PSD_ERR_INVALID_ARG;
+  if ((st = check_strides(g, true)) != PSD_OK) return st;
+  psd::DecodePlan dp;
+  if (!psd::plan_decode(g, b_max, false, &dp)) return PSD_ERR_INVALID_ARG;
+  if (workspace_bytes < dp.bytes) return PSD_ERR_WORKSPACE;
+  void* meta_w = refresh ? const_cast<void*>(meta) : nullptr;
+  if (psd::fused_applies(g, sp, dp, b_max))
+    return launched(psd::launch_select_decode(g, sp, dp, q, meta, k_cache, v_cache, block_table,
+                                              seq_lens, budgets, b_max, scale, sel_pages,
+                                              sel_count, out, workspace, meta_w, stream));
+  hipError_t e = hipSuccess;
+  if (refresh)
+    e = psd::launch_meta_update(g, k_cache, meta_w, block_table, seq_lens, nullptr, stream);
+  if (e == hipSuccess)
+    e = psd::launch_select_score(g, sp, q, meta, block_table, seq_lens, budgets, b_max,
+                                 sel_pages, sel_count, workspace, stream);
+  if (e == hipSuccess)
+    e = psd::launch_select_merge(g, sp, q, meta, block_table, seq_lens, budgets, b_max,
+                                 sel_pages, workspace, stream);
+  if (e == hipSuccess)
+    e = psd::launch_decode(g, dp, q, k_cache, v_cache, block_table, seq_lens, sel_pages,
+                           sel_count, b_max, scale, out, workspace, stream);
+  return launched(e);
+}
+
 size_t psd_select_sparse_decode_workspace_bytes(const psd_shape* shape, int32_t b_max) {
   const size_t sel = psd_select_workspace_bytes(shape, b_max);
   psd::Geo g;
@@ -226,34 +269,17 @@ psd_status psd_select_sparse_decode(const psd_shape* shape, const void* q, const
                                     int32_t* sel_pages, int32_t* sel_count, float* out,
                                     void* workspace, size_t workspace_bytes,
                                     hipStream_t stream) {
-  psd::Geo g;
-  psd::SelectPlan sp;
-  psd_status st = select_common(shape, seq_lens, budgets, b_max, sel_pages, workspace,
-                                workspace_bytes, &g, &sp);
-  if (st != PSD_OK) return st;
-  if (!q || !meta || !block_table || !sel_count || !k_cache || !v_cache || !out)
-    return PSD_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(meta) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(out))
-    return PSD_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || scale == __builtin_inff()) return PSD_ERR_INVALID_ARG;
-  if ((st = check_strides(g, true)) != PSD_OK) return st;
-  psd::DecodePlan dp;
-  if (!psd::plan_decode(g, b_max, false, &dp)) return PSD_ERR_INVALID_ARG;
-  if (workspace_bytes < dp.bytes) return PSD_ERR_WORKSPACE;
-  if (psd::fused_applies(g, sp, dp, b_max))
-    return launched(psd::launch_select_decode(g, sp, dp, q, meta, k_cache, v_cache, block_table,
-                                              seq_lens, budgets, b_max, scale, sel_pages,
-                                              sel_count, out, workspace, stream));
-  hipError_t e = psd::launch_select_score(g, sp, q, meta, block_table, seq_lens, budgets, b_max,
-                                          sel_pages, sel_count, workspace, stream);
-  if (e == hipSuccess)
-    e = psd::launch_select_merge(g, sp, q, meta, block_table, seq_lens, budgets, b_max,
-                                 sel_pages, workspace, stream);
-  if (e == hipSuccess)
-    e = psd::launch_decode(g, dp, q, k_cache, v_cache, block_table, seq_lens, sel_pages,
-                           sel_count, b_max, scale, out, workspace, stream);
-  return launched(e);
+  return step_common(shape, q, meta, k_cache, v_cache, block_table, seq_lens, budgets, b_max,
+                     scale, sel_pages, sel_count, out, workspace, workspace_bytes, false, stream);
+}
+
+psd_status psd_decode_step(const psd_shape* shape, const void* q, void* meta, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* seq_lens, const int32_t* budgets, int32_t b_max,
+                           float scale, int32_t* sel_pages, int32_t* sel_count, float* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return step_common(shape, q, meta, k_cache, v_cache, block_table, seq_lens, budgets, b_max,
+                     scale, sel_pages, sel_count, out, workspace, workspace_bytes, true, stream);
 }
 
 const char* psd_status_string(psd_status s) {

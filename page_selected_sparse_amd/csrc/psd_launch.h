@@ -83,11 +83,13 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& plan, const void* q, co
 // Applies when both plans take one workgroup per unit (DPP scoring of groups of up to 8
 // heads, whole-unit attention): each workgroup scores, ranks and attends its unit, the page
 // list passing through LDS. Writes the selection rows and counts as the separate calls do.
+// With meta_tail (the statistics, writable) each workgroup also refreshes its sequence's
+// tail-page statistics for its KV head, as launch_meta_update with no first_page does.
 bool fused_applies(const Geo& g, const SelectPlan& sp, const DecodePlan& dp, int b_max);
 hipError_t launch_select_decode(const Geo& g, const SelectPlan& sp, const DecodePlan& dp,
                                 const void* q, const void* meta, const void* k, const void* v,
                                 const int32_t* bt, const int32_t* lens, const int32_t* budgets,
                                 int b_max, float scale, int32_t* sel, int32_t* cnt, float* out,
-                                void* ws, hipStream_t st);
+                                void* ws, void* meta_tail, hipStream_t st);
 
 }  // namespace psd

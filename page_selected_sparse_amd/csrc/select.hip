@@ -29,6 +29,7 @@
 // page outranked by fewer than b-2 pages overall is outranked by fewer than b-2 pages of
 // its own chunk. Sink, tail, padding and counts are written by the scoring kernel.
 #include "attn_core.h"
+#include "meta_core.h"
 #include "psd_device.h"
 #include "psd_launch.h"
 
@@ -845,9 +846,16 @@ hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStre
 // closing combine area, inside the statistics staging area: its winners are written by
 // the emission, which follows the last staged load, and its sink, tail or identity
 // entries after the barrier that follows the scoring.
-template <bool BF16, int D, int HB>
+//
+// With `meta_w` (decode step) the workgroup also refreshes the statistics of its
+// sequence's tail page for its KV head, as the statistics kernel does for the tail page.
+// The tail page is never a ranking candidate, so the refresh is independent of the
+// ranking; the last wave, which has the fewest pages to attend, does it before the waves
+// are combined.
+template <bool BF16, int D, int HB, bool REFRESH>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
-void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off) {
+void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, void* meta_w, int64_t kbs,
+                        int64_t kts, int64_t khs) {
   static_assert(PSD_ATTN_UNIT_WAVES == 16, "one attention split per wave of the workgroup");
   extern __shared__ unsigned char lds[];
   int32_t* list = reinterpret_cast<int32_t*>(lds + list_off);
@@ -856,17 +864,39 @@ void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off) {
   __syncthreads();  // every staged load has landed; the ranking keys are no longer read
   const int count = write_list_header<1024>(list, unit_info(a, s), a.b_max);
   __syncthreads();
-  attn_body<BF16, D, D, 1, 16>(aa, 0, g, s, list, count);
+  auto refresh_tail = [&]() {
+    if constexpr (REFRESH) {
+      if ((threadIdx.x >> 6) != 15) return;
+      const int L = a.lens[s];
+      const int p = ceil_div(L, kPage) - 1;
+      if (p < 0) return;
+      const int blk = a.bt[(int64_t)s * a.max_pages + p];
+      const int valid = min(kPage, L - p * kPage);
+      constexpr int VEC = BF16 ? 8 : 4;
+      for (int d = (threadIdx.x & 63) * VEC; d < D; d += 64 * VEC)
+        refresh_stats<BF16>(aa.k, meta_w, blk, valid, g, d, a.Hkv, D, kbs, kts, khs);
+    }
+  };
+  attn_body<BF16, D, D, 1, 16>(aa, 0, g, s, list, count, refresh_tail);
+}
+
+template <bool BF16, int D, bool REFRESH>
+hipError_t launch_fused(const SelArgs& a, const AttnArgs& aa, int head_block, dim3 grid,
+                        size_t lds, int list_off, void* meta_w, const Geo& g, hipStream_t st) {
+  auto kern = head_block == 4 ? &select_attn_kernel<BF16, D, 4, REFRESH>
+                              : &select_attn_kernel<BF16, D, 8, REFRESH>;
+  hipError_t e = set_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(1024), lds, st, a, aa, list_off, meta_w, g.kbs, g.kts,
+                     g.khs);
+  return hipGetLastError();
 }
 
 template <bool BF16, int D>
-hipError_t launch_fused(const SelArgs& a, const AttnArgs& aa, int head_block, dim3 grid,
-                        size_t lds, int list_off, hipStream_t st) {
-  auto kern = head_block == 4 ? &select_attn_kernel<BF16, D, 4> : &select_attn_kernel<BF16, D, 8>;
-  hipError_t e = set_lds(kern, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(1024), lds, st, a, aa, list_off);
-  return hipGetLastError();
+hipError_t launch_fused_r(const SelArgs& a, const AttnArgs& aa, int head_block, dim3 grid,
+                          size_t lds, int list_off, void* meta_w, const Geo& g, hipStream_t st) {
+  return meta_w ? launch_fused<BF16, D, true>(a, aa, head_block, grid, lds, list_off, meta_w, g, st)
+                : launch_fused<BF16, D, false>(a, aa, head_block, grid, lds, list_off, meta_w, g, st);
 }
 
 // Byte offset of the page list and dynamic LDS of the fused launch.
@@ -1080,18 +1110,19 @@ hipError_t launch_select_decode(const Geo& g, const SelectPlan& sp, const Decode
                                 const void* q, const void* meta, const void* k, const void* v,
                                 const int32_t* bt, const int32_t* lens, const int32_t* budgets,
                                 int b_max, float scale, int32_t* sel, int32_t* cnt, float* out,
-                                void* ws, hipStream_t st) {
+                                void* ws, void* meta_tail, hipStream_t st) {
   const SelArgs a = make_args(g, sp, q, meta, bt, lens, budgets, b_max, sel, cnt, ws);
   const AttnArgs aa = make_attn_args(g, dp, q, k, v, bt, lens, sel, cnt, b_max, scale, out, ws);
   size_t list_off, lds;
   fused_layout(g, sp, b_max, &list_off, &lds);
   const dim3 grid(g.Hkv, g.B);
   const bool bf = g.dtype == 1;
+  const int lo = (int)list_off;
   if (g.D == 64)
-    return bf ? launch_fused<true, 64>(a, aa, sp.head_block, grid, lds, (int)list_off, st)
-              : launch_fused<false, 64>(a, aa, sp.head_block, grid, lds, (int)list_off, st);
-  return bf ? launch_fused<true, 128>(a, aa, sp.head_block, grid, lds, (int)list_off, st)
-            : launch_fused<false, 128>(a, aa, sp.head_block, grid, lds, (int)list_off, st);
+    return bf ? launch_fused_r<true, 64>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st)
+              : launch_fused_r<false, 64>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st);
+  return bf ? launch_fused_r<true, 128>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st)
+            : launch_fused_r<false, 128>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st);
 }
 
 }  // namespace psd

@@ -3,10 +3,9 @@
 ``DecodeStep`` owns (as torch tensors) the page statistics, the selection rows, the
 workspaces and the output for a fixed batch geometry, and issues
 
-    page_meta_update (tail page) -> select_sparse_decode
+    decode_step = page_meta_update (tail page) + select_pages + sparse_decode
 
-on one stream; ``step_separate`` issues select_pages and sparse_decode as two calls
-instead. ``dense()`` runs the dense baseline on the same inputs. Nothing here computes:
+as one call on one stream; ``step_separate`` issues the three calls one by one. ``dense()`` runs the dense baseline on the same inputs. Nothing here computes:
 it sizes buffers and forwards pointers to the C-ABI.
 """
 from __future__ import annotations
@@ -116,13 +115,14 @@ class DecodeStep:
                          self.scale, self.out_dense, self.ws_dense, stream)
 
     def step(self, stream=None):
-        """One sparse decode step: tail refresh, then selection and attention over the kept
-        pages in one call."""
-        self.refresh_tail(stream)
-        self.select_sparse(stream)
+        """One sparse decode step in one call: tail refresh, selection, attention over the
+        kept pages."""
+        api.decode_step(self.shape, self.q, self.meta, self.k, self.v, self.block_table,
+                        self.seq_lens, self.budgets, self.b_max, self.scale, self.sel_pages,
+                        self.sel_count, self.out, self.ws_fused, stream)
 
     def step_separate(self, stream=None):
-        """The same step with selection and attention as separate calls."""
+        """The same step as three calls: tail refresh, selection, attention."""
         self.refresh_tail(stream)
         self.select(stream)
         self.sparse(stream)

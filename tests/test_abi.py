@@ -138,6 +138,12 @@ def test_one_call_step_checks(native):
     assert call(ctypes.byref(long), f, f, 60000, 0.1, f, 1 << 40) == -4
     assert call(ctypes.byref(_shape(native, head_dim=96, head_dim_v=96)), f, f, 10, 0.1, f,
                 big) == -2
+    step = lambda shp, meta, b_max, nbytes: lib.psd_decode_step(
+        shp, f, meta, f, f, f, f, f, b_max, 0.1, f, f, f, f, nbytes, None)
+    assert step(ctypes.byref(sh), None, 10, big) == -1
+    assert step(ctypes.byref(sh), ctypes.c_void_p(24), 10, big) == -1  # misaligned
+    assert step(ctypes.byref(sh), f, 10, 8) == -3
+    assert step(ctypes.byref(long), f, 60000, 1 << 40) == -4
 
 
 def test_plans_follow_the_batch_shape(native):

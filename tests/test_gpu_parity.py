@@ -258,6 +258,48 @@ def test_one_call_step_matches_separate_calls(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name", ONE_CALL)
+def test_decode_step_matches_three_calls(name):
+    """psd_decode_step writes what psd_page_meta_update (tail pages), psd_select_pages and
+    psd_sparse_decode write, bit for bit, statistics included. The tail pages' statistics
+    are zeroed first, so that only a refresh restores them."""
+    from page_selected_sparse_amd import DecodeStep
+
+    b_max = None
+    if name == "flagged_units":
+        spec = synth.small_spec(batch=64, seq_lens=(1000, 100) * 32, budget_pages=20,
+                                max_len=1008)
+        b_max = 10
+    elif name in SMALL:
+        spec = SMALL[name]
+    else:
+        spec = name
+    w = synth.make_workload(spec)
+    print(f"[gpu] decode step {name}", flush=True)
+    step = DecodeStep.from_arrays(w.q, w.cache, w.block_table, w.seq_lens, w.budgets,
+                                  w.spec.dtype, w.spec.head_dim_v, w.spec.latent, b_max=b_max)
+    step.build_meta()
+    n = (w.seq_lens.astype(np.int64) + 15) // 16
+    tails = torch.from_numpy(w.block_table[np.arange(w.spec.batch), n - 1].astype(np.int64))
+    step.meta[tails.to(step.meta.device)] = 0
+    stale = step.meta.clone()
+    step.step_separate()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (step.meta, step.sel_pages, step.sel_count, step.out)]
+    assert not _same(ref[0], stale)
+    step.meta.copy_(stale)
+    step.sel_pages.fill_(-7)
+    step.sel_count.fill_(-7)
+    step.out.fill_(123.0)
+    step.step()
+    torch.cuda.synchronize()
+    got = (step.meta, step.sel_pages, step.sel_count, step.out)
+    for what, a, b in zip(("statistics", "rows", "counts", "outputs"), got, ref):
+        assert _same(a, b), what
+    del step
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["latent576", "group32", "mla_64k"])
 def test_prescore_error_bound_holds(name):
     """The approximate many-head scores lie within the proven error bound of the exact fp64
