@@ -9,42 +9,52 @@
 namespace psd {
 namespace {
 
-// All 16 token rows are requested at once; rows past `valid` are not used. Min/max are
-// exact, so the values written are key values themselves.
-template <bool BF16>
+// Token rows are requested TB at a time (all 16 at once by default; TB = 8 halves the
+// registers); rows past `valid` are not used. Tokens are folded in ascending order. Min/max
+// are exact, so the values written are key values themselves.
+template <bool BF16, int TB = kPage>
 __device__ __forceinline__ void refresh_stats(const void* k, void* meta, int blk, int valid, int h,
                                               int d, int Hkv, int D, int64_t kbs, int64_t kts,
                                               int64_t khs) {
+  static_assert(kPage % TB == 0, "token batches");
   constexpr int VEC = BF16 ? 8 : 4;  // elements per 16 bytes
   const int64_t base = (int64_t)blk * kbs + (int64_t)h * khs + d;
-  float v[kPage][VEC];
-#pragma unroll
-  for (int t = 0; t < kPage; ++t) {
-    const int tt = t < valid ? t : 0;
-    if constexpr (BF16) {
-      const uint4 w = load16(static_cast<const uint16_t*>(k) + base + (int64_t)tt * kts);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[t][2 * i] = bf_lo(ws[i]);
-        v[t][2 * i + 1] = bf_hi(ws[i]);
-      }
-    } else {
-      const float4 w =
-          *reinterpret_cast<const float4*>(static_cast<const float*>(k) + base + (int64_t)tt * kts);
-      v[t][0] = w.x; v[t][1] = w.y; v[t][2] = w.z; v[t][3] = w.w;
-    }
-  }
   float mn[VEC], mx[VEC];
+#pragma unroll 1
+  for (int t0 = 0; t0 < kPage; t0 += TB) {
+    if (t0 > 0 && t0 >= valid) break;
+    float v[TB][VEC];
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) mn[i] = mx[i] = v[0][i];
+    for (int i = 0; i < TB; ++i) {
+      const int t = t0 + i;
+      const int tt = t < valid ? t : 0;
+      if constexpr (BF16) {
+        const uint4 w = load16(static_cast<const uint16_t*>(k) + base + (int64_t)tt * kts);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int t = 1; t < kPage; ++t) {
-    if (t < valid) {
+        for (int q = 0; q < 4; ++q) {
+          v[i][2 * q] = bf_lo(ws[q]);
+          v[i][2 * q + 1] = bf_hi(ws[q]);
+        }
+      } else {
+        const float4 w =
+            *reinterpret_cast<const float4*>(static_cast<const float*>(k) + base + (int64_t)tt * kts);
+        v[i][0] = w.x; v[i][1] = w.y; v[i][2] = w.z; v[i][3] = w.w;
+      }
+    }
+    if (t0 == 0) {
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        mn[i] = v[t][i] < mn[i] ? v[t][i] : mn[i];
-        mx[i] = v[t][i] > mx[i] ? v[t][i] : mx[i];
+      for (int j = 0; j < VEC; ++j) mn[j] = mx[j] = v[0][j];
+    }
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int t = t0 + i;
+      if (t > 0 && t < valid) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          mn[j] = v[i][j] < mn[j] ? v[i][j] : mn[j];
+          mx[j] = v[i][j] > mx[j] ? v[i][j] : mx[j];
+        }
       }
     }
   }

@@ -42,10 +42,16 @@ struct SelectPlan {
 bool plan_select(const Geo& g, int b_max, SelectPlan* plan);
 // Scoring stage: chunk candidates into the workspace and every row entry except the
 // ranked winners. Merge stage: the winners, from the workspace.
+// With meta_tail (exact path only, see score_takes_refresh) the scoring launch also
+// refreshes every sequence's tail-page statistics from k, as launch_meta_update with no
+// first_page does: one extra workgroup per unit, dispatched ahead of the unit's chunks.
+constexpr int kComputeUnits = 256;  // MI355X
+bool score_takes_refresh(const Geo& g, const SelectPlan& plan);
 hipError_t launch_select_score(const Geo& g, const SelectPlan& plan, const void* q,
                                const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, int32_t* cnt,
-                               void* ws, hipStream_t st);
+                               void* ws, hipStream_t st, void* meta_tail = nullptr,
+                               const void* k = nullptr);
 hipError_t launch_select_merge(const Geo& g, const SelectPlan& plan, const void* q,
                                const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, void* ws,

@@ -55,6 +55,12 @@ struct SelArgs {
   int32_t* cnt;
   int Hq, Hkv, G, D, max_pages, b_max, chunk, ppt, nchunk, cap, num_blocks;
   int ustride;  // candidate slots per unit: nchunk * cap rounded up to 1 KB of keys
+  // Tail refresh (decode step): with meta_w, workgroup x = 0 of each unit refreshes the
+  // tail page's statistics of its KV head from K (dispatched ahead of the unit's chunks,
+  // which then take x = 1 .. nchunk).
+  void* meta_w;
+  const void* k;
+  int64_t kbs, kts, khs;
 };
 
 struct SelScratch {
@@ -745,9 +751,32 @@ __device__ __forceinline__ void score_body(const SelArgs& a, int c, int g, int s
   }
 }
 
+// The tail page's statistics of unit (s, g), as the statistics kernel writes them. The
+// tail page is never a ranking candidate, so the scoring workgroups of the same launch do
+// not read them.
+template <bool BF16, int D, int NT>
+__device__ void refresh_tail(const SelArgs& a, int g, int s) {
+  const int L = a.lens[s];
+  const int p = ceil_div(L, kPage) - 1;
+  if (p < 0) return;
+  const int blk = a.bt[(int64_t)s * a.max_pages + p];
+  const int valid = min(kPage, L - p * kPage);
+  constexpr int VEC = BF16 ? 8 : 4;
+  for (int d = threadIdx.x * VEC; d < D; d += NT * VEC)
+    refresh_stats<BF16, 8>(a.k, a.meta_w, blk, valid, g, d, a.Hkv, D, a.kbs, a.kts, a.khs);
+}
+
 template <bool BF16, int D, int HB, bool DPP, int NT, int CPL, int S>
 __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
-  score_body<BF16, D, HB, DPP, NT, CPL, S>(a, blockIdx.x, blockIdx.y, blockIdx.z, nullptr);
+  int c = blockIdx.x;
+  if (a.meta_w) {
+    if (c == 0) {
+      refresh_tail<BF16, D, NT>(a, blockIdx.y, blockIdx.z);
+      return;
+    }
+    --c;
+  }
+  score_body<BF16, D, HB, DPP, NT, CPL, S>(a, c, blockIdx.y, blockIdx.z, nullptr);
 }
 
 template <int NT>
@@ -787,7 +816,7 @@ hipError_t set_lds(K kernel, size_t lds) {
 #define PSD_WAVE_CHUNK 64  // pages of a one-wave chunk workgroup
 #endif
 #ifndef PSD_MERGE_BIG
-#define PSD_MERGE_BIG 4096  // candidates above which a unit merge takes 1024 threads
+#define PSD_MERGE_BIG 1024  // candidates above which a unit merge takes 1024 threads
 #endif
 #ifndef PSD_WAVE_WG_MAX
 #define PSD_WAVE_WG_MAX 512  // one-wave chunk workgroups below this many 256-page chunks
@@ -1046,17 +1075,19 @@ static SelArgs make_args(const Geo& g, const SelectPlan& p, const void* q, const
                  reinterpret_cast<uint64_t*>(w), reinterpret_cast<int32_t*>(w + p.off_idx),
                  reinterpret_cast<int32_t*>(w + p.off_cnt), sel, cnt,
                  g.Hq, g.Hkv, g.G, g.D, g.max_pages, b_max, p.chunk, p.ppt, p.nchunk, p.cap,
-                 g.num_blocks, p.ustride};
+                 g.num_blocks, p.ustride, nullptr, nullptr, g.kbs, g.kts, g.khs};
 }
 
 hipError_t launch_select_score(const Geo& g, const SelectPlan& p, const void* q,
                                const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, int32_t* cnt,
-                               void* ws, hipStream_t st) {
+                               void* ws, hipStream_t st, void* meta_tail, const void* k) {
   if (p.prescore)
     return launch_prescore(g, p, q, meta, bt, lens, budgets, b_max, sel, cnt, ws, st);
-  const SelArgs a = make_args(g, p, q, meta, bt, lens, budgets, b_max, sel, cnt, ws);
-  const dim3 sgrid(p.nchunk, g.Hkv, g.B);
+  SelArgs a = make_args(g, p, q, meta, bt, lens, budgets, b_max, sel, cnt, ws);
+  a.meta_w = meta_tail;
+  a.k = k;
+  const dim3 sgrid(p.nchunk + (meta_tail ? 1 : 0), g.Hkv, g.B);
   const bool bf = g.dtype == 1;
   switch (g.D) {
     case 64: return bf ? dispatch_hb<true, 64>(a, p, sgrid, st)
@@ -1066,6 +1097,10 @@ hipError_t launch_select_score(const Geo& g, const SelectPlan& p, const void* q,
     default: return bf ? dispatch_hb<true, 576>(a, p, sgrid, st)
                        : dispatch_hb<false, 576>(a, p, sgrid, st);
   }
+}
+
+bool score_takes_refresh(const Geo& g, const SelectPlan& p) {
+  return !p.prescore && (int64_t)p.nchunk * g.Hkv * g.B <= kComputeUnits;
 }
 
 // The merge runs as its own launch: the kernel boundary makes every chunk's candidates

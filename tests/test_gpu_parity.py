@@ -218,7 +218,7 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
 # groups, D 64 and 128, a flagged unit), and batches where the one call falls back to the
 # separate launches.
 ONE_CALL = ["wide_batch", "wide_group8", "wide_f32_d64", "ragged_b32_32k", "ragged_default",
-            "group16", "latent576", "flagged_units"]
+            "group16", "latent576", "flagged_units", "chunked_wide_grid"]
 
 
 @pytest.mark.parametrize("name", ONE_CALL)
@@ -232,6 +232,10 @@ def test_one_call_step_matches_separate_calls(name):
         spec = synth.small_spec(batch=64, seq_lens=(1000, 100) * 32, budget_pages=20,
                                 max_len=1008)
         b_max = 10
+    elif name == "chunked_wide_grid":
+        spec = synth.small_spec(batch=8, num_q_heads=32, num_kv_heads=8, seq_lens=(),
+                                len_range=(16 * 2500, 16 * 3000), budget_pages=50,
+                                max_len=16 * 3000)
     elif name in SMALL:
         spec = SMALL[name]
     else:
@@ -270,6 +274,12 @@ def test_decode_step_matches_three_calls(name):
         spec = synth.small_spec(batch=64, seq_lens=(1000, 100) * 32, budget_pages=20,
                                 max_len=1008)
         b_max = 10
+    elif name == "chunked_wide_grid":
+        # 64 units scored in chunks over more workgroups than CUs: the tail refresh is
+        # its own launch rather than part of the scoring launch
+        spec = synth.small_spec(batch=8, num_q_heads=32, num_kv_heads=8, seq_lens=(),
+                                len_range=(16 * 2500, 16 * 3000), budget_pages=50,
+                                max_len=16 * 3000)
     elif name in SMALL:
         spec = SMALL[name]
     else:
