@@ -36,6 +36,10 @@
 namespace psd {
 namespace {
 
+#ifndef PSD_FUSED_XCD_MAP
+#define PSD_FUSED_XCD_MAP 1  // the KV heads of a sequence on one XCD
+#endif
+
 constexpr int kThreads = 256;
 constexpr int kMergeCap = 8192;  // candidates one merge workgroup holds in LDS
 constexpr int kMaxChunks = 1024;  // chunks per unit
@@ -888,7 +892,15 @@ void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, void* meta_w, int6
   static_assert(PSD_ATTN_UNIT_WAVES == 16, "one attention split per wave of the workgroup");
   extern __shared__ unsigned char lds[];
   int32_t* list = reinterpret_cast<int32_t*>(lds + list_off);
+#if PSD_FUSED_XCD_MAP
+  // workgroup i runs on XCD i % 8: give each XCD a contiguous range of units, so that
+  // the KV heads of a sequence share an XCD (and its L2)
+  const int U = gridDim.x * gridDim.y, i = blockIdx.x + blockIdx.y * gridDim.x;
+  const int u = (U % 8 == 0) ? (i % 8) * (U / 8) + i / 8 : i;
+  const int g = u % a.Hkv, s = u / a.Hkv;
+#else
   const int g = blockIdx.x, s = blockIdx.y;
+#endif
   score_body<BF16, D, HB, true, 1024, 1, 1>(a, 0, g, s, list);
   __syncthreads();  // every staged load has landed; the ranking keys are no longer read
   const int count = write_list_header<1024>(list, unit_info(a, s), a.b_max);
