@@ -259,11 +259,14 @@ psd_status psd_select_sparse_decode(const psd_shape* shape, const void* q, const
  * tail page of every sequence, every KV head), then psd_select_sparse_decode.
  *
  * Writes exactly what those two calls write, bit for bit (statistics, rows, counts,
- * outputs). Where psd_select_sparse_decode is a single launch, the tail refresh runs
- * inside it: the tail page is never a ranking candidate, so its statistics are not read
- * by the same step's scoring. This needs one more device precondition than the two calls:
- * the block holding a sequence's tail page is not an earlier page of any sequence in the
- * batch (true of a paged cache whose partly filled blocks each belong to one sequence).
+ * outputs). The tail refresh runs inside another launch where it can: inside the single
+ * launch of psd_select_sparse_decode, or as extra workgroups of the exact scoring launch
+ * when that launch has at most one workgroup per compute unit; otherwise it is a launch
+ * of its own, ahead of the selection. The tail page is never a ranking candidate, so its
+ * statistics are not read by the same step's scoring. Running the refresh concurrently
+ * with the scoring needs one more device precondition than the two calls: the block
+ * holding a sequence's tail page is not an earlier page of any sequence in the batch
+ * (true of a paged cache whose partly filled blocks each belong to one sequence).
  *
  *   meta        statistics [num_blocks, H_kv, D / CD, 2, CD] (device, read and written)
  *   others      as for psd_select_sparse_decode, with the same workspace query
