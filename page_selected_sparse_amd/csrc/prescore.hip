@@ -29,6 +29,7 @@
 // the best of them by (exact score desc, page asc). The result is the exact top-(b-2).
 #include <type_traits>
 
+#include "meta_core.h"
 #include "psd_device.h"
 #include "psd_launch.h"
 
@@ -49,6 +50,10 @@ struct PreArgs {
   int32_t* sel;
   int32_t* cnt;
   int Hq, Hkv, G, max_pages, b_max, num_blocks, max_inner, tiles_per_wg;
+  // tail refresh in the certify launch (decode step): workgroups z = 1, one per unit
+  void* meta_w = nullptr;
+  const void* k = nullptr;
+  int64_t kbs = 0, kts = 0, khs = 0;
 };
 
 struct UnitN {
@@ -734,6 +739,11 @@ __global__ __launch_bounds__(NT) void certify_kernel(PreArgs a) {
   extern __shared__ unsigned char lds[];
   const int tid = threadIdx.x;
   const int g = blockIdx.x, s = blockIdx.y;
+  if (blockIdx.z == 1) {  // the unit's tail-page statistics; no ranking reads them
+    refresh_tail_page<true>(a.k, a.meta_w, a.bt, a.lens, a.max_pages, s, g, a.Hkv, D, a.kbs,
+                            a.kts, a.khs, tid, NT);
+    return;
+  }
   const int unit = s * a.Hkv + g;
   const UnitN u = unit_n(a, s);
   if (u.trivial) return;
@@ -940,7 +950,8 @@ hipError_t launch_prescore(const Geo& g, const SelectPlan& p, const void* q, con
 
 hipError_t launch_certify(const Geo& g, const SelectPlan& p, const void* q, const void* meta,
                           const int32_t* bt, const int32_t* lens, const int32_t* budgets,
-                          int b_max, int32_t* sel, void* ws, hipStream_t st) {
+                          int b_max, int32_t* sel, void* ws, hipStream_t st, void* meta_tail,
+                          const void* k) {
   unsigned char* w = static_cast<unsigned char*>(ws);
   const int max_inner = g.max_pages > 2 ? g.max_pages - 2 : 1;
   PreArgs a{static_cast<const uint16_t*>(q), static_cast<const unsigned char*>(meta), bt, lens,
@@ -948,8 +959,13 @@ hipError_t launch_certify(const Geo& g, const SelectPlan& p, const void* q, cons
             reinterpret_cast<float*>(w + 2 * p.off_idx), reinterpret_cast<int32_t*>(w + 3 * p.off_idx),
             reinterpret_cast<double*>(w + p.off_cnt), sel, nullptr, g.Hq, g.Hkv, g.G,
             g.max_pages, b_max, g.num_blocks, max_inner, p.ppt};
+  a.meta_w = meta_tail;
+  a.k = k;
+  a.kbs = g.kbs;
+  a.kts = g.kts;
+  a.khs = g.khs;
   const size_t lds = prescore_lds(max_inner);
-  const dim3 grid(g.Hkv, g.B);
+  const dim3 grid(g.Hkv, g.B, meta_tail ? 2 : 1);
   hipError_t e;
 #define PSD_CERT(DD)                                                                        \
   if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&certify_kernel<DD, 512>),   \

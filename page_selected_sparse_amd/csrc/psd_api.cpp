@@ -238,20 +238,21 @@ static psd_status step_common(const psd_shape* shape, const void* q, const void*
                                               seq_lens, budgets, b_max, scale, sel_pages,
                                               sel_count, out, workspace, meta_w, stream));
   hipError_t e = hipSuccess;
-  // The exact scoring launch takes the tail refresh as one extra workgroup per unit when
-  // its grid is at most one workgroup per CU; a larger grid would give some CUs one more
-  // scoring workgroup than others. Otherwise, and on the certified path, the refresh is
-  // its own launch.
-  const bool in_score = refresh && psd::score_takes_refresh(g, sp);
-  if (refresh && !in_score)
+  // The tail refresh rides on the scoring or the merge launch as one extra workgroup per
+  // unit (refresh_site picks the launch), else it is a launch of its own.
+  const psd::RefreshSite site = psd::refresh_site(g, sp);
+  if (refresh && site == psd::kRefreshOwnLaunch)
     e = psd::launch_meta_update(g, k_cache, meta_w, block_table, seq_lens, nullptr, stream);
   if (e == hipSuccess)
     e = psd::launch_select_score(g, sp, q, meta, block_table, seq_lens, budgets, b_max,
                                  sel_pages, sel_count, workspace, stream,
-                                 in_score ? meta_w : nullptr, k_cache);
+                                 refresh && site == psd::kRefreshInScore ? meta_w : nullptr,
+                                 k_cache);
   if (e == hipSuccess)
     e = psd::launch_select_merge(g, sp, q, meta, block_table, seq_lens, budgets, b_max,
-                                 sel_pages, workspace, stream);
+                                 sel_pages, workspace, stream,
+                                 refresh && site == psd::kRefreshInMerge ? meta_w : nullptr,
+                                 k_cache);
   if (e == hipSuccess)
     e = psd::launch_decode(g, dp, q, k_cache, v_cache, block_table, seq_lens, sel_pages,
                            sel_count, b_max, scale, out, workspace, stream);

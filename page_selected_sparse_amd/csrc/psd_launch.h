@@ -42,11 +42,15 @@ struct SelectPlan {
 bool plan_select(const Geo& g, int b_max, SelectPlan* plan);
 // Scoring stage: chunk candidates into the workspace and every row entry except the
 // ranked winners. Merge stage: the winners, from the workspace.
-// With meta_tail (exact path only, see score_takes_refresh) the scoring launch also
-// refreshes every sequence's tail-page statistics from k, as launch_meta_update with no
-// first_page does: one extra workgroup per unit, dispatched ahead of the unit's chunks.
+// With meta_tail the scoring launch (exact path) or the merge launch also refreshes every
+// sequence's tail-page statistics from k, as launch_meta_update with no first_page does:
+// one extra workgroup per unit. refresh_site() says which launch takes it: the scoring
+// launch when its grid has at most one workgroup per CU (more would give some CUs an
+// extra scoring workgroup), else the merge launch (one workgroup per unit), else, when
+// whole-unit scoring leaves no merge launch, a launch of its own.
 constexpr int kComputeUnits = 256;  // MI355X
-bool score_takes_refresh(const Geo& g, const SelectPlan& plan);
+enum RefreshSite { kRefreshOwnLaunch, kRefreshInScore, kRefreshInMerge };
+RefreshSite refresh_site(const Geo& g, const SelectPlan& plan);
 hipError_t launch_select_score(const Geo& g, const SelectPlan& plan, const void* q,
                                const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, int32_t* cnt,
@@ -55,7 +59,8 @@ hipError_t launch_select_score(const Geo& g, const SelectPlan& plan, const void*
 hipError_t launch_select_merge(const Geo& g, const SelectPlan& plan, const void* q,
                                const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, void* ws,
-                               hipStream_t st);
+                               hipStream_t st, void* meta_tail = nullptr,
+                               const void* k = nullptr);
 
 // Certified many-head path (prescore.hip): the score stage is prescore_kernel (tiles of
 // `ppt` 16-page groups per workgroup, nchunk workgroups per unit), the merge stage is
@@ -68,7 +73,8 @@ hipError_t launch_prescore(const Geo& g, const SelectPlan& plan, const void* q, 
                            int b_max, int32_t* sel, int32_t* cnt, void* ws, hipStream_t st);
 hipError_t launch_certify(const Geo& g, const SelectPlan& plan, const void* q, const void* meta,
                           const int32_t* bt, const int32_t* lens, const int32_t* budgets,
-                          int b_max, int32_t* sel, void* ws, hipStream_t st);
+                          int b_max, int32_t* sel, void* ws, hipStream_t st,
+                          void* meta_tail = nullptr, const void* k = nullptr);
 
 // ---- attention -------------------------------------------------------------------------
 struct DecodePlan {

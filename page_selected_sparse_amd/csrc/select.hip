@@ -59,12 +59,13 @@ struct SelArgs {
   int32_t* cnt;
   int Hq, Hkv, G, D, max_pages, b_max, chunk, ppt, nchunk, cap, num_blocks;
   int ustride;  // candidate slots per unit: nchunk * cap rounded up to 1 KB of keys
-  // Tail refresh (decode step): with meta_w, workgroup x = 0 of each unit refreshes the
-  // tail page's statistics of its KV head from K (dispatched ahead of the unit's chunks,
-  // which then take x = 1 .. nchunk).
+  // Tail refresh (decode step): with meta_w, one extra workgroup per unit refreshes the
+  // tail page's statistics of its KV head from K: x = 0 of the scoring launch (ahead of
+  // the unit's chunks, which then take x = 1 .. nchunk), or z = 1 of the merge launch.
   void* meta_w;
   const void* k;
   int64_t kbs, kts, khs;
+  int bf16 = 0;
 };
 
 struct SelScratch {
@@ -756,18 +757,15 @@ __device__ __forceinline__ void score_body(const SelArgs& a, int c, int g, int s
 }
 
 // The tail page's statistics of unit (s, g), as the statistics kernel writes them. The
-// tail page is never a ranking candidate, so the scoring workgroups of the same launch do
-// not read them.
-template <bool BF16, int D, int NT>
+// tail page is never a ranking candidate, so no scoring or merging workgroup of the same
+// step reads them.
 __device__ void refresh_tail(const SelArgs& a, int g, int s) {
-  const int L = a.lens[s];
-  const int p = ceil_div(L, kPage) - 1;
-  if (p < 0) return;
-  const int blk = a.bt[(int64_t)s * a.max_pages + p];
-  const int valid = min(kPage, L - p * kPage);
-  constexpr int VEC = BF16 ? 8 : 4;
-  for (int d = threadIdx.x * VEC; d < D; d += NT * VEC)
-    refresh_stats<BF16, 8>(a.k, a.meta_w, blk, valid, g, d, a.Hkv, D, a.kbs, a.kts, a.khs);
+  if (a.bf16)
+    refresh_tail_page<true>(a.k, a.meta_w, a.bt, a.lens, a.max_pages, s, g, a.Hkv, a.D, a.kbs,
+                            a.kts, a.khs, threadIdx.x, blockDim.x);
+  else
+    refresh_tail_page<false>(a.k, a.meta_w, a.bt, a.lens, a.max_pages, s, g, a.Hkv, a.D, a.kbs,
+                             a.kts, a.khs, threadIdx.x, blockDim.x);
 }
 
 template <bool BF16, int D, int HB, bool DPP, int NT, int CPL, int S>
@@ -775,7 +773,7 @@ __global__ __launch_bounds__(NT) void score_kernel(SelArgs a) {
   int c = blockIdx.x;
   if (a.meta_w) {
     if (c == 0) {
-      refresh_tail<BF16, D, NT>(a, blockIdx.y, blockIdx.z);
+      refresh_tail(a, blockIdx.y, blockIdx.z);
       return;
     }
     --c;
@@ -788,6 +786,10 @@ __global__ __launch_bounds__(NT) void merge_kernel(SelArgs a) {
   __shared__ SelScratch sc;
   extern __shared__ unsigned char lds[];
   const int g = blockIdx.x, s = blockIdx.y;
+  if (blockIdx.z == 1) {  // the unit's tail refresh (decode step)
+    refresh_tail(a, g, s);
+    return;
+  }
   const UnitInfo u = unit_info(a, s);
   if (u.trivial) return;
   merge_unit<NT>(a, s * a.Hkv + g, u.n, u.kp, lds, sc);
@@ -1087,7 +1089,7 @@ static SelArgs make_args(const Geo& g, const SelectPlan& p, const void* q, const
                  reinterpret_cast<uint64_t*>(w), reinterpret_cast<int32_t*>(w + p.off_idx),
                  reinterpret_cast<int32_t*>(w + p.off_cnt), sel, cnt,
                  g.Hq, g.Hkv, g.G, g.D, g.max_pages, b_max, p.chunk, p.ppt, p.nchunk, p.cap,
-                 g.num_blocks, p.ustride, nullptr, nullptr, g.kbs, g.kts, g.khs};
+                 g.num_blocks, p.ustride, nullptr, nullptr, g.kbs, g.kts, g.khs, g.dtype == 1};
 }
 
 hipError_t launch_select_score(const Geo& g, const SelectPlan& p, const void* q,
@@ -1111,8 +1113,10 @@ hipError_t launch_select_score(const Geo& g, const SelectPlan& p, const void* q,
   }
 }
 
-bool score_takes_refresh(const Geo& g, const SelectPlan& p) {
-  return !p.prescore && (int64_t)p.nchunk * g.Hkv * g.B <= kComputeUnits;
+RefreshSite refresh_site(const Geo& g, const SelectPlan& p) {
+  if (!p.prescore && (int64_t)p.nchunk * g.Hkv * g.B <= kComputeUnits) return kRefreshInScore;
+  if (p.prescore || p.nchunk > 1) return kRefreshInMerge;
+  return kRefreshOwnLaunch;
 }
 
 // The merge runs as its own launch: the kernel boundary makes every chunk's candidates
@@ -1121,12 +1125,14 @@ bool score_takes_refresh(const Geo& g, const SelectPlan& p) {
 hipError_t launch_select_merge(const Geo& g, const SelectPlan& p, const void* q,
                                const void* meta, const int32_t* bt, const int32_t* lens,
                                const int32_t* budgets, int b_max, int32_t* sel, void* ws,
-                               hipStream_t st) {
-  if (p.prescore) return launch_certify(g, p, q, meta, bt, lens, budgets, b_max, sel, ws, st);
+                               hipStream_t st, void* meta_tail, const void* k) {
+  if (p.prescore)
+    return launch_certify(g, p, q, meta, bt, lens, budgets, b_max, sel, ws, st, meta_tail, k);
   if (p.nchunk == 1) return hipSuccess;  // the scoring stage ranked every unit completely
-  const SelArgs a = make_args(g, p, nullptr, nullptr, nullptr, lens, budgets, b_max, sel,
-                              nullptr, ws);
-  const dim3 ugrid(g.Hkv, g.B);
+  SelArgs a = make_args(g, p, nullptr, nullptr, bt, lens, budgets, b_max, sel, nullptr, ws);
+  a.meta_w = meta_tail;
+  a.k = k;
+  const dim3 ugrid(g.Hkv, g.B, meta_tail ? 2 : 1);
   hipError_t e;
   if (p.merge_threads == 64) {
     if ((e = set_lds(&merge_kernel<64>, p.merge_lds)) != hipSuccess) return e;
