@@ -17,6 +17,10 @@ Prints one JSON line. Besides the contract fields it carries:
   dense         the dense baseline (psd_dense_decode) on the same inputs
   graph_replay  the same step replayed from a captured HIP graph (launch cost removed),
                 with a bit-for-bit check against the eager outputs
+  warm          the same step on one copy of the inputs, over and over (caches warm;
+                labeled, never the headline)
+  host_link     with --v-host: the kept pages' V bytes per step and their rate over the
+                host link
 """
 from __future__ import annotations
 
@@ -176,7 +180,22 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
     per_step = total / done * w.spec.batch
     return {"value": round(1.0 / per_step, 6), "unit": "steps/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {w.spec.batch} sequences of the {w.spec.name} step "
-                      f"({total:.1f} s of fp64 NumPy on one thread), scaled to the full batch"}
+                      f"({total:.1f} s of fp64 NumPy on one thread), scaled to the full batch",
+            "host": host_info()}
+
+
+def host_info() -> dict:
+    """CPU model and the cores this process may use (the oracle above uses one)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0))}
 
 
 def main():
@@ -190,6 +209,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step (reported beside the eager rate)")
+    ap.add_argument("--v-host", action="store_true",
+                    help="V cache in pinned host memory (value tier in host DRAM): the step reads "
+                         "the kept pages' V over the host link")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -215,12 +237,13 @@ def main():
     print(f"[bench] workload {w.spec.name} generated in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
     base = DecodeStep.from_arrays(w.q, w.cache, w.block_table, w.seq_lens, w.budgets,
-                                  w.spec.dtype, w.spec.head_dim_v, w.spec.latent, device=dev)
+                                  w.spec.dtype, w.spec.head_dim_v, w.spec.latent, device=dev,
+                                  v_host=args.v_host)
     steps = [base]
     for _ in range(args.rotate - 1):
         steps.append(DecodeStep(base.q.clone(), base.cache.clone(), base.block_table.clone(),
                                 base.seq_lens.clone(), base.budgets.clone(), w.spec.head_dim_v,
-                                w.spec.latent, b_max=base.b_max))
+                                w.spec.latent, b_max=base.b_max, v_host=args.v_host))
     for st in steps:
         st.build_meta()
     torch.cuda.synchronize()
@@ -289,6 +312,9 @@ def main():
     ms_separate = timed(lambda st: st.step_separate(), args.steps)
     dense_ms = timed(lambda st: st.dense(), max(10, args.steps // 4)) if not args.no_dense else None
 
+    # warm: one copy of the inputs, steps back to back (the Infinity Cache may serve reads)
+    ms_warm = timed(lambda st: steps[0].step(), args.steps)
+
     if args.calibrate_copy:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)
@@ -332,7 +358,7 @@ def main():
                    "head_dim": w.spec.head_dim, "page": 16,
                    "budget": f"{w.spec.budget_percent}% of pages" if w.spec.budget_percent
                    else f"{w.spec.budget_pages} pages",
-                   "rotated_copies": R},
+                   "rotated_copies": R, "v_in_host_memory": bool(args.v_host)},
         "effective_hbm_gbs": round(step_gbs, 1),
         "effective_hbm_pct_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": kname, "call": dom,
@@ -346,8 +372,19 @@ def main():
                       for k, v in calls.items()},
         "separate": {"ms_per_step": round(ms_separate, 5),
                      "steps_per_s": round(1000.0 / ms_separate, 3)},
+        "warm": {"ms_per_step": round(ms_warm, 5), "steps_per_s": round(1000.0 / ms_warm, 3),
+                 "note": "one copy of the inputs, caches warm"},
         "algorithmic_bytes": ab,
     }
+    if args.v_host:
+        # the kept pages' valid V rows cross the host link once per step
+        es = 2 if w.spec.dtype == "bf16" else 4
+        lens = w.seq_lens.astype(np.int64)
+        n = (lens + 15) // 16
+        v_tok = int(np.sum(sel_counts.sum(axis=1) * 16 - w.spec.num_kv_heads * (16 - (lens - 16 * (n - 1)))))
+        v_bytes = v_tok * w.spec.head_dim_v * es
+        result["host_link"] = {"v_bytes_per_step": v_bytes,
+                               "gbs": round(v_bytes / (ms_step * 1e-3) / 1e9, 2)}
     if graph is not None:
         result["graph_replay"] = graph
     if dense_ms is not None:

@@ -205,7 +205,13 @@ size_t psd_decode_workspace_bytes(const psd_shape* shape, int32_t max_pages_atte
  * else by a second launch over partials in the workspace. Units whose sel_count is
  * negative get NaN.
  *
- *   q, k_cache, v_cache, block_table, seq_lens as above (device, read)
+ *   q, k_cache, v_cache, block_table, seq_lens as above (device, read). v_cache may
+ *               also be pinned host memory passed by its device address
+ *               (hipHostMalloc, then hipHostGetDevicePointer): the value tier in host
+ *               DRAM, of which only the kept pages' V rows cross the host link (AMASS
+ *               page and LOCKS README, "Configuration": the mem-v variant keeps K
+ *               resident and V in DRAM). The same holds for psd_select_sparse_decode,
+ *               psd_decode_step and psd_dense_decode.
  *   sel_pages, sel_count, b_max   as written by psd_select_pages (device, read)
  *   scale       softmax scale (1 / sqrt(head_dim) for standard attention)
  *   out         [B, H_q, D_v] fp32 (device, written)

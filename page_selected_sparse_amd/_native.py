@@ -56,6 +56,23 @@ class PsdShape(ctypes.Structure):
 
 
 _lib = None
+_hip = None
+
+
+def host_device_pointer(host_ptr: int) -> int:
+    """The device address of pinned host memory (hipHostGetDevicePointer), so that a kernel
+    can read it over the host link. Raises if the runtime does not map it."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                                 ctypes.c_uint]
+    dev = ctypes.c_void_p()
+    err = _hip.hipHostGetDevicePointer(ctypes.byref(dev), ctypes.c_void_p(host_ptr), 0)
+    if err != 0 or not dev.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({err}): host memory not mapped")
+    return dev.value
 
 
 def lib() -> ctypes.CDLL:

@@ -57,7 +57,17 @@ def make_shape(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor: device memory as is; pinned host memory (a CPU tensor
+    allocated with pin_memory=True) through its device mapping, so that kernels read it
+    over the host link. Any other CPU tensor is refused."""
+    if t is None:
+        return None
+    if t.device.type == "cpu":
+        if not t.is_pinned():
+            raise PsdError(-1, "a host tensor passed to the library must be pinned")
+        base = t.untyped_storage().data_ptr()
+        return ctypes.c_void_p(_native.host_device_pointer(base) + (t.data_ptr() - base))
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):

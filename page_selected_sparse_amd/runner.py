@@ -26,14 +26,22 @@ def _to_device_bits(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
 class DecodeStep:
     def __init__(self, q: torch.Tensor, cache: torch.Tensor, block_table: torch.Tensor,
                  seq_lens: torch.Tensor, budgets: torch.Tensor, head_dim_v: int,
-                 latent: bool, b_max: int | None = None):
+                 latent: bool, b_max: int | None = None, v_host: bool = False):
         """q [B, H_q, D]; cache [2, NB, 16, H_kv, D] (or [1, ...] when ``latent``: V is the
         first ``head_dim_v`` dims of K); block_table [B, max_pages] int32; seq_lens and
-        budgets [B] int32. All on the same HIP device."""
+        budgets [B] int32. All on the same HIP device. ``v_host`` moves V to pinned host
+        memory (the value tier in host DRAM): the attention then reads only the kept
+        pages' V rows over the host link."""
         self.q, self.cache = q, cache
         self.block_table, self.seq_lens, self.budgets = block_table, seq_lens, budgets
         self.k = cache[0]
         self.v = cache[0][..., :head_dim_v] if latent else cache[1]
+        if v_host:
+            if latent:
+                raise ValueError("a latent cache holds V inside K: V cannot move alone")
+            host = torch.empty(self.v.shape, dtype=self.v.dtype, pin_memory=True)
+            host.copy_(self.v)
+            self.v = host
         self.shape = api.make_shape(q, self.k, self.v, block_table, head_dim_v)
         B, Hq, D = q.shape
         NB, _, Hkv, _ = self.k.shape
@@ -65,13 +73,13 @@ class DecodeStep:
     @classmethod
     def from_arrays(cls, q: np.ndarray, cache: np.ndarray, block_table: np.ndarray,
                     seq_lens: np.ndarray, budgets: np.ndarray, dtype: str, head_dim_v: int,
-                    latent: bool, device="cuda", b_max: int | None = None):
+                    latent: bool, device="cuda", b_max: int | None = None, v_host: bool = False):
         dev = torch.device(device)
         return cls(_to_device_bits(q, dtype, dev), _to_device_bits(cache, dtype, dev),
                    torch.from_numpy(np.ascontiguousarray(block_table, dtype=np.int32)).to(dev),
                    torch.from_numpy(np.ascontiguousarray(seq_lens, dtype=np.int32)).to(dev),
                    torch.from_numpy(np.ascontiguousarray(budgets, dtype=np.int32)).to(dev),
-                   head_dim_v, latent, b_max)
+                   head_dim_v, latent, b_max, v_host)
 
     # -- the calls ------------------------------------------------------------------------
     def build_meta(self, stream=None):

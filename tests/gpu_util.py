@@ -11,14 +11,15 @@ from page_selected_sparse_amd import DecodeStep
 ATOL = 2e-3  # max abs error on outputs for bf16 inputs, fp32 accumulation
 
 
-def run_gpu(w: synth.Workload, b_max=None, dense=True, cache=None):
-    """Build the statistics, run one sparse step (and the dense decode) on the GPU."""
+def run_gpu(w: synth.Workload, b_max=None, dense=True, cache=None, v_host=False):
+    """Build the statistics, run one sparse step (and the dense decode) on the GPU. With
+    v_host the V cache sits in pinned host memory."""
     print(f"[gpu] {w.spec.name}: B={w.spec.batch} Hq={w.spec.num_q_heads} "
-          f"Hkv={w.spec.num_kv_heads} D={w.spec.head_dim} lens={list(w.seq_lens[:4])}...",
-          flush=True)
+          f"Hkv={w.spec.num_kv_heads} D={w.spec.head_dim} lens={list(w.seq_lens[:4])}... "
+          f"v_host={v_host}", flush=True)
     step = DecodeStep.from_arrays(w.q, w.cache if cache is None else cache, w.block_table,
                                   w.seq_lens, w.budgets, w.spec.dtype, w.spec.head_dim_v,
-                                  w.spec.latent, b_max=b_max)
+                                  w.spec.latent, b_max=b_max, v_host=v_host)
     step.build_meta()
     step.step()
     if dense:

@@ -171,3 +171,13 @@ def test_plans_follow_the_batch_shape(native):
     # a wider budget never needs a smaller workspace
     for sh in (one, mla):
         assert q(sh, 400)[0] >= q(sh, 100)[0]
+
+
+def test_unpinned_host_tensors_refused():
+    """A host tensor reaches the library only when pinned (mapped for the device)."""
+    import torch
+
+    from page_selected_sparse_amd import api
+
+    with pytest.raises(api.PsdError):
+        api._ptr(torch.zeros(4))

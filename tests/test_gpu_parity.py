@@ -310,6 +310,18 @@ def test_decode_step_matches_three_calls(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name", ["wide_batch", "ragged_default", "d128_f32"])
+def test_value_tier_in_host_memory(name):
+    """V in pinned host memory (the value tier in host DRAM, read over the host link): the
+    oracle's pages and outputs, and the same bits as with V in device memory."""
+    w = synth.make_workload(SMALL[name])
+    dev = run_gpu(w)
+    host = run_gpu(w, v_host=True)
+    check_workload(w, host, seqs=[0, w.spec.batch - 1], dense_seqs=[0])
+    for key in ("sel", "cnt", "out", "dense"):
+        assert np.array_equal(dev[key], host[key], equal_nan=True), key
+
+
 @pytest.mark.parametrize("name", ["latent576", "group32", "mla_64k"])
 def test_prescore_error_bound_holds(name):
     """The approximate many-head scores lie within the proven error bound of the exact fp64
