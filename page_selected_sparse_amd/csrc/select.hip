@@ -70,7 +70,7 @@ struct SelArgs {
 
 struct SelScratch {
   uint32_t hist[3][256];  // rotating: one barrier per radix pass
-  int wave_cnt[2][16];    // alternating between the two scans of an emission
+  int wave_cnt[2][16];    // wave totals of a block scan (two buffers: back-to-back scans)
   uint64_t wand[16], wor[16];
 };
 
@@ -84,31 +84,40 @@ struct SelScratch {
 // P = the K-th largest key. Equal digits met in a row by one thread are counted once.
 // One barrier per pass: histograms rotate over three buffers (a buffer is cleared two
 // passes before it is counted into) and every wave scans the histogram itself.
+// With `published`, the caller has already run kth_publish with the AND and OR of each
+// thread's nonzero keys (as it wrote them) and passed a barrier, which saves a pass over
+// the keys and a barrier.
 template <int NT>
-__device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch& sc,
-                                  uint64_t& P, uint64_t& M, int& need) {
-  constexpr int NW = NT / 64;
+__device__ __forceinline__ void kth_publish(SelScratch& sc, uint64_t kand, uint64_t kor) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int i = tid; i < 2 * 256; i += NT) sc.hist[i >> 8][i & 255] = 0;
-  uint64_t kand = ~0ull, kor = 0;
-  for (int i = tid; i < N; i += NT) {
-    const uint64_t key = keys[i];
-    if (key) {
-      kand &= key;
-      kor |= key;
-    }
-  }
   wave_and_or64(kand, kor);
   if (lane == 0) {
     sc.wand[w] = kand;
     sc.wor[w] = kor;
   }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    kand &= sc.wand[i];
-    kor |= sc.wor[i];
+}
+
+template <int NT>
+__device__ void block_kth_largest(const uint64_t* keys, int N, int K, SelScratch& sc,
+                                  uint64_t& P, uint64_t& M, int& need, bool published = false) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (!published) {
+    uint64_t kand = ~0ull, kor = 0;
+    for (int i = tid; i < N; i += NT) {
+      const uint64_t key = keys[i];
+      if (key) {
+        kand &= key;
+        kor |= key;
+      }
+    }
+    kth_publish<NT>(sc, kand, kor);
+    __syncthreads();
   }
+  // the workgroup's AND and OR: lane i < NW brings wave i's, then one wave reduction
+  uint64_t kand = lane < NW ? sc.wand[lane] : ~0ull, kor = lane < NW ? sc.wor[lane] : 0ull;
+  wave_and_or64(kand, kor);
   const uint64_t diff = kand ^ kor;
   if (diff == 0) {  // every nonzero key is equal: the first K of them
     P = kand;
@@ -207,9 +216,10 @@ __device__ __forceinline__ int block_excl_sum(int x, SelScratch& sc, int& total,
 
 // Emits, in position order, every key with (key & M) > P and the first `need` keys with
 // (key & M) == P; calls out(rank, position) for each. Each thread owns one contiguous
-// segment of positions: it counts its keys above and at the threshold, two block scans
-// give its first rank, and it writes its picks. Returns the number emitted. Every thread
-// must call it.
+// segment of positions: it counts its keys above and at the threshold, and one block scan
+// of the two counts packed in 16-bit halves (N < 65536) gives its first rank: the keys
+// above before it plus the equal keys before it, at most `need` of them. Returns the
+// number emitted. Every thread must call it.
 template <int NT, typename Out>
 __device__ int block_emit_top(const uint64_t* keys, int N, uint64_t P, uint64_t M, int need,
                               SelScratch& sc, Out out) {
@@ -222,10 +232,11 @@ __device__ int block_emit_top(const uint64_t* keys, int N, uint64_t P, uint64_t 
     eq += key == P;
   }
   int tot;
-  const int eq_before = block_excl_sum<NT>(eq, sc, tot, 0);
+  const int before = block_excl_sum<NT>((gt << 16) | eq, sc, tot, 0);
+  const int eq_before = before & 0xffff;
   const int eq_take = min(max(need - eq_before, 0), eq);
-  int emitted;
-  int pos = block_excl_sum<NT>(gt + eq_take, sc, emitted, 1);
+  const int emitted = (tot >> 16) + min(tot & 0xffff, need);
+  int pos = (before >> 16) + min(eq_before, need);
   int eq_seen = 0;
   for (int i = b0; i < e0; ++i) {
     const uint64_t key = keys[i] & M;
@@ -579,14 +590,21 @@ __device__ void merge_unit(const SelArgs& a, int unit, int n, int kp, unsigned c
   for (int c = tid; c < nch; c += NT) cnts[c] = a.ccnt[(int64_t)unit * a.nchunk + c];
   wait_vm<0>();
   __syncthreads();
+  uint64_t kand = ~0ull, kor = 0;
   for (int j = tid; j < total; j += NT) {
     const int c = j / a.cap;
-    if (j - c * a.cap >= cnts[c]) keys[j] = 0;
+    if (j - c * a.cap >= cnts[c]) {
+      keys[j] = 0;
+    } else if (const uint64_t key = keys[j]) {
+      kand &= key;
+      kor |= key;
+    }
   }
+  kth_publish<NT>(sc, kand, kor);
   __syncthreads();
   uint64_t P, M;
   int need;
-  block_kth_largest<NT>(keys, total, kp, sc, P, M, need);
+  block_kth_largest<NT>(keys, total, kp, sc, P, M, need, true);
   block_emit_top<NT>(keys, total, P, M, need, sc,
                      [&](int pos, int i) { row[1 + pos] = dense ? i + 1 : idx[i]; });
 }
@@ -674,6 +692,7 @@ __device__ __forceinline__ void score_body(const SelArgs& a, int c, int g, int s
       __syncthreads();
     }
   }
+  uint64_t kand = ~0ull, kor = 0;  // of this thread's keys, for the ranking
   for (int it = 0; it < a.ppt; ++it) {
     const int o = it * NT + tid;
     if constexpr (DPP) {
@@ -717,18 +736,24 @@ __device__ __forceinline__ void score_body(const SelArgs& a, int c, int g, int s
           if (hp * HB + h < a.G && acc[h] > best) best = acc[h];
       }
     }
-    keys[o] = score_key(best);  // every slot written; slots past cnt are never read
+    const uint64_t key = score_key(best);
+    keys[o] = key;  // every slot written; slots past cnt are never read
+    if (have && key) {
+      kand &= key;
+      kor |= key;
+    }
   }
   if constexpr (DPP) {
     if (pre) wait_vm<0>();  // a wave that skipped every round still has its first loads
   }
+  kth_publish<NT>(sc, kand, kor);
   __syncthreads();
 
   if (a.nchunk == 1) {  // the chunk is the whole unit: its top-kp is the selection
     int32_t* row = a.sel + (int64_t)unit * a.b_max;
     uint64_t P, M;
     int need;
-    block_kth_largest<NT>(keys, cnt, kp, sc, P, M, need);
+    block_kth_largest<NT>(keys, cnt, kp, sc, P, M, need, true);
     block_emit_top<NT>(keys, cnt, P, M, need, sc, [&](int pos, int i) {
       row[1 + pos] = 1 + i;
       if (list) list[1 + pos] = 1 + i;
@@ -747,7 +772,7 @@ __device__ __forceinline__ void score_body(const SelArgs& a, int c, int g, int s
   } else {
     uint64_t P, M;
     int need;
-    block_kth_largest<NT>(keys, cnt, kp, sc, P, M, need);
+    block_kth_largest<NT>(keys, cnt, kp, sc, P, M, need, true);
     const int emitted = block_emit_top<NT>(keys, cnt, P, M, need, sc, [&](int pos, int i) {
       okey[pos] = keys[i];
       oidx[pos] = lo + i;
