@@ -56,6 +56,10 @@ SMALL = {
     "wide_f32_d64": synth.small_spec(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=64,
                                      head_dim_v=64, dtype="f32", seq_lens=(),
                                      len_range=(1000, 20000), budget_percent=3, max_len=20000),
+    # one workgroup per unit (128 units, up to 2048 candidates) with one- and two-page
+    # sequences, page-boundary lengths and the longest whole unit, side by side
+    "wide_edges": synth.small_spec(batch=64, seq_lens=(1, 15, 16, 17, 33, 31, 250, 32800) * 8,
+                                   budget_percent=5, max_len=32800),
 }
 
 
@@ -218,7 +222,8 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
 # groups, D 64 and 128, a flagged unit), and batches where the one call falls back to the
 # separate launches.
 ONE_CALL = ["wide_batch", "wide_group8", "wide_f32_d64", "ragged_b32_32k", "ragged_default",
-            "group16", "latent576", "flagged_units", "chunked_wide_grid"]
+            "group16", "latent576", "flagged_units", "chunked_wide_grid", "wide_edges",
+            "edge_lengths"]
 
 
 @pytest.mark.parametrize("name", ONE_CALL)
