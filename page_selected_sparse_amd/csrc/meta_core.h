@@ -82,9 +82,9 @@ __device__ __forceinline__ void refresh_stats(const void* k, void* meta, int blk
 
 // The statistics of sequence s's tail page for KV head g (the page launch_meta_update
 // refreshes when it is given no first_page). Threads tid of nt share the dims; every
-// thread of the group calls it. Rows are folded 8 at a time to keep registers low.
-template <bool BF16>
-__device__ void refresh_tail_page(const void* k, void* meta, const int32_t* bt,
+// thread of the group calls it. Rows are requested TB at a time (8 keeps registers low).
+template <bool BF16, int TB = 8>
+__device__ __forceinline__ void refresh_tail_page(const void* k, void* meta, const int32_t* bt,
                                   const int32_t* lens, int max_pages, int s, int g, int Hkv,
                                   int D, int64_t kbs, int64_t kts, int64_t khs, int tid, int nt) {
   const int L = lens[s];
@@ -94,7 +94,7 @@ __device__ void refresh_tail_page(const void* k, void* meta, const int32_t* bt,
   const int valid = min(kPage, L - p * kPage);
   constexpr int VEC = BF16 ? 8 : 4;
   for (int d = tid * VEC; d < D; d += nt * VEC)
-    refresh_stats<BF16, 8>(k, meta, blk, valid, g, d, Hkv, D, kbs, kts, khs);
+    refresh_stats<BF16, TB>(k, meta, blk, valid, g, d, Hkv, D, kbs, kts, khs);
 }
 
 }  // namespace

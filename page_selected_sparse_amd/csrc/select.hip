@@ -934,15 +934,9 @@ void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, void* meta_w, int6
   __syncthreads();
   auto refresh_tail = [&]() {
     if constexpr (REFRESH) {
-      if ((threadIdx.x >> 6) != 15) return;
-      const int L = a.lens[s];
-      const int p = ceil_div(L, kPage) - 1;
-      if (p < 0) return;
-      const int blk = a.bt[(int64_t)s * a.max_pages + p];
-      const int valid = min(kPage, L - p * kPage);
-      constexpr int VEC = BF16 ? 8 : 4;
-      for (int d = (threadIdx.x & 63) * VEC; d < D; d += 64 * VEC)
-        refresh_stats<BF16>(aa.k, meta_w, blk, valid, g, d, a.Hkv, D, kbs, kts, khs);
+      if ((threadIdx.x >> 6) == 15)  // all 16 rows at once: the attention's registers are free
+        refresh_tail_page<BF16, kPage>(aa.k, meta_w, a.bt, a.lens, a.max_pages, s, g, a.Hkv, D,
+                                       kbs, kts, khs, threadIdx.x & 63, 64);
     }
   };
   attn_body<BF16, D, D, 1, 16>(aa, 0, g, s, list, count, refresh_tail);
