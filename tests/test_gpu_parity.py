@@ -60,6 +60,9 @@ SMALL = {
     # sequences, page-boundary lengths and the longest whole unit, side by side
     "wide_edges": synth.small_spec(batch=64, seq_lens=(1, 15, 16, 17, 33, 31, 250, 32800) * 8,
                                    budget_percent=5, max_len=32800),
+    # 130 units: not a multiple of the 8 XCDs, so the one-launch step maps units in order
+    "wide_odd_units": synth.small_spec(batch=65, seq_lens=(), len_range=(200, 9000),
+                                       budget_percent=5, max_len=9008),
 }
 
 
@@ -223,7 +226,7 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
 # separate launches.
 ONE_CALL = ["wide_batch", "wide_group8", "wide_f32_d64", "ragged_b32_32k", "ragged_default",
             "group16", "latent576", "flagged_units", "chunked_wide_grid", "wide_edges",
-            "edge_lengths"]
+            "edge_lengths", "wide_odd_units"]
 
 
 @pytest.mark.parametrize("name", ONE_CALL)
