@@ -379,7 +379,11 @@ bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* p
   p->waves = (g.G + 15) / 16;
   const int64_t units = (int64_t)g.B * g.Hkv;
   p->unit = 0;
-  if (g.G <= 16 && g.D <= 128 && units >= PSD_ATTN_UNIT_MIN && (!dense || PSD_ATTN_UNIT_DENSE)) {
+  // fp32 data take whole-unit workgroups at D = 64 only: the standalone fp32 D = 128 build
+  // of the 16-wave body was measured to give wrong outputs (cause not found; the split-K
+  // build of the same body is exact there and takes that shape instead)
+  const bool unit_ok = g.dtype == 1 ? g.D <= 128 : g.D <= 64;
+  if (g.G <= 16 && unit_ok && units >= PSD_ATTN_UNIT_MIN && (!dense || PSD_ATTN_UNIT_DENSE)) {
     // one workgroup per unit, its waves the splits, combined in LDS: no partials
     p->unit = PSD_ATTN_UNIT_WAVES;
     p->pps = (max_pages_attended + p->unit - 1) / p->unit;

@@ -60,6 +60,13 @@ SMALL = {
     # sequences, page-boundary lengths and the longest whole unit, side by side
     "wide_edges": synth.small_spec(batch=64, seq_lens=(1, 15, 16, 17, 33, 31, 250, 32800) * 8,
                                    budget_percent=5, max_len=32800),
+    # fp32 D = 128 over enough units for whole-unit workgroups (they take split-K instead)
+    "wide_f32_d128": synth.small_spec(batch=32, num_q_heads=32, num_kv_heads=8, dtype="f32",
+                                      seq_lens=(), len_range=(1000, 6000), budget_percent=5,
+                                      max_len=6000),
+    # chunked selection over few units in fp32: merge and attention stay separate launches
+    "many_chunks_f32": synth.small_spec(batch=2, seq_lens=(16 * 3000 - 5, 16 * 700),
+                                        budget_pages=40, max_len=16 * 3000, dtype="f32"),
     # 130 units: not a multiple of the 8 XCDs, so the one-launch step maps units in order
     "wide_odd_units": synth.small_spec(batch=65, seq_lens=(), len_range=(200, 9000),
                                        budget_percent=5, max_len=9008),
@@ -223,10 +230,11 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
 
 # Batches where one workgroup ranks and attends each unit (bf16 and fp32, 4- and 8-head
 # groups, D 64 and 128, a flagged unit), and batches where the one call falls back to the
-# separate launches.
+# separate launches (chunked selection, fp32 at D = 128).
 ONE_CALL = ["wide_batch", "wide_group8", "wide_f32_d64", "ragged_b32_32k", "ragged_default",
             "group16", "latent576", "flagged_units", "chunked_wide_grid", "wide_edges",
-            "edge_lengths", "wide_odd_units"]
+            "edge_lengths", "wide_odd_units", "many_chunks", "budget_over_chunk",
+            "many_chunks_f32", "wide_f32_d128"]
 
 
 @pytest.mark.parametrize("name", ONE_CALL)
