@@ -173,6 +173,36 @@ def test_plans_follow_the_batch_shape(native):
         assert q(sh, 400)[0] >= q(sh, 100)[0]
 
 
+def test_fp32_d128_batches_take_split_attention(native):
+    """Whole-unit attention (no split partials, the one-launch step) serves bf16 at D = 128
+    and fp32 at D = 64; fp32 at D = 128 takes split-K, whose partials the one-call
+    workspace then holds."""
+    lib = native.lib()
+    one_call = lambda sh: lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(sh), 102)
+    wide = dict(batch=32, max_pages_per_seq=2048, num_blocks=65536)
+    bf16 = _shape(native, **wide)
+    f32 = _shape(native, dtype=0, **wide)
+    f32_d64 = _shape(native, dtype=0, head_dim=64, head_dim_v=64, k_block_stride=16 * 8 * 64,
+                     k_token_stride=8 * 64, k_head_stride=64, v_block_stride=16 * 8 * 64,
+                     v_token_stride=8 * 64, v_head_stride=64, **wide)
+    partials = 32 * 32 * 2 * 128 * 4  # B x H_q x (at least two splits) x D_v fp32
+    assert 0 < one_call(bf16) < 64 * 1024
+    assert 0 < one_call(f32_d64) < 64 * 1024
+    assert one_call(f32) >= partials
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU and says so when asked for more."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+
+
 def test_unpinned_host_tensors_refused():
     """A host tensor reaches the library only when pinned (mapped for the device)."""
     import torch
