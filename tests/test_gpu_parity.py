@@ -381,3 +381,56 @@ def test_prescore_error_bound_holds(name):
             worst = max(worst, float(np.max(err / e)))
             assert np.all(err <= e), (s, g, float(np.max(err / e)))
     print(f"[ok] {name}: worst error / bound = {worst:.3f}", flush=True)
+
+
+def _random_spec(i: int):
+    """Seeded shape mix: KV heads 1-8, groups 1-32, D 64/128, bf16 and fp32, batches 1-64,
+    lengths from a few tokens to 20K, budgets from 1 page to every page."""
+    import random
+
+    rng = random.Random(20261 + i)
+    hkv = rng.choice([1, 2, 4, 8])
+    G = rng.choice([1, 2, 4, 4, 8, 16, 32])
+    D = rng.choice([64, 128, 128])
+    dtype = rng.choice(["bf16", "bf16", "f32"])
+    B = rng.choice([1, 2, 3, 5, 8, 16, 17, 32, 33, 64])
+    hi = rng.choice([40, 500, 3000, 9000, 20000])
+    while B * hi > 200000:
+        hi //= 2
+    hi = max(hi, 17)
+    if rng.random() < 0.5:
+        kw = dict(budget_percent=rng.choice([1, 5, 10, 50, 100]))
+    else:
+        kw = dict(budget_pages=rng.choice([0, 1, 2, 3, 8, 40, 130]))
+    return synth.small_spec(name=f"random_{i}", batch=B, num_q_heads=hkv * G,
+                            num_kv_heads=hkv, head_dim=D, head_dim_v=D, dtype=dtype,
+                            seq_lens=(), len_range=(1, hi),
+                            max_len=hi + 16 * rng.choice([0, 1, 3]), seed=500 + i, **kw)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes(i):
+    """The step against the oracle on three sampled sequences, and the one-call step
+    against the separate calls bit for bit, over a seeded mix of shapes."""
+    from page_selected_sparse_amd import DecodeStep
+
+    w = synth.make_workload(_random_spec(i))
+    res = run_gpu(w, dense=False)
+    B = w.spec.batch
+    check_workload(w, res, seqs=sorted({0, B // 2, B - 1}), dense_seqs=[])
+    step = DecodeStep.from_arrays(w.q, w.cache, w.block_table, w.seq_lens, w.budgets,
+                                  w.spec.dtype, w.spec.head_dim_v, w.spec.latent)
+    step.build_meta()
+    step.select()
+    step.sparse()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (step.sel_pages, step.sel_count, step.out)]
+    step.sel_pages.fill_(-7)
+    step.sel_count.fill_(-7)
+    step.out.fill_(123.0)
+    step.select_sparse()
+    torch.cuda.synchronize()
+    for a, b in zip((step.sel_pages, step.sel_count, step.out), ref):
+        assert _same(a, b)
+    del step
+    torch.cuda.empty_cache()
