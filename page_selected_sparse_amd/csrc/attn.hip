@@ -347,9 +347,8 @@ hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) 
   return hipGetLastError();
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, int NW = PSD_ATTN_UNIT_WAVES>
 hipError_t launch_unit(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  constexpr int NW = PSD_ATTN_UNIT_WAVES;
   auto kern = &attn_kernel<BF16, D, D, 1, (NW + 3) / 4, NW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -379,13 +378,12 @@ bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* p
   p->waves = (g.G + 15) / 16;
   const int64_t units = (int64_t)g.B * g.Hkv;
   p->unit = 0;
-  // fp32 data take whole-unit workgroups at D = 64 only: the standalone fp32 D = 128 build
-  // of the 16-wave body was measured to give wrong outputs (cause not found; the split-K
-  // build of the same body is exact there and takes that shape instead)
-  const bool unit_ok = g.dtype == 1 ? g.D <= 128 : g.D <= 64;
-  if (g.G <= 16 && unit_ok && units >= PSD_ATTN_UNIT_MIN && (!dense || PSD_ATTN_UNIT_DENSE)) {
-    // one workgroup per unit, its waves the splits, combined in LDS: no partials
-    p->unit = PSD_ATTN_UNIT_WAVES;
+  if (g.G <= 16 && g.D <= 128 && units >= PSD_ATTN_UNIT_MIN && (!dense || PSD_ATTN_UNIT_DENSE)) {
+    // one workgroup per unit, its waves the splits, combined in LDS: no partials. fp32 at
+    // D = 128 takes 8 waves: its 16-wave build spills at the 128-VGPR budget and was
+    // measured to give wrong outputs for two of every four heads, while the 8-wave build
+    // (176 VGPRs, no spill) of the same body is exact
+    p->unit = (g.dtype != 1 && g.D > 64) ? 8 : PSD_ATTN_UNIT_WAVES;
     p->pps = (max_pages_attended + p->unit - 1) / p->unit;
     p->nsplit = 1;
     p->off_ml = 0;
@@ -421,7 +419,7 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
     const dim3 ugrid(g.Hkv, g.B);
     if (g.D == 64)
       return bf ? launch_unit<true, 64>(a, ugrid, lds, st) : launch_unit<false, 64>(a, ugrid, lds, st);
-    return bf ? launch_unit<true, 128>(a, ugrid, lds, st) : launch_unit<false, 128>(a, ugrid, lds, st);
+    return bf ? launch_unit<true, 128>(a, ugrid, lds, st) : launch_unit<false, 128, 8>(a, ugrid, lds, st);
   }
   if (g.D == 64)
     e = bf ? launch_attn<true, 64, 64>(a, grid, p.waves, st)

@@ -173,22 +173,21 @@ def test_plans_follow_the_batch_shape(native):
         assert q(sh, 400)[0] >= q(sh, 100)[0]
 
 
-def test_fp32_d128_batches_take_split_attention(native):
-    """Whole-unit attention (no split partials, the one-launch step) serves bf16 at D = 128
-    and fp32 at D = 64; fp32 at D = 128 takes split-K, whose partials the one-call
-    workspace then holds."""
+def test_whole_unit_attention_needs_no_partials(native):
+    """With 256 units, whole-unit attention (bf16 and fp32, D = 64 and 128) keeps no split
+    partials, so the one-call workspace stays small; at 64 units split-K holds them."""
     lib = native.lib()
     one_call = lambda sh: lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(sh), 102)
-    wide = dict(batch=32, max_pages_per_seq=2048, num_blocks=65536)
-    bf16 = _shape(native, **wide)
-    f32 = _shape(native, dtype=0, **wide)
-    f32_d64 = _shape(native, dtype=0, head_dim=64, head_dim_v=64, k_block_stride=16 * 8 * 64,
-                     k_token_stride=8 * 64, k_head_stride=64, v_block_stride=16 * 8 * 64,
-                     v_token_stride=8 * 64, v_head_stride=64, **wide)
-    partials = 32 * 32 * 2 * 128 * 4  # B x H_q x (at least two splits) x D_v fp32
-    assert 0 < one_call(bf16) < 64 * 1024
-    assert 0 < one_call(f32_d64) < 64 * 1024
-    assert one_call(f32) >= partials
+    d64 = dict(head_dim=64, head_dim_v=64, k_block_stride=16 * 8 * 64, k_token_stride=8 * 64,
+               k_head_stride=64, v_block_stride=16 * 8 * 64, v_token_stride=8 * 64,
+               v_head_stride=64)
+    for dtype in (0, 1):
+        for extra in ({}, d64):
+            sh = _shape(native, batch=32, max_pages_per_seq=2048, num_blocks=65536, dtype=dtype,
+                        **extra)
+            assert 0 < one_call(sh) < 64 * 1024
+        few = _shape(native, batch=8, max_pages_per_seq=2048, num_blocks=65536, dtype=dtype)
+        assert one_call(few) >= 8 * 32 * 2 * 128 * 4  # B x H_q x (2+ splits) x D_v fp32
 
 
 def test_bench_refuses_more_than_one_gpu():

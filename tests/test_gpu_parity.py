@@ -60,7 +60,7 @@ SMALL = {
     # sequences, page-boundary lengths and the longest whole unit, side by side
     "wide_edges": synth.small_spec(batch=64, seq_lens=(1, 15, 16, 17, 33, 31, 250, 32800) * 8,
                                    budget_percent=5, max_len=32800),
-    # fp32 D = 128 over enough units for whole-unit workgroups (they take split-K instead)
+    # fp32 D = 128 over enough units for whole-unit workgroups (8 waves each)
     "wide_f32_d128": synth.small_spec(batch=32, num_q_heads=32, num_kv_heads=8, dtype="f32",
                                       seq_lens=(), len_range=(1000, 6000), budget_percent=5,
                                       max_len=6000),
