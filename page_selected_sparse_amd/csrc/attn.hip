@@ -419,7 +419,9 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
     const dim3 ugrid(g.Hkv, g.B);
     if (g.D == 64)
       return bf ? launch_unit<true, 64>(a, ugrid, lds, st) : launch_unit<false, 64>(a, ugrid, lds, st);
-    return bf ? launch_unit<true, 128>(a, ugrid, lds, st) : launch_unit<false, 128, 8>(a, ugrid, lds, st);
+    if (bf) return launch_unit<true, 128>(a, ugrid, lds, st);
+    // fp32 D = 128 is built for 8-wave workgroups only (plan_decode)
+    return p.unit == 8 ? launch_unit<false, 128, 8>(a, ugrid, lds, st) : hipErrorInvalidValue;
   }
   if (g.D == 64)
     e = bf ? launch_attn<true, 64, 64>(a, grid, p.waves, st)
