@@ -241,8 +241,9 @@ size_t psd_select_sparse_decode_workspace_bytes(const psd_shape* shape, int32_t 
  * units of at most 2050 pages, groups of up to 8 heads, D <= 128 in bf16 or D = 64 in
  * fp32) it is a single launch: each workgroup scores and ranks its unit's pages, keeps
  * the page list on chip and attends over it, so that no unit waits for the slowest
- * ranking of the batch before its attention starts. Otherwise the call enqueues the two calls' launches in turn, sharing
- * the workspace. sel_pages and sel_count are still written in full.
+ * ranking of the batch before its attention starts. Otherwise the call enqueues the two
+ * calls' launches in turn, sharing the workspace. sel_pages and sel_count are still
+ * written in full.
  *
  *   arguments   as for psd_select_pages and psd_sparse_decode
  *   workspace   >= psd_select_sparse_decode_workspace_bytes(shape, b_max) bytes (scratch)
