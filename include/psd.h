@@ -269,8 +269,9 @@ psd_status psd_select_sparse_decode(const psd_shape* shape, const void* q, const
  * outputs). The tail refresh runs inside another launch where it can: inside the single
  * launch of psd_select_sparse_decode, or as one extra workgroup per unit of the exact
  * scoring launch (when that launch has at most one workgroup per compute unit) or of the
- * selection's merge launch; otherwise it is a launch of its own, ahead of the selection. The tail page is never a ranking candidate, so its
- * statistics are not read by the same step's scoring. Running the refresh concurrently
+ * selection's merge launch; otherwise it is a launch of its own, ahead of the selection.
+ * The tail page is never a ranking candidate, so its statistics are not read by the same
+ * step's scoring. Running the refresh concurrently
  * with the scoring needs one more device precondition than the two calls: the block
  * holding a sequence's tail page is not an earlier page of any sequence in the batch
  * (true of a paged cache whose partly filled blocks each belong to one sequence).
