@@ -276,6 +276,24 @@ __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a) {
   __shared__ float red[NT / 64];
   const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int g = h / a.G;
+  const int64_t row = ((int64_t)s * a.Hq + h) * a.nsplit;
+  const int v4 = a.Dv / 4;
+  const int slices = NT / v4;
+  const int slice = tid / v4, c = tid - slice * v4;
+  const float4* acc = reinterpret_cast<const float4*>(a.pacc) + row * v4 + c;
+  // The first (m, l) of each thread and its slice's first PF partial rows are requested
+  // together with the length and the count, before the number of splits is known: the
+  // workspace holds nsplit entries per row, and entries past the unit's splits are never
+  // used. The sums below run in the same order either way.
+  constexpr int PF = 4;
+  const float2 ml0 = tid < a.nsplit ? a.pml[row + tid] : make_float2(-INFINITY, 0.f);
+  float4 xp[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    const int i = slice + k * slices;
+    xp[k] = (slice < slices && i < a.nsplit) ? acc[(int64_t)i * v4]
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const int L = a.lens[s];
   const int n = ceil_div(L, kPage);
   const int count = a.cnt ? min(a.cnt[s * a.Hkv + g], a.b_max) : n;
@@ -285,34 +303,33 @@ __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a) {
     return;
   }
   const int nsp = ceil_div(count, a.pps);
-  const int64_t row = ((int64_t)s * a.Hq + h) * a.nsplit;
   float m = -INFINITY;
-  for (int i = tid; i < nsp; i += NT) m = fmaxf(m, a.pml[row + i].x);
+  if (tid < nsp) m = fmaxf(m, ml0.x);
+  for (int i = tid + NT; i < nsp; i += NT) m = fmaxf(m, a.pml[row + i].x);
   const float M = block_reduce<NT>(m, red, true);
   float* wts = sh;
   float l = 0.f;
   for (int i = tid; i < nsp; i += NT) {
-    const float2 ml = a.pml[row + i];
+    const float2 ml = i == tid ? ml0 : a.pml[row + i];
     const float w = exp2f(ml.x - M);
     wts[i] = w;
     l += ml.y * w;
   }
   const float inv = 1.f / block_reduce<NT>(l, red, false);  // also publishes wts
-  const int v4 = a.Dv / 4;
-  const int slices = NT / v4;
-  const int slice = tid / v4, c = tid - slice * v4;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   if (slice < slices) {
-    const float4* acc = reinterpret_cast<const float4*>(a.pacc) + row * v4 + c;
-#pragma unroll 4
-    for (int i = slice; i < nsp; i += slices) {
-      const float4 x = acc[(int64_t)i * v4];
+    auto add = [&](const float4& x, int i) {
       const float w = wts[i];
       o.x += x.x * w;
       o.y += x.y * w;
       o.z += x.z * w;
       o.w += x.w * w;
-    }
+    };
+#pragma unroll
+    for (int k = 0; k < PF; ++k)
+      if (slice + k * slices < nsp) add(xp[k], slice + k * slices);
+#pragma unroll 4
+    for (int i = slice + PF * slices; i < nsp; i += slices) add(acc[(int64_t)i * v4], i);
   }
   float4* part = reinterpret_cast<float4*>(sh + ((a.nsplit + 3) & ~3));
   if (slices > 1) {
