@@ -30,6 +30,19 @@ What it computes, one decode step, for every sequence s and KV head g:
    softmax(scale * q.k) over the valid tokens of the kept pages, times V.
 6. Dense decode: step 5 over every page.
 
+Adaptive coverage (AMASS README, "Key AmassConfig fields"; LOCKS README,
+"Configuration", the ``coverage`` knob: a per-head nucleus over exact page masses,
+0.95 by default, GQA only) replaces steps 2-4 with:
+
+2'. Page mass: for query head h, the share of its exact softmax(scale * q_h.k) over the
+   sequence's valid tokens that falls on page p. Each head's masses sum to 1.
+3'. Group mass: the mean of the masses over the query heads of group g (the LOCKS
+   ``nrm`` combine of per-head masses; it keeps a distribution over pages).
+4'. Selection: the sink and the tail, then pages 1..n-2 in (mass descending, page
+   ascending) order, added one at a time until the kept mass reaches ``coverage`` or
+   the row (b_max entries) is full; coverage >= 1 keeps every page that fits. The list
+   is returned ascending.
+
 Where the pages leave a step open this module takes these readings: the bound is the
 exact max of q.k over the min/max box; the group combine is the max; ties go to the
 lower page index; the softmax scale is 1/sqrt(D_qk); a budget below 2 still keeps the
@@ -209,3 +222,66 @@ def dense_step(q, k_cache, v_cache, block_table, seq_lens, scale: float, head_di
         res[s] = decode_sequence(q[s], k_cache, v_cache, block_table[s], L, every, scale,
                                  head_dim_v)
     return res
+
+
+def page_masses(q_group, keys, length: int, scale: float) -> np.ndarray:
+    """Group page masses W [n] of one (sequence, KV head) unit (steps 2' and 3').
+
+    ``q_group``: [G, D] queries of the group; ``keys``: [L, D] the sequence's valid keys
+    in token order. For each head, w_h(p) is the softmax weight of head h summed over
+    the tokens of page p; W(p) is the mean of w_h(p) over the G heads.
+    """
+    q_group = np.asarray(q_group, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    n = pages_of(length)
+    z = scale * (q_group @ keys.T)                    # [G, L]
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    w = e / e.sum(axis=1, keepdims=True)              # each row sums to 1
+    page_of_token = np.arange(length) // PAGE
+    per_head = np.zeros((q_group.shape[0], n))
+    for h in range(q_group.shape[0]):
+        per_head[h] = np.bincount(page_of_token, weights=w[h], minlength=n)
+    return per_head.mean(axis=0)
+
+
+def select_coverage(mass: np.ndarray, n: int, coverage: float, b_max: int) -> np.ndarray:
+    """Kept logical pages, ascending, for coverage selection (step 4')."""
+    if n <= 2:
+        return np.arange(n, dtype=np.int64)
+    mass = np.asarray(mass, dtype=np.float64)
+    inner = np.arange(1, n - 1, dtype=np.int64)
+    order = inner[np.lexsort((inner, -mass[inner]))]
+    room = min(n - 2, max(int(b_max), 2) - 2)
+    if coverage >= 1.0:
+        take = room
+    else:
+        kept = mass[0] + mass[n - 1]
+        take = 0
+        while kept < coverage and take < room:
+            kept += mass[order[take]]
+            take += 1
+    return np.sort(np.concatenate([[0], order[:take], [n - 1]]).astype(np.int64))
+
+
+def coverage_select_sequence(q_seq, k_cache, block_table_row, length: int, num_kv_heads: int,
+                             scale: float, coverage: float, b_max: int):
+    """Coverage selection for every KV head of one sequence.
+
+    Returns (pages per head, group masses per head [H_kv, n]).
+    """
+    q_seq = np.asarray(q_seq, dtype=np.float64)
+    Hq, D = q_seq.shape
+    G = Hq // num_kv_heads
+    n = pages_of(length)
+    sel, masses = [], []
+    for g in range(num_kv_heads):
+        if n == 0:
+            sel.append(np.zeros(0, dtype=np.int64))
+            masses.append(np.zeros(0))
+            continue
+        keys = gather_tokens(k_cache, block_table_row, length, np.arange(n), g, D)
+        W = page_masses(q_seq[g * G:(g + 1) * G], keys, length, scale)
+        masses.append(W)
+        sel.append(select_coverage(W, n, coverage, b_max))
+    return sel, masses
+
