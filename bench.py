@@ -21,6 +21,9 @@ Prints one JSON line. Besides the contract fields it carries:
                 labeled, never the headline)
   host_link     with --v-host: the kept pages' V bytes per step and their rate over the
                 host link
+  coverage_select  the adaptive coverage selection (--coverage, default 0.95) on the
+                same inputs: selection alone and selection plus sparse attention, with
+                the algorithmic GB/s of the dense K read the page masses need
 """
 from __future__ import annotations
 
@@ -234,6 +237,8 @@ def main():
                          "the kept pages' V over the host link")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--coverage", type=float, default=0.95,
+                    help="target mass of the adaptive coverage selection leg (0: skip it)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -335,6 +340,52 @@ def main():
     # warm: one copy of the inputs, steps back to back (the Infinity Cache may serve reads)
     ms_warm = timed(lambda st: steps[0].step(), args.steps)
 
+    # Adaptive coverage selection (GQA shapes only): the selection alone, and selection
+    # plus the sparse attention over its rows, which hold every page of a sequence.
+    cov = None
+    if args.coverage > 0 and w.spec.group <= 8 and not w.spec.latent:
+        wide = int(w.block_table.shape[1])
+        csteps = [DecodeStep(st.q, st.cache, st.block_table, st.seq_lens, st.budgets,
+                             w.spec.head_dim_v, w.spec.latent, b_max=wide) for st in steps]
+
+        def ctimed(fn, iters):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(iters):
+                fn(csteps[i % R])
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / iters
+
+        for st in csteps:
+            st.select_coverage(args.coverage)
+            st.sparse()
+        iters = max(10, args.steps // 4)
+        ms_sel = ctimed(lambda st: st.select_coverage(args.coverage), iters)
+        ms_cstep = ctimed(lambda st: (st.select_coverage(args.coverage), st.sparse()), iters)
+        ccounts = csteps[0].sel_count.cpu().numpy()
+        es = 2 if w.spec.dtype == "bf16" else 4
+        lens = w.seq_lens.astype(np.int64)
+        n_pages = (lens + 15) // 16
+        # every valid K row once per KV head, q, and the per-head page max and sum written
+        # by the mass kernel and read back by the cut kernel
+        k_bytes = int(lens.sum()) * w.spec.num_kv_heads * w.spec.head_dim * es
+        sel_bytes = (k_bytes + w.q.nbytes + 2 * 2 * 4 * w.spec.num_q_heads * int(n_pages.sum())
+                     + ccounts.size * (wide + 1) * 4)
+        cstep_bytes = sel_bytes + algorithmic_bytes(w, ccounts)["sparse_decode"]
+        cov = {"coverage": args.coverage, "row_entries": wide,
+               "kept_pages_mean": round(float(ccounts.mean()), 1),
+               "kept_fraction_mean": round(float((ccounts / n_pages[:, None]).mean()), 4),
+               "select_ms": round(ms_sel, 5),
+               "select_gbs": round(sel_bytes / (ms_sel * 1e-3) / 1e9, 1),
+               "select_bytes": sel_bytes,
+               "step_ms": round(ms_cstep, 5),
+               "step_gbs": round(cstep_bytes / (ms_cstep * 1e-3) / 1e9, 1),
+               "step_bytes": cstep_bytes,
+               "kernels": "page_mass_kernel + coverage_cut_kernel"}
+        del csteps
+
     if args.calibrate_copy:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)
@@ -405,6 +456,8 @@ def main():
         v_bytes = v_tok * w.spec.head_dim_v * es
         result["host_link"] = {"v_bytes_per_step": v_bytes,
                                "gbs": round(v_bytes / (ms_step * 1e-3) / 1e9, 2)}
+    if cov is not None:
+        result["coverage_select"] = cov
     if graph is not None:
         result["graph_replay"] = graph
     if dense_ms is not None:

@@ -300,6 +300,46 @@ psd_status psd_dense_decode(const psd_shape* shape, const void* q, const void* k
                             const int32_t* seq_lens, float scale, float* out, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * psd_select_pages_coverage - adaptive coverage selection: keep, per (sequence, KV head),
+ * the fewest pages whose exact attention mass reaches `coverage` (a variant of
+ * psd_select_pages that needs K itself instead of the page statistics).
+ *
+ * For query head h the page mass w_h(p) is the share of h's exact
+ * softmax(scale * q_h . k) over the sequence's valid tokens that falls on page p; the
+ * group mass W(p) is the mean of w_h(p) over the group's query heads. The kept set is
+ * page 0 (sink), page n-1 (tail) and the pages 1..n-2 in (W descending, page index
+ * ascending) order, added until the kept mass reaches `coverage` or b_max pages are
+ * kept; coverage >= 1 keeps every page that fits. Sequences of n <= 2 pages keep every
+ * page.
+ *
+ *   q            [B, H_q, D] dtype, 16-byte aligned
+ *   k_cache      paged K cache (shape strides), 16-byte aligned; only valid rows are read
+ *   block_table  [B, max_pages_per_seq] int32 physical block ids
+ *   seq_lens     [B] int32 token counts
+ *   coverage     target kept mass, in (0, 1]; larger values act as 1
+ *   scale        softmax scale (> 0), normally 1/sqrt(D)
+ *   b_max        entries per selection row (>= 2); caps the kept pages
+ *   sel_pages    [B, H_kv, b_max] int32 out: kept logical pages ascending, -1 padded
+ *   sel_count    [B, H_kv] int32 out: kept pages per row
+ *   workspace    >= psd_select_coverage_workspace_bytes(shape) bytes (each query head's
+ *                page max and page exp-sum, fp32)
+ *
+ * Supported: group size G <= 8, D in {64, 128}, max_pages_per_seq <= 4096; otherwise
+ * PSD_ERR_UNSUPPORTED (the pages offer the coverage knob for GQA models only). The
+ * outputs feed psd_sparse_decode unchanged. Masses are formed in fp32 per page and
+ * normalised in fp64, so pages whose masses differ by less than about 1e-6 may order
+ * either way.
+ * Source: AMASS README, "Key AmassConfig fields" (coverage: adaptive per-head nucleus
+ * over exact page masses, default 0.95); LOCKS README, "Configuration".
+ */
+size_t psd_select_coverage_workspace_bytes(const psd_shape* shape);
+psd_status psd_select_pages_coverage(const psd_shape* shape, const void* q, const void* k_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     float coverage, float scale, int32_t b_max,
+                                     int32_t* sel_pages, int32_t* sel_count, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* psd_status_string(psd_status status);
 

@@ -7,6 +7,7 @@ from .api import (PsdError, PsdShape, decode_step, decode_workspace_bytes, dense
                   make_shape,
                   page_meta_update, select_merge, select_pages, select_score,
                   select_sparse_decode, select_sparse_decode_workspace_bytes,
+                  select_coverage_workspace_bytes, select_pages_coverage,
                   select_workspace_bytes, sparse_decode, status_string, version)
 from .runner import DecodeStep
 
@@ -14,4 +15,5 @@ __all__ = ["DecodeStep", "PsdError", "PsdShape", "decode_step", "decode_workspac
            "dense_decode",
            "make_shape", "page_meta_update", "select_merge", "select_pages", "select_score",
            "select_sparse_decode", "select_sparse_decode_workspace_bytes", "select_workspace_bytes",
+           "select_coverage_workspace_bytes", "select_pages_coverage",
            "sparse_decode", "status_string", "version"]

@@ -38,6 +38,10 @@ SIGNATURES = {
                                 c_void_p, c_size, c_void_p]),
     "psd_dense_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_float, c_void_p, c_void_p, c_size, c_void_p]),
+    "psd_select_coverage_workspace_bytes": (c_size, [c_void_p]),
+    "psd_select_pages_coverage": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_float, c_float, c_i32, c_void_p, c_void_p, c_void_p,
+                                          c_size, c_void_p]),
     "psd_status_string": (ctypes.c_char_p, [c_i32]),
     "psd_version": (c_i32, []),
 }

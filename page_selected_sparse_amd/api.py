@@ -162,3 +162,17 @@ def dense_decode(shape: PsdShape, q, k_cache, v_cache, block_table, seq_lens, sc
                                        _ptr(workspace),
                                        workspace.numel() * workspace.element_size(),
                                        _stream(stream)), "psd_dense_decode")
+
+
+def select_coverage_workspace_bytes(shape: PsdShape) -> int:
+    return int(_native.lib().psd_select_coverage_workspace_bytes(ctypes.byref(shape)))
+
+
+def select_pages_coverage(shape: PsdShape, q, k_cache, block_table, seq_lens, coverage: float,
+                          scale: float, b_max: int, sel_pages, sel_count, workspace, stream=None):
+    _ok(_native.lib().psd_select_pages_coverage(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(block_table), _ptr(seq_lens),
+        float(coverage), float(scale), int(b_max), _ptr(sel_pages), _ptr(sel_count),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "psd_select_pages_coverage")
+

@@ -1,0 +1,361 @@
+// Adaptive coverage selection: a per-(sequence, KV head) nucleus over exact page masses
+// (AMASS README, "Key AmassConfig fields", and LOCKS README, "Configuration": the
+// `coverage` knob, 0.95 by default, GQA models only).
+//
+// Page mass of query head h on page p: the share of h's exact softmax(scale * q_h.k)
+// over the sequence's valid tokens that falls on p's tokens. The group mass W(p) is the
+// mean over the group's G heads. The kept set is the sink (page 0), the tail (page n-1)
+// and the inner pages in (W descending, page ascending) order, added until the kept
+// mass reaches `coverage` or the row of b_max entries is full; coverage >= 1 keeps every
+// page that fits. The list is written ascending and padded with -1, like the budgeted
+// selection's, so that the sparse attention consumes it unchanged.
+//
+// Two launches:
+//  1. page_mass_kernel: one thread per cached token row, 16 pages per 256-thread
+//     workgroup. Each thread computes q_h.k for the group's heads in fp32; the 16 lanes of
+//     a page reduce to the page's max m_h(p) and sum s_h(p) = sum_t exp(z_t - m_h(p)),
+//     written to the workspace. This reads every valid K row once (the dense K read:
+//     exact masses cannot come from the page statistics).
+//  2. coverage_cut_kernel: one 1024-thread workgroup per unit. It forms
+//     M_h = max_p m_h(p), Z_h = sum_p s_h(p) exp(m_h(p) - M_h) and
+//     W(p) = mean_h s_h(p) exp(m_h(p) - M_h) / Z_h in fp64, sorts the inner pages in LDS
+//     (bitonic network over at most 4096 entries), finds the cut with a block scan of
+//     the sorted masses, and compacts the kept pages in ascending order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "psd_device.h"
+#include "psd_launch.h"
+
+namespace psd {
+namespace {
+
+constexpr int kCovMaxG = 8;        // query heads per group handled by the mass kernel
+constexpr int kCovMaxPages = 4096; // pages per sequence the LDS sort holds
+constexpr int kCutThreads = 1024;
+
+struct CovArgs {
+  const void* q;
+  const void* k;
+  const int32_t* bt;
+  const int32_t* lens;
+  int32_t* sel;
+  int32_t* cnt;
+  float* pm;  // [B * Hq, max_pages] page max of each query head
+  float* ps;  // [B * Hq, max_pages] page exp-sum of each query head
+  float scale, coverage;
+  int Hq, Hkv, G, max_pages, num_blocks, b_max;
+  int64_t kbs, kts, khs;
+};
+
+__device__ __forceinline__ int seq_pages(const CovArgs& a, int s) {
+  const int L = a.lens[s];
+  return min(max(ceil_div(max(L, 0), kPage), 0), a.max_pages);
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void page_mass_kernel(CovArgs a) {
+  __shared__ float qs[kCovMaxG * D];
+  const int s = blockIdx.z, g = blockIdx.y;
+  const int L = a.lens[s];
+  const int n = seq_pages(a, s);
+  if ((int)blockIdx.x * 16 >= n) return;  // uniform over the workgroup
+  const int tid = threadIdx.x;
+  const int lp = blockIdx.x * 16 + (tid >> 4), row = tid & 15;
+  const int G = a.G;
+  const int64_t q0 = ((int64_t)s * a.Hq + (int64_t)g * G) * D;
+  for (int i = tid; i < G * D; i += 256) {
+    if constexpr (BF16)
+      qs[i] = __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.q)[q0 + i] << 16);
+    else
+      qs[i] = static_cast<const float*>(a.q)[q0 + i];
+  }
+  __syncthreads();
+
+  const bool valid = lp < n && lp * kPage + row < L;
+  float z[kCovMaxG];
+#pragma unroll
+  for (int h = 0; h < kCovMaxG; ++h) z[h] = 0.f;
+  if (valid) {
+    int blk = a.bt[(int64_t)s * a.max_pages + lp];
+    blk = min(max(blk, 0), a.num_blocks - 1);
+    const int64_t base = (int64_t)blk * a.kbs + (int64_t)row * a.kts + (int64_t)g * a.khs;
+    constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte load
+#pragma unroll 4
+    for (int d0 = 0; d0 < D; d0 += EPV) {
+      float kv[EPV];
+      if constexpr (BF16) {
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + base + d0);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kv[2 * j] = bf_lo(ws[j]);
+          kv[2 * j + 1] = bf_hi(ws[j]);
+        }
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + base + d0);
+        kv[0] = f.x; kv[1] = f.y; kv[2] = f.z; kv[3] = f.w;
+      }
+#pragma unroll
+      for (int h = 0; h < kCovMaxG; ++h) {
+        if (h < G) {
+#pragma unroll
+          for (int j = 0; j < EPV; ++j) z[h] = fmaf(qs[h * D + d0 + j], kv[j], z[h]);
+        }
+      }
+    }
+  }
+  if (lp >= n) return;  // whole 16-lane page groups leave together
+#pragma unroll
+  for (int h = 0; h < kCovMaxG; ++h) {
+    if (h < G) {
+      const float zz = valid ? a.scale * z[h] : -INFINITY;
+      float m = zz;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+      float e = valid ? expf(zz - m) : 0.f;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o, 16);
+      if (row == 0) {
+        const int64_t at = ((int64_t)s * a.Hq + (int64_t)g * G + h) * a.max_pages + lp;
+        a.pm[at] = m;
+        a.ps[at] = e;
+      }
+    }
+  }
+}
+
+// Block-wide inclusive scan of one double per thread (Hillis-Steele in LDS).
+__device__ double block_scan_incl(double v, double* buf) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kCutThreads; off <<= 1) {
+    const double add = t >= off ? buf[t - off] : 0.0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  const double r = buf[t];
+  __syncthreads();
+  return r;
+}
+
+// Entry a goes before entry b: heavier first, lower page on equal mass.
+__device__ __forceinline__ bool goes_first(double wa, int pa, double wb, int pb) {
+  return wa > wb || (wa == wb && pa < pb);
+}
+
+__global__ __launch_bounds__(kCutThreads) void coverage_cut_kernel(CovArgs a) {
+  __shared__ double key[kCovMaxPages];
+  __shared__ int pg[kCovMaxPages];
+  __shared__ double buf[kCutThreads];
+  __shared__ unsigned char flag[kCovMaxPages];
+  __shared__ float Mh[kCovMaxG];
+  __shared__ double Zh[kCovMaxG];
+  __shared__ double ends[2];
+  __shared__ int kcut, total;
+
+  const int g = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
+  const int unit = s * a.Hkv + g;
+  const int G = a.G;
+  int32_t* out = a.sel + (int64_t)unit * a.b_max;
+  const int n = seq_pages(a, s);
+  if (n <= 2) {
+    for (int i = t; i < a.b_max; i += kCutThreads) out[i] = i < n ? i : -1;
+    if (t == 0) a.cnt[unit] = n;
+    return;
+  }
+  const int64_t h0 = (int64_t)s * a.Hq + (int64_t)g * G;
+
+  // Per-head max and normalizer over the sequence's pages.
+  for (int h = 0; h < G; ++h) {
+    const float* pm = a.pm + (h0 + h) * a.max_pages;
+    const float* ps = a.ps + (h0 + h) * a.max_pages;
+    float m = -INFINITY;
+    for (int p = t; p < n; p += kCutThreads) m = fmaxf(m, pm[p]);
+    buf[t] = m;
+    __syncthreads();
+    for (int w = kCutThreads / 2; w > 0; w >>= 1) {
+      if (t < w) buf[t] = fmax(buf[t], buf[t + w]);
+      __syncthreads();
+    }
+    const float M = (float)buf[0];
+    __syncthreads();
+    double z = 0.0;
+    for (int p = t; p < n; p += kCutThreads) z += (double)ps[p] * exp((double)pm[p] - (double)M);
+    buf[t] = z;
+    __syncthreads();
+    for (int w = kCutThreads / 2; w > 0; w >>= 1) {
+      if (t < w) buf[t] += buf[t + w];
+      __syncthreads();
+    }
+    if (t == 0) {
+      Mh[h] = M;
+      Zh[h] = buf[0];
+    }
+    __syncthreads();
+  }
+
+  // Group masses: inner pages 1..n-2 go to sort slot p-1; the ends are kept aside.
+  const int mc = n - 2;
+  int np2 = 1;
+  while (np2 < mc) np2 <<= 1;
+  for (int p = t; p < n; p += kCutThreads) {
+    double w = 0.0;
+    for (int h = 0; h < G; ++h) {
+      const int64_t at = (h0 + h) * a.max_pages + p;
+      w += (double)a.ps[at] * exp((double)a.pm[at] - (double)Mh[h]) / Zh[h];
+    }
+    w /= (double)G;
+    if (p == 0) {
+      ends[0] = w;
+    } else if (p == n - 1) {
+      ends[1] = w;
+    } else {
+      key[p - 1] = w;
+      pg[p - 1] = p;
+    }
+  }
+  for (int i = mc + t; i < np2; i += kCutThreads) {  // padding sorts last
+    key[i] = -1.0;
+    pg[i] = INT32_MAX;
+  }
+  __syncthreads();
+
+  // Bitonic sort of slots [0, np2) into (mass descending, page ascending) order.
+  for (int k = 2; k <= np2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = t; i < np2; i += kCutThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const bool up = (i & k) == 0;
+          const bool swap = up ? goes_first(key[l], pg[l], key[i], pg[i])
+                               : goes_first(key[i], pg[i], key[l], pg[l]);
+          if (swap) {
+            const double tk = key[i];
+            key[i] = key[l];
+            key[l] = tk;
+            const int tp = pg[i];
+            pg[i] = pg[l];
+            pg[l] = tp;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // The cut: the fewest leading slots whose mass, with the ends, reaches the coverage.
+  const int room = min(mc, a.b_max - 2);
+  constexpr int PER = kCovMaxPages / kCutThreads;  // sorted slots per thread
+  const double base = ends[0] + ends[1];
+  if (t == 0) kcut = mc;
+  double local = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = t * PER + j;
+    if (i < mc) local += key[i];
+  }
+  const double incl = block_scan_incl(local, buf);  // also orders kcut's init before use
+  int take;
+  if (a.coverage >= 1.f) {
+    take = room;
+  } else if (base >= (double)a.coverage) {
+    take = 0;
+  } else {
+    double run = base + incl - local;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = t * PER + j;
+      if (i < mc) {
+        run += key[i];
+        if (run >= (double)a.coverage) {
+          atomicMin(&kcut, i + 1);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    take = min(kcut, room);
+  }
+
+  // Flags in page order, then an ascending compaction.
+  for (int p = t; p < n; p += kCutThreads) flag[p] = (p == 0 || p == n - 1) ? 1 : 0;
+  __syncthreads();
+  for (int i = t; i < take; i += kCutThreads) {
+    const int p = pg[i];
+    if (p < n) flag[p] = 1;  // padding (page id past n) sorts last unless masses are NaN
+  }
+  __syncthreads();
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int p = t * PER + j;
+    if (p < n) mine += flag[p];
+  }
+  const int incl_cnt = (int)block_scan_incl((double)mine, buf);
+  if (t == kCutThreads - 1) total = incl_cnt;
+  int at = incl_cnt - mine;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int p = t * PER + j;
+    if (p < n && flag[p]) out[at++] = p;
+  }
+  __syncthreads();
+  const int count = total;  // take + 2 for finite masses
+  for (int i = count + t; i < a.b_max; i += kCutThreads) out[i] = -1;
+  if (t == 0) a.cnt[unit] = count;
+}
+
+template <bool BF16, int D>
+hipError_t launch_mass(const CovArgs& a, int B, hipStream_t st) {
+  dim3 grid((a.max_pages + 15) / 16, a.Hkv, B);
+  hipLaunchKernelGGL((page_mass_kernel<BF16, D>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t coverage_workspace_bytes(const Geo& g) {
+  return 2 * sizeof(float) * (size_t)g.B * g.Hq * g.max_pages;
+}
+
+bool coverage_supported(const Geo& g) {
+  return g.G <= kCovMaxG && g.max_pages <= kCovMaxPages && (g.D == 64 || g.D == 128);
+}
+
+hipError_t launch_coverage_select(const Geo& g, const void* q, const void* k, const int32_t* bt,
+                                  const int32_t* lens, float coverage, float scale, int b_max,
+                                  int32_t* sel, int32_t* cnt, void* ws, hipStream_t st) {
+  CovArgs a;
+  a.q = q;
+  a.k = k;
+  a.bt = bt;
+  a.lens = lens;
+  a.sel = sel;
+  a.cnt = cnt;
+  a.pm = static_cast<float*>(ws);
+  a.ps = a.pm + (size_t)g.B * g.Hq * g.max_pages;
+  a.scale = scale;
+  a.coverage = coverage;
+  a.Hq = g.Hq;
+  a.Hkv = g.Hkv;
+  a.G = g.G;
+  a.max_pages = g.max_pages;
+  a.num_blocks = g.num_blocks;
+  a.b_max = b_max;
+  a.kbs = g.kbs;
+  a.kts = g.kts;
+  a.khs = g.khs;
+  hipError_t e;
+  if (g.dtype == 1)
+    e = g.D == 64 ? launch_mass<true, 64>(a, g.B, st) : launch_mass<true, 128>(a, g.B, st);
+  else
+    e = g.D == 64 ? launch_mass<false, 64>(a, g.B, st) : launch_mass<false, 128>(a, g.B, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(coverage_cut_kernel, dim3(g.Hkv, g.B), dim3(kCutThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace psd

@@ -304,3 +304,36 @@ const char* psd_status_string(psd_status s) {
 int32_t psd_version(void) { return 100; }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t psd_select_coverage_workspace_bytes(const psd_shape* shape) {
+  psd::Geo g;
+  if (check_shape(shape, &g) != PSD_OK || !psd::coverage_supported(g)) return 0;
+  return psd::coverage_workspace_bytes(g);
+}
+
+psd_status psd_select_pages_coverage(const psd_shape* shape, const void* q, const void* k_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     float coverage, float scale, int32_t b_max,
+                                     int32_t* sel_pages, int32_t* sel_count, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  psd::Geo g;
+  psd_status st = check_shape(shape, &g);
+  if (st != PSD_OK) return st;
+  if (!q || !k_cache || !block_table || !seq_lens || !sel_pages || !sel_count)
+    return PSD_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(q)) return PSD_ERR_INVALID_ARG;
+  if (b_max < 2 || !(coverage > 0.f) || !(scale > 0.f) || coverage != coverage)
+    return PSD_ERR_INVALID_ARG;
+  if ((st = check_strides(g, false)) != PSD_OK) return st;
+  if (!psd::coverage_supported(g)) return PSD_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < psd::coverage_workspace_bytes(g) || !aligned16(workspace))
+    return PSD_ERR_WORKSPACE;
+  return launched(psd::launch_coverage_select(g, q, k_cache, block_table, seq_lens, coverage,
+                                              scale, b_max, sel_pages, sel_count, workspace,
+                                              stream));
+}
+
+}  // extern "C"
+

@@ -104,4 +104,14 @@ hipError_t launch_select_decode(const Geo& g, const SelectPlan& sp, const Decode
                                 int b_max, float scale, int32_t* sel, int32_t* cnt, float* out,
                                 void* ws, void* meta_tail, hipStream_t st);
 
+// ---- adaptive coverage selection ---------------------------------------------------------
+// Exact page masses from every valid K row, then a per-unit nucleus cut (G <= 8,
+// max_pages <= 4096, D in {64, 128}). Writes selection rows and counts like the budgeted
+// selection. The workspace holds each query head's page max and page exp-sum.
+size_t coverage_workspace_bytes(const Geo& g);
+bool coverage_supported(const Geo& g);
+hipError_t launch_coverage_select(const Geo& g, const void* q, const void* k, const int32_t* bt,
+                                  const int32_t* lens, float coverage, float scale, int b_max,
+                                  int32_t* sel, int32_t* cnt, void* ws, hipStream_t st);
+
 }  // namespace psd

@@ -69,6 +69,7 @@ class DecodeStep:
             raise api.PsdError(-2, "workspace query")
         self.ws_fused = torch.empty(fused_ws, dtype=torch.uint8, device=dev)
         self.first_page_zero = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.ws_coverage = None  # sized on first use of select_coverage
 
     @classmethod
     def from_arrays(cls, q: np.ndarray, cache: np.ndarray, block_table: np.ndarray,
@@ -106,6 +107,18 @@ class DecodeStep:
         """Second stage of ``select``: the winners of every unit from the candidates."""
         api.select_merge(self.shape, self.q, self.meta, self.block_table, self.seq_lens,
                          self.budgets, self.b_max, self.sel_pages, self.ws_select, stream)
+
+    def select_coverage(self, coverage: float, stream=None):
+        """Adaptive coverage selection into ``sel_pages`` / ``sel_count`` (reads every
+        valid K row; the statistics are not used)."""
+        if self.ws_coverage is None:
+            nbytes = api.select_coverage_workspace_bytes(self.shape)
+            if nbytes == 0:
+                raise api.PsdError(-2, "psd_select_coverage_workspace_bytes")
+            self.ws_coverage = torch.empty(nbytes, dtype=torch.uint8, device=self.q.device)
+        api.select_pages_coverage(self.shape, self.q, self.k, self.block_table, self.seq_lens,
+                                  coverage, self.scale, self.b_max, self.sel_pages,
+                                  self.sel_count, self.ws_coverage, stream)
 
     def sparse(self, stream=None):
         api.sparse_decode(self.shape, self.q, self.k, self.v, self.block_table, self.seq_lens,

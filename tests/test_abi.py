@@ -210,3 +210,25 @@ def test_unpinned_host_tensors_refused():
 
     with pytest.raises(api.PsdError):
         api._ptr(torch.zeros(4))
+
+
+def test_coverage_selection_checks(native):
+    lib = native.lib()
+    sh = _shape(native)
+    f = ctypes.c_void_p(16)
+    need = lib.psd_select_coverage_workspace_bytes(ctypes.byref(sh))
+    assert need == 2 * 4 * sh.batch * sh.num_q_heads * sh.max_pages_per_seq
+    call = lib.psd_select_pages_coverage
+    assert call(None, f, f, f, f, 0.95, 0.1, 10, f, f, f, need, None) == -1
+    assert call(ctypes.byref(sh), None, f, f, f, 0.95, 0.1, 10, f, f, f, need, None) == -1
+    assert call(ctypes.byref(sh), f, f, f, f, 0.0, 0.1, 10, f, f, f, need, None) == -1
+    assert call(ctypes.byref(sh), f, f, f, f, float("nan"), 0.1, 10, f, f, f, need, None) == -1
+    assert call(ctypes.byref(sh), f, f, f, f, 0.95, 0.0, 10, f, f, f, need, None) == -1
+    assert call(ctypes.byref(sh), f, f, f, f, 0.95, 0.1, 1, f, f, f, need, None) == -1
+    assert call(ctypes.byref(sh), f, f, f, f, 0.95, 0.1, 10, f, f, f, need - 4, None) == -3
+    assert call(ctypes.byref(sh), f, f, f, f, 0.95, 0.1, 10, f, f, None, need, None) == -3
+    # groups of more than 8 query heads, more than 4096 pages, and the latent shape
+    for kw in (dict(num_q_heads=sh.num_kv_heads * 16), dict(max_pages_per_seq=4097)):
+        big = _shape(native, **kw)
+        assert lib.psd_select_coverage_workspace_bytes(ctypes.byref(big)) == 0
+        assert call(ctypes.byref(big), f, f, f, f, 0.95, 0.1, 10, f, f, f, 1 << 40, None) == -2
