@@ -79,7 +79,8 @@ KERNEL_SOURCES = {"score_kernel": ("select.hip",), "merge_kernel": ("select.hip"
                   "prescore_kernel": ("prescore.hip",), "certify_kernel": ("prescore.hip",),
                   "meta_kernel": ("meta.hip",), "attn_kernel": ("attn.hip", "attn_core.h"),
                   "attn_latent_kernel": ("attn.hip", "attn_core.h"),
-                  "lse_merge_kernel": ("attn.hip", "attn_core.h")}
+                  "lse_merge_kernel": ("attn.hip", "attn_core.h"),
+                  "page_mass_kernel": ("coverage.hip",), "coverage_cut_kernel": ("coverage.hip",)}
 
 
 def one_call_kernel(w):
@@ -383,7 +384,10 @@ def main():
                "step_ms": round(ms_cstep, 5),
                "step_gbs": round(cstep_bytes / (ms_cstep * 1e-3) / 1e9, 1),
                "step_bytes": cstep_bytes,
-               "kernels": "page_mass_kernel + coverage_cut_kernel"}
+               "kernels": "page_mass_kernel + coverage_cut_kernel",
+               # HBM bytes per launch from the committed counters (None when stale)
+               "traffic": {k: measured_traffic(k, w.spec.name)
+                           for k in ("page_mass_kernel", "coverage_cut_kernel")}}
         del csteps
 
     if args.calibrate_copy:
