@@ -11,10 +11,10 @@
 // selection's, so that the sparse attention consumes it unchanged.
 //
 // Two launches:
-//  1. page_mass_kernel: one thread per cached token row, 16 pages per 256-thread
-//     workgroup. Each thread computes q_h.k for the group's heads in fp32; the 16 lanes of
-//     a page reduce to the page's max m_h(p) and sum s_h(p) = sum_t exp(z_t - m_h(p)),
-//     written to the workspace. This reads every valid K row once (the dense K read:
+//  1. page_mass_kernel: one wave per page, 16 pages per 256-thread workgroup. Each
+//     load instruction reads whole token rows; the lanes of a row add their slices of
+//     q_h.k (fp32), and the wave reduces the page's max m_h(p) and sum
+//     s_h(p) = sum_t exp(z_t - m_h(p)), written to the workspace. This reads every valid K row once (the dense K read:
 //     exact masses cannot come from the page statistics).
 //  2. coverage_cut_kernel: one 1024-thread workgroup per unit. It forms
 //     M_h = max_p m_h(p), Z_h = sum_p s_h(p) exp(m_h(p) - M_h) and
@@ -53,73 +53,127 @@ __device__ __forceinline__ int seq_pages(const CovArgs& a, int s) {
   return min(max(ceil_div(max(L, 0), kPage), 0), a.max_pages);
 }
 
-template <bool BF16, int D>
+// Sum over each group of LPR consecutive lanes, in every lane of the group.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPR == 16) {  // a DPP row: rotations by 1, 2, 4 and 8 within the row
+    v += __int_as_float(dpp_move<0x121>(__float_as_int(v)));
+    v += __int_as_float(dpp_move<0x122>(__float_as_int(v)));
+    v += __int_as_float(dpp_move<0x124>(__float_as_int(v)));
+    v += __int_as_float(dpp_move<0x128>(__float_as_int(v)));
+  } else {
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) v += __shfl_xor(v, o);
+  }
+  return v;
+}
+
+// One wave per page: each load instruction covers whole token rows (LPR lanes x 16 bytes
+// per row, 64 / LPR rows per instruction), so a page's K rows arrive as 16 contiguous
+// row reads; each lane keeps its 16-byte slice of q for every head of the group in
+// registers. A workgroup of 4 waves covers 16 consecutive pages.
+template <bool BF16, int D, int GM>
 __global__ __launch_bounds__(256) void page_mass_kernel(CovArgs a) {
-  __shared__ float qs[kCovMaxG * D];
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int EPL = 16 / ES;         // elements per lane and row
+  constexpr int LPR = D * ES / 16;     // lanes per row
+  constexpr int RPI = kWave / LPR;     // rows per load instruction
+  constexpr int RPL = kPage / RPI;     // rows per lane
+  static_assert(LPR * RPI == kWave && RPL * RPI == kPage, "row tiling");
   const int s = blockIdx.z, g = blockIdx.y;
   const int L = a.lens[s];
   const int n = seq_pages(a, s);
-  if ((int)blockIdx.x * 16 >= n) return;  // uniform over the workgroup
-  const int tid = threadIdx.x;
-  const int lp = blockIdx.x * 16 + (tid >> 4), row = tid & 15;
+  if ((int)blockIdx.x * 16 >= n) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = lane % LPR, rs = lane / LPR;
   const int G = a.G;
-  const int64_t q0 = ((int64_t)s * a.Hq + (int64_t)g * G) * D;
-  for (int i = tid; i < G * D; i += 256) {
-    if constexpr (BF16)
-      qs[i] = __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.q)[q0 + i] << 16);
-    else
-      qs[i] = static_cast<const float*>(a.q)[q0 + i];
-  }
-  __syncthreads();
 
-  const bool valid = lp < n && lp * kPage + row < L;
-  float z[kCovMaxG];
+  float qv[GM][EPL];
+  const int64_t q0 = ((int64_t)s * a.Hq + (int64_t)g * G) * D + part * EPL;
 #pragma unroll
-  for (int h = 0; h < kCovMaxG; ++h) z[h] = 0.f;
-  if (valid) {
+  for (int h = 0; h < GM; ++h) {
+    if (h < G) {
+      const uint4 w = load16(static_cast<const unsigned char*>(a.q) + (q0 + (int64_t)h * D) * ES);
+      if constexpr (BF16) {
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          qv[h][2 * j] = bf_lo(ws[j]);
+          qv[h][2 * j + 1] = bf_hi(ws[j]);
+        }
+      } else {
+        qv[h][0] = __uint_as_float(w.x);
+        qv[h][1] = __uint_as_float(w.y);
+        qv[h][2] = __uint_as_float(w.z);
+        qv[h][3] = __uint_as_float(w.w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) qv[h][j] = 0.f;
+    }
+  }
+
+  for (int it = 0; it < 4; ++it) {
+    const int lp = blockIdx.x * 16 + it * 4 + wave;
+    if (lp >= n) break;  // uniform over the wave
     int blk = a.bt[(int64_t)s * a.max_pages + lp];
     blk = min(max(blk, 0), a.num_blocks - 1);
-    const int64_t base = (int64_t)blk * a.kbs + (int64_t)row * a.kts + (int64_t)g * a.khs;
-    constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte load
-#pragma unroll 4
-    for (int d0 = 0; d0 < D; d0 += EPV) {
-      float kv[EPV];
+    const unsigned char* kb = static_cast<const unsigned char*>(a.k) +
+        ((int64_t)blk * a.kbs + (int64_t)g * a.khs + part * EPL) * ES;
+    // Rows past the length are loaded (they lie inside the block) and masked below.
+    uint4 raw[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) raw[i] = load16(kb + (int64_t)(rs + RPI * i) * a.kts * ES);
+    float z[RPL][GM];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      float kv[EPL];
       if constexpr (BF16) {
-        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + base + d0);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        const uint32_t ws[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           kv[2 * j] = bf_lo(ws[j]);
           kv[2 * j + 1] = bf_hi(ws[j]);
         }
       } else {
-        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + base + d0);
-        kv[0] = f.x; kv[1] = f.y; kv[2] = f.z; kv[3] = f.w;
+        kv[0] = __uint_as_float(raw[i].x);
+        kv[1] = __uint_as_float(raw[i].y);
+        kv[2] = __uint_as_float(raw[i].z);
+        kv[3] = __uint_as_float(raw[i].w);
       }
 #pragma unroll
-      for (int h = 0; h < kCovMaxG; ++h) {
+      for (int h = 0; h < GM; ++h) {
+        float acc = 0.f;
         if (h < G) {
 #pragma unroll
-          for (int j = 0; j < EPV; ++j) z[h] = fmaf(qs[h * D + d0 + j], kv[j], z[h]);
+          for (int j = 0; j < EPL; ++j) acc = fmaf(qv[h][j], kv[j], acc);
+          acc = group_sum<LPR>(acc);
         }
+        z[i][h] = acc;
       }
     }
-  }
-  if (lp >= n) return;  // whole 16-lane page groups leave together
 #pragma unroll
-  for (int h = 0; h < kCovMaxG; ++h) {
-    if (h < G) {
-      const float zz = valid ? a.scale * z[h] : -INFINITY;
-      float m = zz;
+    for (int h = 0; h < GM; ++h) {
+      if (h < G) {
+        float m = -INFINITY;
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
-      float e = valid ? expf(zz - m) : 0.f;
+        for (int i = 0; i < RPL; ++i) {
+          const bool valid = lp * kPage + rs + RPI * i < L;
+          z[i][h] = valid ? a.scale * z[i][h] : -INFINITY;
+          m = fmaxf(m, z[i][h]);
+        }
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o, 16);
-      if (row == 0) {
-        const int64_t at = ((int64_t)s * a.Hq + (int64_t)g * G + h) * a.max_pages + lp;
-        a.pm[at] = m;
-        a.ps[at] = e;
+        for (int o = LPR; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        float e = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) e += z[i][h] == -INFINITY ? 0.f : expf(z[i][h] - m);
+#pragma unroll
+        for (int o = LPR; o < kWave; o <<= 1) e += __shfl_xor(e, o);
+        if (lane == 0) {
+          const int64_t at = ((int64_t)s * a.Hq + (int64_t)g * G + h) * a.max_pages + lp;
+          a.pm[at] = m;
+          a.ps[at] = e;
+        }
       }
     }
   }
@@ -311,7 +365,10 @@ __global__ __launch_bounds__(kCutThreads) void coverage_cut_kernel(CovArgs a) {
 template <bool BF16, int D>
 hipError_t launch_mass(const CovArgs& a, int B, hipStream_t st) {
   dim3 grid((a.max_pages + 15) / 16, a.Hkv, B);
-  hipLaunchKernelGGL((page_mass_kernel<BF16, D>), grid, dim3(256), 0, st, a);
+  if (a.G <= 4)  // head slots held in registers: 4 or 8
+    hipLaunchKernelGGL((page_mass_kernel<BF16, D, 4>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((page_mass_kernel<BF16, D, kCovMaxG>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -153,3 +153,12 @@ def test_coverage_full_size_sampled():
     cnt = res["cnt"]
     for s in range(w.spec.batch):
         assert np.all((cnt[s] >= 2) & (cnt[s] <= n[s])), s
+
+
+@pytest.mark.parametrize("dtype,d,hq", [("bf16", 64, 4), ("f32", 128, 8), ("bf16", 128, 16)])
+def test_coverage_row_widths(dtype, d, hq):
+    # rows of 8 lanes (bf16 D=64), 32 lanes (fp32 D=128), and 8-head groups at bf16 D=128
+    spec = synth.small_spec(f"cov_{dtype}_{d}", num_q_heads=hq, num_kv_heads=2, head_dim=d,
+                            head_dim_v=d, dtype=dtype, **SMALL)
+    w = synth.make_workload(spec)
+    check(w, run_coverage(w, 0.9, 258), 0.9, 258)
