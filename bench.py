@@ -80,7 +80,8 @@ KERNEL_SOURCES = {"score_kernel": ("select.hip",), "merge_kernel": ("select.hip"
                   "meta_kernel": ("meta.hip",), "attn_kernel": ("attn.hip", "attn_core.h"),
                   "attn_latent_kernel": ("attn.hip", "attn_core.h"),
                   "lse_merge_kernel": ("attn.hip", "attn_core.h"),
-                  "page_mass_kernel": ("coverage.hip",), "coverage_cut_kernel": ("coverage.hip",)}
+                  "page_mass_mfma_kernel": ("coverage.hip",),
+                  "coverage_cut_kernel": ("coverage.hip",)}
 
 
 def one_call_kernel(w):
@@ -384,10 +385,11 @@ def main():
                "step_ms": round(ms_cstep, 5),
                "step_gbs": round(cstep_bytes / (ms_cstep * 1e-3) / 1e9, 1),
                "step_bytes": cstep_bytes,
-               "kernels": "page_mass_kernel + coverage_cut_kernel",
+               "kernels": "page_mass_mfma_kernel (bf16) or page_mass_kernel (fp32) + "
+                          "coverage_cut_kernel",
                # HBM bytes per launch from the committed counters (None when stale)
                "traffic": {k: measured_traffic(k, w.spec.name)
-                           for k in ("page_mass_kernel", "coverage_cut_kernel")}}
+                           for k in ("page_mass_mfma_kernel", "coverage_cut_kernel")}}
         del csteps
 
     if args.calibrate_copy:

@@ -11,10 +11,11 @@
 // selection's, so that the sparse attention consumes it unchanged.
 //
 // Two launches:
-//  1. page_mass_kernel: one wave per page, 16 pages per 256-thread workgroup. Each
-//     load instruction reads whole token rows; the lanes of a row add their slices of
-//     q_h.k (fp32), and the wave reduces the page's max m_h(p) and sum
-//     s_h(p) = sum_t exp(z_t - m_h(p)), written to the workspace. This reads every valid K row once (the dense K read:
+//  1. page_mass_mfma_kernel (bf16) / page_mass_kernel (fp32): one wave per page, 16
+//     pages per 256-thread workgroup. The page's q_h.k for the group's heads come from
+//     matrix-core steps (bf16) or from whole-row loads and lane sums (fp32); the wave
+//     reduces the page's max m_h(p) and sum s_h(p) = sum_t exp(z_t - m_h(p)), written
+//     to the workspace. This reads every valid K row once (the dense K read:
 //     exact masses cannot come from the page statistics).
 //  2. coverage_cut_kernel: one 1024-thread workgroup per unit. It forms
 //     M_h = max_p m_h(p), Z_h = sum_p s_h(p) exp(m_h(p) - M_h) and
@@ -33,6 +34,8 @@ namespace {
 constexpr int kCovMaxG = 8;        // query heads per group handled by the mass kernel
 constexpr int kCovMaxPages = 4096; // pages per sequence the LDS sort holds
 constexpr int kCutThreads = 1024;
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 struct CovArgs {
   const void* q;
@@ -175,6 +178,72 @@ __global__ __launch_bounds__(256) void page_mass_kernel(CovArgs a) {
           a.ps[at] = e;
         }
       }
+    }
+  }
+}
+
+// bf16 pages on the matrix cores: one wave per page computes S^T = K_page Q^T (16 tokens x
+// up to 16 heads) with D/32 v_mfma_f32_16x16x32_bf16 steps. Lane l loads 16 bytes of token
+// row l % 16 at dims 32c + 8 (l / 16) (the A operand) and holds the same dims of head
+// l % 16 (the B operand; heads past the group are zero). The result leaves in lane l the
+// scores of head l % 16 for tokens 4 (l / 16) .. +3, so the page's max and exp-sum per
+// head take two lane exchanges each.
+template <int D>
+__global__ __launch_bounds__(256) void page_mass_mfma_kernel(CovArgs a) {
+  constexpr int NQ = D / 32;
+  const int s = blockIdx.z, g = blockIdx.y;
+  const int L = a.lens[s];
+  const int n = seq_pages(a, s);
+  if ((int)blockIdx.x * 16 >= n) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int G = a.G;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  uint4 qf[NQ];
+  const int64_t qrow = ((int64_t)s * a.Hq + (int64_t)g * G + (r < G ? r : 0)) * D + 8 * grp;
+#pragma unroll
+  for (int c = 0; c < NQ; ++c)
+    qf[c] = r < G ? load16(q + qrow + 32 * c) : make_uint4(0, 0, 0, 0);
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + (int64_t)g * a.khs +
+                          (int64_t)r * a.kts + 8 * grp;
+
+  for (int it = 0; it < 4; ++it) {
+    const int lp = blockIdx.x * 16 + it * 4 + wave;
+    if (lp >= n) break;  // uniform over the wave
+    int blk = a.bt[(int64_t)s * a.max_pages + lp];
+    blk = min(max(blk, 0), a.num_blocks - 1);
+    const uint16_t* kr = kbase + (int64_t)blk * a.kbs;
+    // Rows past the length are loaded (they lie inside the block) and masked below.
+    uint4 kf[NQ];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) kf[c] = load16(kr + 32 * c);
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      const u32x4 kv = {kf[c].x, kf[c].y, kf[c].z, kf[c].w};
+      const u32x4 qv = {qf[c].x, qf[c].y, qf[c].z, qf[c].w};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                    __builtin_bit_cast(bf16x8, qv), acc, 0, 0, 0);
+    }
+    const int t0 = lp * kPage + 4 * grp;
+    float z[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      z[k] = t0 + k < L ? a.scale * acc[k] : -INFINITY;
+      m = fmaxf(m, z[k]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float e = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e += z[k] == -INFINITY ? 0.f : expf(z[k] - m);
+    e += __shfl_xor(e, 16);
+    e += __shfl_xor(e, 32);
+    if (grp == 0 && r < G) {
+      const int64_t at = ((int64_t)s * a.Hq + (int64_t)g * G + r) * a.max_pages + lp;
+      a.pm[at] = m;
+      a.ps[at] = e;
     }
   }
 }
@@ -365,7 +434,9 @@ __global__ __launch_bounds__(kCutThreads) void coverage_cut_kernel(CovArgs a) {
 template <bool BF16, int D>
 hipError_t launch_mass(const CovArgs& a, int B, hipStream_t st) {
   dim3 grid((a.max_pages + 15) / 16, a.Hkv, B);
-  if (a.G <= 4)  // head slots held in registers: 4 or 8
+  if constexpr (BF16)  // the matrix cores take the page's q.k
+    hipLaunchKernelGGL((page_mass_mfma_kernel<D>), grid, dim3(256), 0, st, a);
+  else if (a.G <= 4)  // head slots held in registers: 4 or 8
     hipLaunchKernelGGL((page_mass_kernel<BF16, D, 4>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((page_mass_kernel<BF16, D, kCovMaxG>), grid, dim3(256), 0, st, a);
