@@ -20,7 +20,7 @@
 //  2. coverage_cut_kernel: one 1024-thread workgroup per unit. It forms
 //     M_h = max_p m_h(p), Z_h = sum_p s_h(p) exp(m_h(p) - M_h) and
 //     W(p) = mean_h s_h(p) exp(m_h(p) - M_h) / Z_h in fp64, sorts the inner pages in LDS
-//     (bitonic network over at most 4096 entries), finds the cut with a block scan of
+//     on 64-bit (fp32 mass, page) keys (bitonic network over at most 4096 entries), finds the cut with a block scan of
 //     the sorted masses, and compacts the kept pages in ascending order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -264,22 +264,23 @@ __device__ double block_scan_incl(double v, double* buf) {
   return r;
 }
 
-// Entry a goes before entry b: heavier first, lower page on equal mass.
-__device__ __forceinline__ bool goes_first(double wa, int pa, double wb, int pb) {
-  return wa > wb || (wa == wb && pa < pb);
-}
-
 __global__ __launch_bounds__(kCutThreads) void coverage_cut_kernel(CovArgs a) {
-  __shared__ double key[kCovMaxPages];
-  __shared__ int pg[kCovMaxPages];
+  constexpr int NW = kCutThreads / kWave;
+  // Sort keys: the group mass as fp32 bits (non-negative, so the bits order like the
+  // values) above the inverted page index, so that a descending sort gives
+  // (mass descending, page ascending); 0 pads and sorts last.
+  __shared__ uint64_t key[kCovMaxPages];
   __shared__ double buf[kCutThreads];
   __shared__ unsigned char flag[kCovMaxPages];
+  __shared__ float redf[NW][kCovMaxG];
+  __shared__ double redd[NW][kCovMaxG];
   __shared__ float Mh[kCovMaxG];
   __shared__ double Zh[kCovMaxG];
   __shared__ double ends[2];
   __shared__ int kcut, total;
 
   const int g = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int unit = s * a.Hkv + g;
   const int G = a.G;
   int32_t* out = a.sel + (int64_t)unit * a.b_max;
@@ -291,34 +292,54 @@ __global__ __launch_bounds__(kCutThreads) void coverage_cut_kernel(CovArgs a) {
   }
   const int64_t h0 = (int64_t)s * a.Hq + (int64_t)g * G;
 
-  // Per-head max and normalizer over the sequence's pages.
-  for (int h = 0; h < G; ++h) {
-    const float* pm = a.pm + (h0 + h) * a.max_pages;
-    const float* ps = a.ps + (h0 + h) * a.max_pages;
-    float m = -INFINITY;
-    for (int p = t; p < n; p += kCutThreads) m = fmaxf(m, pm[p]);
-    buf[t] = m;
-    __syncthreads();
-    for (int w = kCutThreads / 2; w > 0; w >>= 1) {
-      if (t < w) buf[t] = fmax(buf[t], buf[t + w]);
-      __syncthreads();
-    }
-    const float M = (float)buf[0];
-    __syncthreads();
-    double z = 0.0;
-    for (int p = t; p < n; p += kCutThreads) z += (double)ps[p] * exp((double)pm[p] - (double)M);
-    buf[t] = z;
-    __syncthreads();
-    for (int w = kCutThreads / 2; w > 0; w >>= 1) {
-      if (t < w) buf[t] += buf[t + w];
-      __syncthreads();
-    }
-    if (t == 0) {
-      Mh[h] = M;
-      Zh[h] = buf[0];
-    }
-    __syncthreads();
+  // Each head's max over the pages, then its normaliser: per-thread values, wave
+  // shuffles, one pass through LDS.
+  float mloc[kCovMaxG];
+#pragma unroll
+  for (int h = 0; h < kCovMaxG; ++h) mloc[h] = -INFINITY;
+  for (int p = t; p < n; p += kCutThreads) {
+#pragma unroll
+    for (int h = 0; h < kCovMaxG; ++h)
+      if (h < G) mloc[h] = fmaxf(mloc[h], a.pm[(h0 + h) * a.max_pages + p]);
   }
+#pragma unroll
+  for (int h = 0; h < kCovMaxG; ++h) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mloc[h] = fmaxf(mloc[h], __shfl_xor(mloc[h], o));
+    if (lane == 0) redf[wave][h] = mloc[h];
+  }
+  __syncthreads();
+  if (t < G) {
+    float m = -INFINITY;
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, redf[w][t]);
+    Mh[t] = m;
+  }
+  __syncthreads();
+  double zloc[kCovMaxG];
+#pragma unroll
+  for (int h = 0; h < kCovMaxG; ++h) zloc[h] = 0.0;
+  for (int p = t; p < n; p += kCutThreads) {
+#pragma unroll
+    for (int h = 0; h < kCovMaxG; ++h) {
+      if (h < G) {
+        const int64_t at = (h0 + h) * a.max_pages + p;
+        zloc[h] += (double)a.ps[at] * exp((double)a.pm[at] - (double)Mh[h]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kCovMaxG; ++h) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) zloc[h] += __shfl_xor(zloc[h], o);
+    if (lane == 0) redd[wave][h] = zloc[h];
+  }
+  __syncthreads();
+  if (t < G) {
+    double z = 0.0;
+    for (int w = 0; w < NW; ++w) z += redd[w][t];
+    Zh[t] = z;
+  }
+  __syncthreads();
 
   // Group masses: inner pages 1..n-2 go to sort slot p-1; the ends are kept aside.
   const int mc = n - 2;
@@ -336,38 +357,30 @@ __global__ __launch_bounds__(kCutThreads) void coverage_cut_kernel(CovArgs a) {
     } else if (p == n - 1) {
       ends[1] = w;
     } else {
-      key[p - 1] = w;
-      pg[p - 1] = p;
+      key[p - 1] = ((uint64_t)__float_as_uint((float)w) << 32) | (uint32_t)(0xffffffffu - p);
     }
   }
-  for (int i = mc + t; i < np2; i += kCutThreads) {  // padding sorts last
-    key[i] = -1.0;
-    pg[i] = INT32_MAX;
-  }
+  for (int i = mc + t; i < np2; i += kCutThreads) key[i] = 0;  // padding sorts last
   __syncthreads();
 
-  // Bitonic sort of slots [0, np2) into (mass descending, page ascending) order.
+  // Bitonic sort of slots [0, np2) into descending key order.
   for (int k = 2; k <= np2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = t; i < np2; i += kCutThreads) {
         const int l = i ^ j;
         if (l > i) {
-          const bool up = (i & k) == 0;
-          const bool swap = up ? goes_first(key[l], pg[l], key[i], pg[i])
-                               : goes_first(key[i], pg[i], key[l], pg[l]);
-          if (swap) {
-            const double tk = key[i];
-            key[i] = key[l];
-            key[l] = tk;
-            const int tp = pg[i];
-            pg[i] = pg[l];
-            pg[l] = tp;
+          const uint64_t ki = key[i], kl = key[l];
+          if ((i & k) == 0 ? kl > ki : ki > kl) {
+            key[i] = kl;
+            key[l] = ki;
           }
         }
       }
       __syncthreads();
     }
   }
+  auto slot_mass = [&](int i) { return (double)__uint_as_float((uint32_t)(key[i] >> 32)); };
+  auto slot_page = [&](int i) { return (int)(0xffffffffu - (uint32_t)key[i]); };
 
   // The cut: the fewest leading slots whose mass, with the ends, reaches the coverage.
   const int room = min(mc, a.b_max - 2);
@@ -378,7 +391,7 @@ __global__ __launch_bounds__(kCutThreads) void coverage_cut_kernel(CovArgs a) {
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = t * PER + j;
-    if (i < mc) local += key[i];
+    if (i < mc) local += slot_mass(i);
   }
   const double incl = block_scan_incl(local, buf);  // also orders kcut's init before use
   int take;
@@ -392,7 +405,7 @@ __global__ __launch_bounds__(kCutThreads) void coverage_cut_kernel(CovArgs a) {
     for (int j = 0; j < PER; ++j) {
       const int i = t * PER + j;
       if (i < mc) {
-        run += key[i];
+        run += slot_mass(i);
         if (run >= (double)a.coverage) {
           atomicMin(&kcut, i + 1);
           break;
@@ -407,8 +420,8 @@ __global__ __launch_bounds__(kCutThreads) void coverage_cut_kernel(CovArgs a) {
   for (int p = t; p < n; p += kCutThreads) flag[p] = (p == 0 || p == n - 1) ? 1 : 0;
   __syncthreads();
   for (int i = t; i < take; i += kCutThreads) {
-    const int p = pg[i];
-    if (p < n) flag[p] = 1;  // padding (page id past n) sorts last unless masses are NaN
+    const int p = slot_page(i);
+    if ((unsigned)p < (unsigned)n) flag[p] = 1;  // padding decodes past n
   }
   __syncthreads();
   int mine = 0;
