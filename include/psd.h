@@ -327,9 +327,9 @@ psd_status psd_dense_decode(const psd_shape* shape, const void* q, const void* k
  *
  * Supported: group size G <= 8, D in {64, 128}, max_pages_per_seq <= 4096; otherwise
  * PSD_ERR_UNSUPPORTED (the pages offer the coverage knob for GQA models only). The
- * outputs feed psd_sparse_decode unchanged. Masses are formed in fp32 per page and
- * normalised in fp64, so pages whose masses differ by less than about 1e-6 may order
- * either way.
+ * outputs feed psd_sparse_decode unchanged. Masses are formed in fp32 per page,
+ * normalised in fp64 and ranked as fp32 values, so pages whose masses differ by less than
+ * about 1e-6 may order either way.
  * Source: AMASS README, "Key AmassConfig fields" (coverage: adaptive per-head nucleus
  * over exact page masses, default 0.95); LOCKS README, "Configuration".
  */
