@@ -207,16 +207,28 @@ __global__ __launch_bounds__(256) void page_mass_mfma_kernel(CovArgs a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + (int64_t)g * a.khs +
                           (int64_t)r * a.kts + 8 * grp;
 
+  // The wave's four pages: block ids up front, then each page's rows requested while
+  // the previous page is reduced. Rows past the length are loaded (they lie inside the
+  // block) and masked below.
+  int blks[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int lp = blockIdx.x * 16 + it * 4 + wave;
+    blks[it] = lp < n ? min(max(a.bt[(int64_t)s * a.max_pages + lp], 0), a.num_blocks - 1) : 0;
+  }
+  uint4 kf[NQ], nx[NQ];
+  if (blockIdx.x * 16 + wave < n) {
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) kf[c] = load16(kbase + (int64_t)blks[0] * a.kbs + 32 * c);
+  }
+#pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int lp = blockIdx.x * 16 + it * 4 + wave;
     if (lp >= n) break;  // uniform over the wave
-    int blk = a.bt[(int64_t)s * a.max_pages + lp];
-    blk = min(max(blk, 0), a.num_blocks - 1);
-    const uint16_t* kr = kbase + (int64_t)blk * a.kbs;
-    // Rows past the length are loaded (they lie inside the block) and masked below.
-    uint4 kf[NQ];
+    if (it < 3 && lp + 4 < n) {
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) kf[c] = load16(kr + 32 * c);
+      for (int c = 0; c < NQ; ++c) nx[c] = load16(kbase + (int64_t)blks[it + 1] * a.kbs + 32 * c);
+    }
     float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
@@ -245,6 +257,8 @@ __global__ __launch_bounds__(256) void page_mass_mfma_kernel(CovArgs a) {
       a.pm[at] = m;
       a.ps[at] = e;
     }
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) kf[c] = nx[c];
   }
 }
 
