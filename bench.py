@@ -10,8 +10,12 @@ do not hit in the last-level cache.
 
 Prints one JSON line. Besides the contract fields it carries:
   roofline      achieved algorithmic GB/s of the dominant kernel against 8 TB/s
-  cpu_baseline  the fp64 oracle's step on the host, on a bounded sample of sequences
+  cpu_baseline  the fp64 oracle's step on the host: all usable cores (the value), one
+                thread, and the oracle's dense step
   calls         per-call average durations (HIP events on the launch stream)
+  launch_floor  back-to-back empty kernels on the same stream (the per-launch floor)
+  configs       the other measured workloads (tiny, 8B-GQA shape at 32K, 1M tokens, MLA
+                latent): one decode step and the dense decode, with the speed-up
   separate      the same step as three calls (page_meta_update, select_pages,
                 sparse_decode)
   dense         the dense baseline (psd_dense_decode) on the same inputs
@@ -88,13 +92,13 @@ def one_call_kernel(w):
     """The kernel behind decode_step and select_sparse_decode when each is a single launch,
     else None.
     Follows the library's planning rule: at least 128 (sequence, KV head) units, at most
-    2048 candidate pages per unit, groups of up to 8 query heads, D = D_v <= 128 (bf16) or
+    2048 candidate pages per unit, groups of up to 4 query heads, D = D_v <= 128 (bf16) or
     D = D_v = 64 (fp32), and no certified pre-score."""
     sp = w.spec
     G = sp.num_q_heads // sp.num_kv_heads
     units = sp.batch * sp.num_kv_heads
     d_ok = sp.head_dim <= 128 if sp.dtype == "bf16" else sp.head_dim == 64
-    if (G <= 8 and d_ok and sp.head_dim_v == sp.head_dim and units >= 128 and
+    if (G <= 4 and d_ok and sp.head_dim_v == sp.head_dim and units >= 128 and
             w.block_table.shape[1] - 2 <= 2048):
         return "select_attn_kernel"
     return None
@@ -157,47 +161,97 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(w, budget_s: float = 15.0, min_s: float = 10.0) -> dict:
-    """Time the fp64 oracle's decode step (tail refresh, bound, selection, attention) with
-    BLAS pinned to one thread. When the whole batch takes under min_s / 3, whole-batch
-    passes repeat until min_s has elapsed (at least three) and the median pass is
-    reported; otherwise as many sequences as fit in ~budget_s are timed and scaled to
-    the batch."""
+def _oracle_seq_time(w, inp, s, prefill, kind: str) -> float:
+    """Seconds of the oracle's step for sequence s: the decode step (tail refresh, bound,
+    selection, attention; the prefill statistics are given, untimed) or the dense step."""
+    from oracle import psd_oracle as O
+
+    L = int(w.seq_lens[s])
+    n = O.pages_of(L)
+    if kind == "dense":
+        t0 = time.perf_counter()
+        O.dense_step(inp["q"], inp["k_cache"], inp["v_cache"], w.block_table, w.seq_lens,
+                     w.scale, w.spec.head_dim_v, w.spec.num_kv_heads, sequences=[s])
+        return time.perf_counter() - t0
+    kmin, kmax = (m.copy() for m in prefill[s])
+    t0 = time.perf_counter()
+    tail = inp["k_cache"][w.block_table[s, n - 1: n]][0, : O.valid_in_page(L, n - 1)]
+    kmin[n - 1], kmax[n - 1] = O.page_minmax(tail)
+    sel, _ = O.select_sequence(inp["q"][s], kmin, kmax, w.spec.num_kv_heads, n,
+                               int(w.budgets[s]))
+    O.decode_sequence(inp["q"][s], inp["k_cache"], inp["v_cache"], w.block_table[s], L, sel,
+                      w.scale, w.spec.head_dim_v)
+    return time.perf_counter() - t0
+
+
+_FORKED = {}  # the workload, inherited by forked oracle workers
+
+
+def _oracle_worker(job):
+    """One forked worker: its share of the batch (every P-th sequence), `passes` times.
+    Returns the seconds of each pass."""
     from threadpoolctl import threadpool_limits
 
     import synth
     from oracle import psd_oracle as O
 
+    j, P, passes, kind = job
+    w = _FORKED["w"]
     inp = synth.oracle_inputs(w)
-    Hkv = w.spec.num_kv_heads
+    seqs = list(range(j, w.spec.batch, P))
+    with threadpool_limits(limits=1):
+        prefill = {} if kind == "dense" else {
+            s: O.sequence_meta(inp["k_cache"], w.block_table[s], int(w.seq_lens[s])) for s in seqs}
+        return [sum(_oracle_seq_time(w, inp, s, prefill, kind) for s in seqs)
+                for _ in range(passes)]
 
+
+def _oracle_all_cores(w, kind: str, cores: int, passes: int) -> float:
+    """Median seconds of a whole-batch oracle pass with the sequences spread over `cores`
+    forked processes (BLAS one thread each): a pass lasts as long as its busiest worker."""
+    import multiprocessing as mp
+
+    _FORKED["w"] = w
+    P = max(1, min(cores, w.spec.batch))
+    with mp.get_context("fork").Pool(P) as pool:
+        per_worker = pool.map(_oracle_worker, [(j, P, passes, kind) for j in range(P)])
+    return float(np.median(np.max(np.array(per_worker), axis=0)))
+
+
+def cpu_baseline(w, budget_s: float = 15.0, min_s: float = 10.0) -> dict:
+    """The fp64 oracle as it stands, timed on the host. Runs before the GPU is touched
+    (it forks worker processes).
+
+    value: the decode step (tail refresh, bound, selection, attention) over the whole
+    batch with the sequences spread over all usable cores (one process per core, at most
+    16, BLAS one thread each), median of three passes. one_thread: the same step on one
+    thread: whole-batch passes repeated until min_s has elapsed (at least three, median
+    reported) when a pass takes under min_s / 3, else as many sequences as fit in
+    ~budget_s, scaled to the batch. dense: the oracle's dense step on all cores."""
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import psd_oracle as O
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    t_all = _oracle_all_cores(w, "sparse", cores, 3)
+    t_dense = _oracle_all_cores(w, "dense", cores, 1 if w.spec.batch < cores else 3)
+
+    inp = synth.oracle_inputs(w)
     prefill = {}
-
-    def one(s):
-        L = int(w.seq_lens[s])
-        n = O.pages_of(L)
-        if s not in prefill:  # the statistics of every page (prefill), untimed
-            prefill[s] = O.sequence_meta(inp["k_cache"], w.block_table[s], L)
-        kmin, kmax = (m.copy() for m in prefill[s])
-        t0 = time.perf_counter()
-        tail = inp["k_cache"][w.block_table[s, n - 1: n]][0, : O.valid_in_page(L, n - 1)]
-        kmin[n - 1], kmax[n - 1] = O.page_minmax(tail)
-        sel, _ = O.select_sequence(inp["q"][s], kmin, kmax, Hkv, n, int(w.budgets[s]))
-        O.decode_sequence(inp["q"][s], inp["k_cache"], inp["v_cache"], w.block_table[s], L,
-                          sel, w.scale, w.spec.head_dim_v)
-        return time.perf_counter() - t0
-
     with threadpool_limits(limits=1):
         total, done = 0.0, 0
         for s in range(w.spec.batch):
-            total += one(s)
+            prefill[s] = O.sequence_meta(inp["k_cache"], w.block_table[s], int(w.seq_lens[s]))
+            total += _oracle_seq_time(w, inp, s, prefill, "sparse")
             done += 1
             if total >= budget_s:
                 break
         if done == w.spec.batch and total < min_s / 3:
             passes = [total]
             while len(passes) < 3 or sum(passes) < min_s:
-                passes.append(sum(one(s) for s in range(w.spec.batch)))
+                passes.append(sum(_oracle_seq_time(w, inp, s, prefill, "sparse")
+                                  for s in range(w.spec.batch)))
             per_step = float(np.median(passes))
             sample = (f"the whole {w.spec.name} step, {len(passes)} passes "
                       f"({sum(passes):.1f} s of fp64 NumPy on one thread), median pass")
@@ -205,8 +259,16 @@ def cpu_baseline(w, budget_s: float = 15.0, min_s: float = 10.0) -> dict:
             per_step = total / done * w.spec.batch
             sample = (f"{done} of {w.spec.batch} sequences of the {w.spec.name} step "
                       f"({total:.1f} s of fp64 NumPy on one thread), scaled to the full batch")
-    return {"value": round(1.0 / per_step, 6), "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "host": host_info()}
+    used = min(cores, w.spec.batch)
+    return {"value": round(1.0 / t_all, 6), "unit": "steps/s", "cores": used, "kind": "oracle",
+            "sample": (f"the whole {w.spec.name} step, sequences spread over {used} processes "
+                       f"(BLAS one thread each), median of 3 passes of {t_all:.2f} s"),
+            "one_thread": {"value": round(1.0 / per_step, 6), "unit": "steps/s", "cores": 1,
+                           "sample": sample},
+            "dense": {"value": round(1.0 / t_dense, 6), "unit": "steps/s", "cores": used,
+                      "sample": f"the oracle's dense step over the whole batch, {t_dense:.2f} s "
+                                f"per pass on {used} processes"},
+            "host": host_info()}
 
 
 def host_info() -> dict:
@@ -221,6 +283,68 @@ def host_info() -> dict:
     except OSError:
         pass
     return {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0))}
+
+
+def timed_over(objs, fn, iters: int) -> float:
+    """Average ms of fn(objs[i % len(objs)]) over iters back-to-back calls: HIP events on
+    torch's current stream (the stream the library's kernels are queued on), bracketed by
+    device synchronisations."""
+    import torch
+
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(objs[i % len(objs)])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def launch_floor(iters: int) -> dict:
+    """Back-to-back empty kernels (torch's spin kernel with zero cycles) on the current
+    stream: the per-launch cost below which no dependent launch chain can go."""
+    import torch
+
+    for _ in range(10):
+        torch.cuda._sleep(0)
+    ms = timed_over([None], lambda _: torch.cuda._sleep(0), iters)
+    return {"us_per_launch": round(ms * 1e3, 3), "launches": iters,
+            "kernel": "torch.cuda._sleep(0), back to back on one stream"}
+
+
+def measure_config(name: str, args, dev) -> dict:
+    """One decode step (psd_decode_step) and the dense decode (psd_dense_decode) of
+    another measured workload, on rotated resident copies as for the headline."""
+    import torch
+
+    import synth
+    from page_selected_sparse_amd import DecodeStep
+
+    w = synth.make_workload(name)
+    base = DecodeStep.from_arrays(w.q, w.cache, w.block_table, w.seq_lens, w.budgets,
+                                  w.spec.dtype, w.spec.head_dim_v, w.spec.latent, device=dev)
+    sts = [base] + [DecodeStep(base.q.clone(), base.cache.clone(), base.block_table.clone(),
+                               base.seq_lens.clone(), base.budgets.clone(), w.spec.head_dim_v,
+                               w.spec.latent, b_max=base.b_max) for _ in range(args.rotate - 1)]
+    for st in sts:
+        st.build_meta()
+    for i in range(max(args.warmup, 2 * len(sts))):
+        sts[i % len(sts)].step()
+        sts[i % len(sts)].dense()
+    iters = max(20, args.steps)
+    ms_step = timed_over(sts, lambda st: st.step(), iters)
+    ms_dense = timed_over(sts, lambda st: st.dense(), max(10, iters // 4))
+    ab = algorithmic_bytes(w, sts[0].sel_count.cpu().numpy())
+    res = {"workload": name, "step_us": round(ms_step * 1e3, 2),
+           "dense_us": round(ms_dense * 1e3, 2),
+           "speedup_vs_dense": round(ms_dense / ms_step, 3),
+           "step_gbs": round(ab["step"] / (ms_step * 1e-3) / 1e9, 1),
+           "dense_gbs": round(ab["dense_decode"] / (ms_dense * 1e-3) / 1e9, 1),
+           "dtype": w.spec.dtype, "rotated_copies": len(sts)}
+    del sts, base
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -241,6 +365,8 @@ def main():
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--coverage", type=float, default=0.95,
                     help="target mass of the adaptive coverage selection leg (0: skip it)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the step / dense pairs of the other measured workloads")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -248,9 +374,21 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import synth
+
+    t0 = time.time()
+    w = synth.make_workload(args.workload)
+    print(f"[bench] workload {w.spec.name} generated in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:  # forks worker processes: before the GPU is initialised
+        t0 = time.time()
+        cpu = cpu_baseline(w)
+        print(f"[bench] oracle baseline timed in {time.time() - t0:.1f}s", file=sys.stderr,
+              flush=True)
+
     import torch
 
-    import synth
     from page_selected_sparse_amd import DecodeStep
 
     if not torch.cuda.is_available():
@@ -259,10 +397,6 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    t0 = time.time()
-    w = synth.make_workload(args.workload)
-    print(f"[bench] workload {w.spec.name} generated in {time.time() - t0:.1f}s", file=sys.stderr,
-          flush=True)
     base = DecodeStep.from_arrays(w.q, w.cache, w.block_table, w.seq_lens, w.budgets,
                                   w.spec.dtype, w.spec.head_dim_v, w.spec.latent, device=dev,
                                   v_host=args.v_host)
@@ -470,8 +604,12 @@ def main():
         result["dense"] = {"ms": round(dense_ms, 5),
                            "gbs": round(ab["dense_decode"] / (dense_ms * 1e-3) / 1e9, 1),
                            "step_speedup_vs_dense": round(dense_ms / ms_step, 3)}
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w)
+    result["launch_floor"] = launch_floor(max(100, args.steps))
+    if not args.no_configs:
+        result["configs"] = [measure_config(name, args, dev) for name in synth.CONFIG_ORDER
+                             if name != w.spec.name]
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -870,6 +870,8 @@ hipError_t launch_score(const SelArgs& a, const SelectPlan& p, dim3 sgrid, hipSt
 
 // (threads, chunks per load group, groups in flight) triples the planner picks from;
 // (CPL, S) = (1, 1) is the fallback when the tuned staging does not fit in LDS.
+// 1024-thread workgroups are built for 4-head groups only: at the 128-VGPR budget of 16
+// waves per CU the 8-head accumulators spill, so 8-head whole units take 512 threads.
 template <bool BF16, int D, int HB>
 hipError_t dispatch_dpp(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStream_t st) {
   const bool tuned = p.cpl > 1 || p.stages > 1;
@@ -881,7 +883,9 @@ hipError_t dispatch_dpp(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStr
     case 512:
       return tuned ? launch_score<BF16, D, HB, true, 512, PSD_UNIT_CPL, PSD_UNIT_STAGES>(a, p, grid, st)
                    : launch_score<BF16, D, HB, true, 512, 1, 1>(a, p, grid, st);
-    default: return launch_score<BF16, D, HB, true, 1024, 1, 1>(a, p, grid, st);
+    default:
+      if constexpr (HB == 4) return launch_score<BF16, D, HB, true, 1024, 1, 1>(a, p, grid, st);
+      return hipErrorInvalidValue;  // not planned: plan_select gives 8-head units 512 threads
   }
 }
 
@@ -917,6 +921,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
 void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, void* meta_w, int64_t kbs,
                         int64_t kts, int64_t khs) {
   static_assert(PSD_ATTN_UNIT_WAVES == 16, "one attention split per wave of the workgroup");
+  // Built only where it fits the 128 VGPRs of 16 waves per CU without spilling: 4-head
+  // groups, and fp32 only at D = 64 (8-head groups and fp32 at D = 128 spill).
+  static_assert(HB == 4 && (BF16 || D <= 64), "fused step: no spill-free build");
   extern __shared__ unsigned char lds[];
   int32_t* list = reinterpret_cast<int32_t*>(lds + list_off);
 #if PSD_FUSED_XCD_MAP
@@ -945,8 +952,8 @@ void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, void* meta_w, int6
 template <bool BF16, int D, bool REFRESH>
 hipError_t launch_fused(const SelArgs& a, const AttnArgs& aa, int head_block, dim3 grid,
                         size_t lds, int list_off, void* meta_w, const Geo& g, hipStream_t st) {
-  auto kern = head_block == 4 ? &select_attn_kernel<BF16, D, 4, REFRESH>
-                              : &select_attn_kernel<BF16, D, 8, REFRESH>;
+  if (head_block != 4) return hipErrorInvalidValue;  // fused_applies admits 4-head groups only
+  auto kern = &select_attn_kernel<BF16, D, 4, REFRESH>;
   hipError_t e = set_lds(kern, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(1024), lds, st, a, aa, list_off, meta_w, g.kbs, g.kts,
@@ -1036,7 +1043,7 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
   bool ok = false;
   if (dpp && inner <= 2048 && units >= PSD_UNIT_MIN_UNITS) {
     // one workgroup per unit: scores every page and ranks them, no merge
-    p->threads = PSD_UNIT_THREADS;
+    p->threads = p->head_block == 4 ? PSD_UNIT_THREADS : 512;
     p->ppt = (inner + p->threads - 1) / p->threads;
     p->chunk = p->threads * p->ppt;
     p->nchunk = 1;
@@ -1168,7 +1175,7 @@ hipError_t launch_select_merge(const Geo& g, const SelectPlan& p, const void* q,
 
 bool fused_applies(const Geo& g, const SelectPlan& sp, const DecodePlan& dp, int b_max) {
   if (sp.prescore || sp.nchunk != 1 || sp.threads != 1024 || !sp.all_q) return false;
-  if (sp.head_block != 4 && sp.head_block != 8) return false;
+  if (sp.head_block != 4 || (g.dtype != 1 && g.D > 64)) return false;  // spill-free builds
   if (sp.cpl != 1 || sp.stages != 1) return false;
   if (dp.unit != 16 || g.D > 128 || g.Dv != g.D) return false;
   size_t list_off, lds;
@@ -1193,8 +1200,8 @@ hipError_t launch_select_decode(const Geo& g, const SelectPlan& sp, const Decode
   if (g.D == 64)
     return bf ? launch_fused_r<true, 64>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st)
               : launch_fused_r<false, 64>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st);
-  return bf ? launch_fused_r<true, 128>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st)
-            : launch_fused_r<false, 128>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st);
+  if (!bf) return hipErrorInvalidValue;  // fp32 at D = 128: no fused build (fused_applies)
+  return launch_fused_r<true, 128>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st);
 }
 
 }  // namespace psd
