@@ -27,7 +27,9 @@
  * - All data pointers are DEVICE pointers owned by the caller. The library allocates
  *   nothing, keeps no state between calls and is reentrant. Workspaces are caller-owned
  *   device buffers of at least the size the matching *_workspace_bytes query returns;
- *   their contents need no initialisation and are scratch after the call.
+ *   their contents need no initialisation and are scratch after the call. The one
+ *   exception is psd_decode_step_noalloc, whose workspace is a static device array the
+ *   library holds on each GPU (see that call).
  * - Every call only enqueues work on `stream` (HIP stream, may be 0 / the null stream)
  *   and returns without synchronising. A workspace or output may be reused only in
  *   stream order.
@@ -59,7 +61,9 @@ typedef enum psd_status {
   PSD_ERR_UNSUPPORTED = -2, /* head dims / group size outside what the kernels build */
   PSD_ERR_WORKSPACE = -3,   /* workspace null or smaller than the query returned */
   PSD_ERR_CAPACITY = -4,    /* b_max (pages kept per unit) beyond the selection limit */
-  PSD_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch */
+  PSD_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
+  PSD_ERR_SCRATCH = -6      /* psd_decode_step_noalloc: the step needs more workspace than
+                               PSD_SCRATCH_BYTES */
 } psd_status;
 
 typedef enum psd_dtype { PSD_F32 = 0, PSD_BF16 = 1 } psd_dtype;
@@ -339,6 +343,30 @@ psd_status psd_select_pages_coverage(const psd_shape* shape, const void* q, cons
                                      float coverage, float scale, int32_t b_max,
                                      int32_t* sel_pages, int32_t* sel_count, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * psd_decode_step_noalloc - psd_decode_step without a caller workspace, for callers that
+ * cannot allocate device memory around the call (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).
+ *
+ * Writes exactly what psd_decode_step with the same arguments writes. Instead of a
+ * workspace argument it uses a static device array of PSD_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; its device address is looked up
+ * once per device on the first call with that device current. The call allocates and
+ * frees nothing. A step whose workspace (psd_select_sparse_decode_workspace_bytes) would
+ * exceed PSD_SCRATCH_BYTES returns PSD_ERR_SCRATCH before anything is launched. Every call
+ * on one GPU shares that GPU's array and leaves its contents behind: calls that overlap on
+ * one GPU (other streams, other host threads) race, so order them on one stream.
+ *
+ *   arguments   as for psd_decode_step, without workspace and workspace_bytes
+ */
+#define PSD_SCRATCH_BYTES ((size_t)64 << 20) /* 64 MiB per GPU */
+psd_status psd_decode_step_noalloc(const psd_shape* shape, const void* q, void* meta,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* budgets, int32_t b_max, float scale,
+                                   int32_t* sel_pages, int32_t* sel_count, float* out,
+                                   hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* psd_status_string(psd_status status);

@@ -12,7 +12,10 @@ c_i32, c_i64, c_size, c_void_p, c_float = (ctypes.c_int32, ctypes.c_int64, ctype
 PSD_F32, PSD_BF16 = 0, 1
 
 STATUS = {0: "PSD_OK", -1: "PSD_ERR_INVALID_ARG", -2: "PSD_ERR_UNSUPPORTED",
-          -3: "PSD_ERR_WORKSPACE", -4: "PSD_ERR_CAPACITY", -5: "PSD_ERR_LAUNCH"}
+          -3: "PSD_ERR_WORKSPACE", -4: "PSD_ERR_CAPACITY", -5: "PSD_ERR_LAUNCH",
+          -6: "PSD_ERR_SCRATCH"}
+
+SCRATCH_BYTES = 64 << 20  # PSD_SCRATCH_BYTES
 
 # Every entry point of include/psd.h: name -> (restype, argtypes).
 SIGNATURES = {
@@ -36,6 +39,9 @@ SIGNATURES = {
     "psd_decode_step": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_i32, c_float, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_size, c_void_p]),
+    "psd_decode_step_noalloc": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_i32, c_float, c_void_p,
+                                        c_void_p, c_void_p, c_void_p]),
     "psd_dense_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_float, c_void_p, c_void_p, c_size, c_void_p]),
     "psd_select_coverage_workspace_bytes": (c_size, [c_void_p]),

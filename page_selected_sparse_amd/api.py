@@ -155,6 +155,15 @@ def decode_step(shape: PsdShape, q, meta, k_cache, v_cache, block_table, seq_len
         _stream(stream)), "psd_decode_step")
 
 
+def decode_step_noalloc(shape: PsdShape, q, meta, k_cache, v_cache, block_table, seq_lens,
+                        budgets, b_max: int, scale: float, sel_pages, sel_count, out,
+                        stream=None):
+    _ok(_native.lib().psd_decode_step_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(meta), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), _ptr(seq_lens), _ptr(budgets), b_max, scale, _ptr(sel_pages),
+        _ptr(sel_count), _ptr(out), _stream(stream)), "psd_decode_step_noalloc")
+
+
 def dense_decode(shape: PsdShape, q, k_cache, v_cache, block_table, seq_lens, scale: float, out,
                  workspace, stream=None):
     _ok(_native.lib().psd_dense_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),

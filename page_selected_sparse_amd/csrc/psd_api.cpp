@@ -2,7 +2,10 @@
 // sizing and stream-ordered kernel launches. Nothing here allocates or synchronises.
 #include "psd.h"
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "psd_launch.h"
 
@@ -297,6 +300,8 @@ const char* psd_status_string(psd_status s) {
     case PSD_ERR_WORKSPACE: return "workspace missing or too small";
     case PSD_ERR_CAPACITY: return "selection capacity (b_max) exceeded";
     case PSD_ERR_LAUNCH: return "kernel launch failed";
+    case PSD_ERR_SCRATCH:
+      return "step needs more workspace than the library's static scratch (PSD_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -337,3 +342,59 @@ psd_status psd_select_pages_coverage(const psd_shape* shape, const void* q, cons
 
 }  // extern "C"
 
+
+// ---- the decode step without a caller workspace -------------------------------------------
+//
+// psd_decode_step_noalloc keeps its workspace in `scratch`, a file-scope device array of
+// PSD_SCRATCH_BYTES that every GPU the library runs on holds until the process ends. In
+// host code `scratch` names a host-side stand-in, not device memory: its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current) and only that
+// address is passed to kernels. The step's kernels need no zeroed workspace, so nothing is
+// cleared between calls.
+namespace {
+
+__device__ __align__(256) unsigned char scratch[PSD_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, or nullptr if the runtime cannot say.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+psd_status psd_decode_step_noalloc(const psd_shape* shape, const void* q, void* meta,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* budgets, int32_t b_max, float scale,
+                                   int32_t* sel_pages, int32_t* sel_count, float* out,
+                                   hipStream_t stream) {
+  // the size check comes first, before the device is touched
+  const size_t need = psd_select_sparse_decode_workspace_bytes(shape, b_max);
+  if (need == 0) {
+    psd::Geo g;
+    psd_status st = check_shape(shape, &g);
+    if (st != PSD_OK) return st;
+    return b_max < 2 ? PSD_ERR_INVALID_ARG : PSD_ERR_CAPACITY;
+  }
+  if (need > PSD_SCRATCH_BYTES) return PSD_ERR_SCRATCH;
+  void* ws = scratch_on_current_device();
+  if (!ws) return PSD_ERR_LAUNCH;
+  return step_common(shape, q, meta, k_cache, v_cache, block_table, seq_lens, budgets, b_max,
+                     scale, sel_pages, sel_count, out, ws, PSD_SCRATCH_BYTES, true, stream);
+}
+
+}  // extern "C"

@@ -142,6 +142,12 @@ class DecodeStep:
                         self.seq_lens, self.budgets, self.b_max, self.scale, self.sel_pages,
                         self.sel_count, self.out, self.ws_fused, stream)
 
+    def step_noalloc(self, stream=None):
+        """The same step with the library's static scratch instead of a workspace."""
+        api.decode_step_noalloc(self.shape, self.q, self.meta, self.k, self.v, self.block_table,
+                                self.seq_lens, self.budgets, self.b_max, self.scale,
+                                self.sel_pages, self.sel_count, self.out, stream)
+
     def step_separate(self, stream=None):
         """The same step as three calls: tail refresh, selection, attention."""
         self.refresh_tail(stream)

@@ -232,3 +232,26 @@ def test_coverage_selection_checks(native):
         big = _shape(native, **kw)
         assert lib.psd_select_coverage_workspace_bytes(ctypes.byref(big)) == 0
         assert call(ctypes.byref(big), f, f, f, f, 0.95, 0.1, 10, f, f, f, 1 << 40, None) == -2
+
+
+def test_noalloc_step_rejects_oversize_before_touching_the_device(native):
+    """psd_decode_step_noalloc checks the step's workspace against its static scratch
+    (PSD_SCRATCH_BYTES) first: a step that needs more returns PSD_ERR_SCRATCH without
+    launching or even looking the scratch up (no GPU needed)."""
+    lib = native.lib()
+    sh = _shape(native, batch=128, num_q_heads=128, num_kv_heads=1, head_dim=576,
+                head_dim_v=512, num_blocks=65536, max_pages_per_seq=4096,
+                k_block_stride=16 * 576, k_token_stride=576, k_head_stride=576,
+                v_block_stride=16 * 576, v_token_stride=576, v_head_stride=576)
+    assert lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(sh), 2048) > native.SCRATCH_BYTES
+    f = ctypes.c_void_p(16)
+    st = lib.psd_decode_step_noalloc(ctypes.byref(sh), f, f, f, f, f, f, f, 2048, 0.04, f, f, f,
+                                     None)
+    assert st == -6
+    assert b"scratch" in lib.psd_status_string(-6)
+    # shape errors come back as for the other calls
+    bad = _shape(native, page_size=32)
+    assert lib.psd_decode_step_noalloc(ctypes.byref(bad), f, f, f, f, f, f, f, 10, 0.1, f, f, f,
+                                       None) == -1
+    assert lib.psd_decode_step_noalloc(ctypes.byref(_shape(native)), f, f, f, f, f, f, f, 1,
+                                       0.1, f, f, f, None) == -1
