@@ -83,6 +83,7 @@ KERNEL_SOURCES = {"score_kernel": ("select.hip",), "merge_kernel": ("select.hip"
                   "prescore_kernel": ("prescore.hip",), "certify_kernel": ("prescore.hip",),
                   "meta_kernel": ("meta.hip",), "attn_kernel": ("attn.hip", "attn_core.h"),
                   "attn_latent_kernel": ("attn.hip", "attn_core.h"),
+                  "attn_latent_tile_kernel": ("attn.hip", "attn_core.h"),
                   "lse_merge_kernel": ("attn.hip", "attn_core.h"),
                   "page_mass_mfma_kernel": ("coverage.hip",),
                   "coverage_cut_kernel": ("coverage.hip",)}

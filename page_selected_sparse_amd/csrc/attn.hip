@@ -249,6 +249,295 @@ __global__ __launch_bounds__(64 * WAVES) void attn_latent_kernel(AttnArgs a) {
   if (grp == 0 && hvalid) a.pml[(ubase + head) * a.nsplit + split] = make_float2(m_run, l_run);
 }
 
+// ---- latent (MLA-style) attention, one 16-head tile per workgroup ----------------------
+//
+// The sparse latent step keeps about 200 pages per sequence for 128 query heads. Splitting
+// those pages over enough workgroups to fill the GPU, each attending every head, writes
+// one 128-head partial per split, as many bytes as the latent rows it read. Here a
+// workgroup takes one (sequence, split, 16-head tile); the tiles of one (sequence, split)
+// are mapped to one XCD, so that all but the first read of each latent row hit its L2.
+// The SUB waves of the workgroup take every SUB-th page of the split, and their states are
+// combined in LDS into one partial of 16 heads, so the partials shrink to (splits per
+// sequence) x 128 heads x (512 + 2) floats.
+//
+// Each wave streams its own pages through a private two-slot LDS ring with direct-to-LDS
+// loads (page i + 1 in flight while page i is computed; no registers held by loads in
+// flight), in the padded row layout of the staged kernel above, and reads its K and V
+// fragments from there: S^T = K Q^T (18 MFMAs 16x16x32 bf16, q of its 16 heads in
+// registers) and O += P V (32 MFMAs; V rows 4grp + j at piece 16w + r serve tiles 8w + cc).
+// Two fp32 values rounded to bf16 (nearest even) and packed, the first in bits 15:0.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+constexpr int kLatSub = 4;     // waves (page sub-splits) of a tile workgroup
+
+// Waits until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
+constexpr float kLazy = 8.f;   // reference-max slack of the tile kernel's softmax (base 2)
+
+__device__ __forceinline__ int latent_tile_count(const AttnArgs& a) {
+  return (a.G + 15) / 16;
+}
+
+// LDS of a tile workgroup: the rings (2 pages per wave) and, after the page loop, the
+// combine area acc [SUB][16][512] | (m, l) [SUB][16], which overlaps them.
+template <int SUB>
+constexpr size_t latent_tile_lds() {
+  constexpr size_t ring = (size_t)SUB * 2 * kLatStage * 16;
+  constexpr size_t comb = (size_t)SUB * 16 * 512 * 4 + SUB * 16 * 8;
+  return ring > comb ? ring : comb;
+}
+
+template <int SUB>
+__global__ __launch_bounds__(64 * SUB) __attribute__((amdgpu_waves_per_eu(1)))
+void attn_latent_tile_kernel(AttnArgs a) {
+  constexpr int DQK = 576, DV = 512, NQ = DQK / 32, NC = DV / 16;  // 18 and 32
+  extern __shared__ uint4 ring[];  // [SUB][2][kLatStage]; later the combine area
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS bases
+  const int r = lane & 15, grp = lane >> 4;
+  // Workgroup i runs on XCD i % 8: each XCD gets a contiguous range of work items, and
+  // the tiles of a (sequence, split) are consecutive items.
+  const int tiles = latent_tile_count(a);
+  const int N = gridDim.x, wi = blockIdx.x;
+  const int idx = (N % 8 == 0) ? (wi % 8) * (N / 8) + wi / 8 : wi;
+  const int tile = idx % tiles;
+  const int pair = idx / tiles;
+  const int split = pair % a.nsplit;
+  const int g = (pair / a.nsplit) % a.Hkv, s = pair / a.nsplit / a.Hkv;
+
+  const int L = a.lens[s];
+  const int n = ceil_div(L, kPage);
+  int count = a.sel ? min(a.cnt[s * a.Hkv + g], a.b_max) : n;
+  if (count < 0) count = 0;  // flagged unit: the merge writes NaN
+  const int p0 = split * a.pps;
+  if (p0 >= count) return;  // uniform over the workgroup, before any barrier
+  const int span = min(count - p0, a.pps);
+  const int mine = span > wave ? (span - wave + SUB - 1) / SUB : 0;  // <= 64 (plan)
+
+  // lane j holds this wave's j-th page: list entry p0 + wave + SUB j
+  int my_lp = 0, my_blk = 0;
+  if (lane < mine) {
+    const int e = p0 + wave + SUB * lane;
+    int lp = a.sel ? a.sel[(int64_t)(s * a.Hkv + g) * a.b_max + e] : e;
+    lp = min(max(lp, 0), n - 1);
+    my_lp = lp;
+    my_blk = min(max(a.bt[(int64_t)s * a.max_pages + lp], 0), a.num_blocks - 1);
+  }
+
+  // this wave's 16 heads' q as B fragments: head r, dims 32c + 8grp .. +8
+  const int head = tile * 16 + r;  // within the group
+  const bool hvalid = head < a.G;
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) +
+                       ((int64_t)s * a.Hq + g * a.G + (hvalid ? head : 0)) * DQK + 8 * grp;
+  uint4 qf[NQ];
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) qf[c] = hvalid ? load16(qb + 32 * c) : make_uint4(0, 0, 0, 0);
+
+  // Page i of this wave into ring slot i & 1: load instruction `ins` fills slots
+  // 64 ins + lane = (row, piece) of the padded layout (the pad and tail slots fetch piece
+  // 0 of row 15, never read). Past the wave's last page it repeats the last page, so that
+  // exactly one page's kLatLoads loads are in flight behind the page being computed.
+  uint4* myring = ring + wave * 2 * kLatStage;
+  const unsigned char* kb = static_cast<const unsigned char*>(a.k);
+  const uint32_t kts_bytes = (uint32_t)(a.kts * 2);  // a page's rows span < 32 KB
+  // byte offsets within a page of this lane's piece in each staging load (loop-invariant)
+  uint32_t soff[kLatLoads];
+#pragma unroll
+  for (int ins = 0; ins < kLatLoads; ++ins) {
+    const int at = ins * 64 + lane;
+    int row = at / kLatRowPieces, piece = at - row * kLatRowPieces;
+    if (row >= 16) {
+      row = 15;
+      piece = 0;
+    }
+    if (piece == kLatRowPieces - 1) piece = 0;
+    soff[ins] = (uint32_t)row * kts_bytes + (uint32_t)piece * 16u;
+  }
+  auto page_base = [&](int i) {
+    const int blk = __builtin_amdgcn_readlane(my_blk, min(i, mine - 1));
+    return kb + ((int64_t)blk * a.kbs + (int64_t)g * a.khs) * 2;
+  };
+  auto issue = [&](int i) {
+    const unsigned char* pbase = page_base(i);
+    uint4* slot = myring + (i & 1) * kLatStage;
+#pragma unroll
+    for (int ins = 0; ins < kLatLoads; ++ins)
+      __builtin_amdgcn_global_load_lds(pbase + soff[ins],
+                                       (__attribute__((address_space(3))) void*)(slot + ins * 64),
+                                       16, 0, 0);
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float4v acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t rbase = (uint32_t)(uintptr_t)myring;
+  // S^T = K Q^T for page i, once its loads have landed: K row r, dims 32c + 8grp
+  // (piece 4c + grp), scaled to base-2 exponents and masked past the sequence
+  auto scores = [&](int i, float (&z)[4]) {
+    issue(i + 1);
+    wait_vm_n<kLatLoads>();  // page i has landed: only page i + 1's loads are in flight
+    const uint32_t st = rbase + (uint32_t)((i & 1) * kLatStage * 16);
+    const int valid = min(kPage, L - __builtin_amdgcn_readlane(my_lp, i) * kPage);
+    // three independent accumulation chains over the 18 steps, summed at the end
+    float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0;
+    const uint32_t krow = st + (uint32_t)(r * kLatRowPieces + grp) * 16;
+#pragma unroll
+    for (int c0 = 0; c0 < NQ; c0 += 6) {
+      uint4 k[6];
+      lds_read2(krow + 64 * c0, krow + 64 * (c0 + 1), k[0], k[1]);
+      lds_read4(krow + 64 * (c0 + 2), krow + 64 * (c0 + 3), krow + 64 * (c0 + 4),
+                krow + 64 * (c0 + 5), k[2], k[3], k[4], k[5]);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[0]), as_bf16x8(qf[c0]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[1]), as_bf16x8(qf[c0 + 1]), s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[2]), as_bf16x8(qf[c0 + 2]), s2, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[3]), as_bf16x8(qf[c0 + 3]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[4]), as_bf16x8(qf[c0 + 4]), s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[5]), as_bf16x8(qf[c0 + 5]), s2, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      z[j] = 4 * grp + j < valid ? (s0[j] + s1[j] + s2[j]) * a.sl2 : -INFINITY;
+  };
+  // the page's weights against the current reference, then O += P V (V rows 4grp + j at
+  // piece 16w + r)
+  auto accumulate = [&](int i, const float (&z)[4]) {
+    const uint32_t st = rbase + (uint32_t)((i & 1) * kLatStage * 16);
+    const int valid = min(kPage, L - __builtin_amdgcn_readlane(my_lp, i) * kPage);
+    const bool live = m_run != -INFINITY;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = live ? exp2f(z[j] - m_run) : 0.f;
+    l_run += wave_sum4(p[0] + p[1] + p[2] + p[3]);
+    // P as bf16 hi + lo parts (hardware round to nearest even, two values per convert)
+    const uint32_t h01 = pk_bf16(p[0], p[1]), h23 = pk_bf16(p[2], p[3]);
+    const uint32_t l01 = pk_bf16(p[0] - bf_lo(h01), p[1] - bf_hi(h01));
+    const uint32_t l23 = pk_bf16(p[2] - bf_lo(h23), p[3] - bf_hi(h23));
+    const bf16x8 PP = as_bf16x8(make_uint4(h01, h23, l01, l23));
+    const uint32_t vrow = st + (uint32_t)((4 * grp) * kLatRowPieces + r) * 16;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint4 x[4];
+      lds_read4(vrow + 16 * (0 * kLatRowPieces + 16 * w), vrow + 16 * (1 * kLatRowPieces + 16 * w),
+                vrow + 16 * (2 * kLatRowPieces + 16 * w), vrow + 16 * (3 * kLatRowPieces + 16 * w),
+                x[0], x[1], x[2], x[3]);
+      uint32_t vh[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (4 * grp + j >= valid) x[j] = make_uint4(0u, 0u, 0u, 0u);  // unwritten slots
+        vh[j][0] = x[j].x; vh[j][1] = x[j].y; vh[j][2] = x[j].z; vh[j][3] = x[j].w;
+      }
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        // column cc of the four rows: half cc & 1 of word cc / 2, packed by byte permutes
+        const int wd = cc >> 1;
+        const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t v01 = __builtin_amdgcn_perm(vh[1][wd], vh[0][wd], sel);
+        const uint32_t v23 = __builtin_amdgcn_perm(vh[3][wd], vh[2][wd], sel);
+        acc[8 * w + cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            PP, as_bf16x8(make_uint4(v01, v23, v01, v23)), acc[8 * w + cc], 0, 0, 0);
+      }
+    }
+  };
+
+  // Online softmax with a lazily moved reference: a head's weights are taken relative to
+  // a reference m_run that moves (and the accumulators with it) only when the page max
+  // exceeds it by more than kLazy (base-2 units), so every weight stays below 2^kLazy,
+  // far inside fp32, and the weights and the normaliser share one reference. The move is
+  // the outer step below; the inner loop never touches the accumulators outside the
+  // matrix cores (a conditional rescale inside it made the compiler copy all 128
+  // accumulators out of and back into the AGPRs on every page).
+  if (mine > 0) {
+    issue(0);
+  }
+  int i = 0;
+  float z[4];
+  bool have = false;  // z holds page i's scores already
+  while (i < mine) {
+    if (!have) scores(i, z);
+    {
+      const float m_loc = wave_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      const float m_new = m_loc > m_run + kLazy ? m_loc : m_run;  // -inf + kLazy is -inf
+      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      float al[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 4 * grp + j, 64);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[c][j] *= al[j];
+    }
+    accumulate(i, z);
+    have = false;
+    for (++i; i < mine; ++i) {
+      scores(i, z);
+      const float m_loc = wave_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      if (__ballot(m_loc > m_run + kLazy)) {
+        have = true;
+        break;
+      }
+      accumulate(i, z);
+    }
+  }
+
+  // ---- the SUB waves' states -> one partial of 16 heads for this split -----------------
+  // acc rows are heads 4grp + j; tile 8w + cc column r is d = 128w + 8r + cc. The combine
+  // area overlaps the rings: the trailing repeat of the last page must land, and every
+  // wave must be past its pages, first.
+  wait_vm_upto20(0);
+  __syncthreads();
+  float* tsh = reinterpret_cast<float*>(ring);
+  float2* tml = reinterpret_cast<float2*>(tsh + SUB * 16 * DV);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float* dst = tsh + (wave * 16 + 4 * grp + j) * DV + 8 * r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      *reinterpret_cast<float4*>(dst + 128 * w) =
+          make_float4(acc[8 * w][j], acc[8 * w + 1][j], acc[8 * w + 2][j], acc[8 * w + 3][j]);
+      *reinterpret_cast<float4*>(dst + 128 * w + 4) =
+          make_float4(acc[8 * w + 4][j], acc[8 * w + 5][j], acc[8 * w + 6][j], acc[8 * w + 7][j]);
+    }
+  }
+  if (grp == 0) tml[wave * 16 + r] = make_float2(m_run, l_run);
+  __syncthreads();
+  const int64_t ubase = (int64_t)s * a.Hq + g * a.G;
+  for (int t = threadIdx.x; t < 16 * (DV / 4); t += 64 * SUB) {
+    const int h = t / (DV / 4), d4 = t - h * (DV / 4);
+    if (tile * 16 + h >= a.G) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < SUB; ++w) M = fmaxf(M, tml[w * 16 + h].x);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < SUB; ++w) {
+      const float2 ml = tml[w * 16 + h];
+      const float wt = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);  // a wave without pages
+      const float4 x = *reinterpret_cast<const float4*>(tsh + (w * 16 + h) * DV + 4 * d4);
+      o.x += x.x * wt;
+      o.y += x.y * wt;
+      o.z += x.z * wt;
+      o.w += x.w * wt;
+      l += ml.y * wt;
+    }
+    const int64_t row = (ubase + tile * 16 + h) * a.nsplit + split;
+    reinterpret_cast<float4*>(a.pacc + row * DV)[d4] = o;
+    if (d4 == 0) a.pml[row] = make_float2(M, l);
+  }
+}
+
 template <int NT>
 __device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) {
   constexpr int NW = NT / 64;
@@ -374,6 +663,17 @@ hipError_t launch_unit(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st)
   return hipGetLastError();
 }
 
+hipError_t launch_latent_tiles(const AttnArgs& a, int workgroups, hipStream_t st) {
+  constexpr size_t lds = latent_tile_lds<kLatSub>();
+  static_assert(lds <= 160 * 1024, "LDS of a tile workgroup");
+  auto kern = &attn_latent_tile_kernel<kLatSub>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(workgroups), dim3(64 * kLatSub), lds, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_latent(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) {
   switch (waves) {
     case 1: hipLaunchKernelGGL(attn_latent_kernel<1>, grid, dim3(64), 0, st, a); break;
@@ -395,6 +695,7 @@ bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* p
   p->waves = (g.G + 15) / 16;
   const int64_t units = (int64_t)g.B * g.Hkv;
   p->unit = 0;
+  p->latent_tiles = 0;
   if (g.G <= 16 && g.D <= 128 && units >= PSD_ATTN_UNIT_MIN && (!dense || PSD_ATTN_UNIT_DENSE)) {
     // one workgroup per unit, its waves the splits, combined in LDS: no partials. fp32 at
     // D = 128 takes 8 waves: its 16-wave build spills at the 128-VGPR budget and was
@@ -405,6 +706,23 @@ bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* p
     p->nsplit = 1;
     p->off_ml = 0;
     p->bytes = 256;
+    return true;
+  }
+  if (!dense && g.D == 576 && g.Dv == 512 && g.dtype == 1) {
+    // latent tile plan: (sequence, split, 16-head tile) workgroups of kLatSub waves, about
+    // one per CU; each wave takes at most 64 of its split's pages
+    const int64_t tiles = (g.G + 15) / 16;
+    int64_t ns = (kComputeUnits + units * tiles - 1) / (units * tiles);
+    ns = ns < 1 ? 1 : ns;
+    const int64_t cap = 64 * kLatSub;
+    if ((max_pages_attended + ns - 1) / ns > cap) ns = (max_pages_attended + cap - 1) / cap;
+    if (ns > max_pages_attended) ns = max_pages_attended;
+    p->latent_tiles = (int)tiles;
+    p->nsplit = (int)ns;
+    p->pps = (int)((max_pages_attended + ns - 1) / ns);
+    const size_t parts = (size_t)g.B * g.Hq * p->nsplit;
+    p->off_ml = (parts * g.Dv * sizeof(float) + 255) / 256 * 256;
+    p->bytes = p->off_ml + parts * sizeof(float2) + 256;
     return true;
   }
   // Aim for PSD_ATTN_TARGET single-wave workgroups (fewer, larger ones for many-head
@@ -446,6 +764,8 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
   else if (g.D == 128)
     e = bf ? launch_attn<true, 128, 128>(a, grid, p.waves, st)
            : launch_attn<false, 128, 128>(a, grid, p.waves, st);
+  else if (p.latent_tiles && bf && k == v && g.kbs == g.vbs && g.kts == g.vts && g.khs == g.vhs)
+    e = launch_latent_tiles(a, (int)((int64_t)g.B * g.Hkv * p.nsplit * p.latent_tiles), st);
   else if (bf && k == v && g.kbs == g.vbs && g.kts == g.vts && g.khs == g.vhs)
     e = launch_latent(a, grid, p.waves, st);
   else

@@ -82,6 +82,7 @@ struct DecodePlan {
   int nsplit;  // splits per unit
   int waves;   // waves per workgroup = ceil(G / 16) head tiles
   int unit;    // > 0: one workgroup of `unit` waves per unit, combined in LDS (no merge)
+  int latent_tiles;  // > 0: latent sparse plan, one workgroup per (unit, split, 16-head tile)
   size_t off_ml, bytes;
 };
 // dense: every page of each sequence is attended (splits sized for long page walks).

@@ -34,6 +34,9 @@ CASES = [
                      len_range=(3000, 9000), budget_percent=5, max_len=9008),
     synth.small_spec("noalloc_certified", batch=2, num_q_heads=64, num_kv_heads=2,
                      seq_lens=(9000, 3000), budget_percent=5, max_len=9008),
+    synth.small_spec("noalloc_latent", batch=4, num_q_heads=128, num_kv_heads=1, head_dim=576,
+                     head_dim_v=512, latent=True, seq_lens=(16 * 700 - 5, 1500, 333, 16 * 300),
+                     budget_percent=5, max_len=16 * 700),
 ]
 
 
