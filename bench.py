@@ -6,7 +6,9 @@ workgroup refreshes, ranks and attends each unit. The default workload is the
 ragged batch: B=32 sequences of 16K..32K tokens, 32 query / 8 KV heads, D=128, bf16,
 5% page budget (sink and tail included). Inputs are resident in HBM before timing; steps
 rotate over --rotate device copies of (cache, statistics, q) so that consecutive steps
-do not hit in the last-level cache.
+do not hit in the last-level cache. The other legs run before the W warmup steps and the
+K measured ones, so that the measured region runs at steady clocks (a 20-step region
+right after the GPU wakes runs about 8 % slower).
 
 Prints one JSON line. Besides the contract fields it carries:
   roofline      achieved algorithmic GB/s of the dominant kernel against 8 TB/s
@@ -411,7 +413,12 @@ def main():
     torch.cuda.synchronize()
     R = len(steps)
 
-    def timed(fn, iters):
+    def timed(fn, iters, prime=True):
+        """Average ms of fn over iters calls on the rotated copies (HIP events on torch's
+        current stream); with `prime`, one untimed call per copy first."""
+        if prime:
+            for st in steps:
+                fn(st)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -421,56 +428,14 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / iters  # ms
 
-    for i in range(args.warmup):
-        steps[i % R].step()
-        if not args.no_dense:
-            steps[i % R].dense()
-    torch.cuda.synchronize()
-
-    # The measured region: K whole steps, rotating copies.
-    ms_step = timed(lambda st: st.step(), args.steps)
-
-    graph = None
-    if not args.no_graph:
-        # The same step replayed from a HIP graph (one captured step per rotated copy),
-        # checked bit for bit against the eager outputs.
-        for st in steps:
-            st.step()
-        torch.cuda.synchronize()
-        eager_out = [st.out.clone() for st in steps]
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for st in steps:
-                st.step()
-        replays = max(1, args.steps // R)
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        same = all(torch.equal(st.out, o) for st, o in zip(steps, eager_out))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(replays):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        same = same and all(torch.equal(st.out, o) for st, o in zip(steps, eager_out))
-        ms_graph = e0.elapsed_time(e1) / (replays * R)
-        graph = {"ms_per_step": round(ms_graph, 5), "steps_per_s": round(1000.0 / ms_graph, 3),
-                 "matches_eager": bool(same)}
-        del g
-
-    # Per-call averages, each call timed in its own loop with events on the stream the
-    # kernels are launched on (torch's current stream). page_meta_update, select_score and
-    # select_merge are single kernels (select_merge launches none when each scoring
-    # workgroup ranked a whole unit); sparse_decode is the attention kernel, plus the split
-    # merge unless one workgroup attends each unit; decode_step and select_sparse_decode are
-    # one kernel each where one_call_kernel() names it, else the launches of their calls.
-    calls = {"decode_step": timed(lambda st: st.step(), args.steps),
-             "page_meta_update": timed(lambda st: st.refresh_tail(), args.steps),
-             "select_sparse_decode": timed(lambda st: st.select_sparse(), args.steps),
-             "select_score": timed(lambda st: st.select_score(), args.steps),
-             "select_merge": timed(lambda st: st.select_merge(), args.steps),
-             "sparse_decode": timed(lambda st: st.sparse(), args.steps)}
+    # The other legs run before the measured region, the other workloads first, so that
+    # the measured region runs at steady clocks on inputs the legs just before it have
+    # touched (a 20-step region right after the GPU wakes runs about 8 % slower).
+    launch_fl = launch_floor(max(100, args.steps))
+    configs = None
+    if not args.no_configs:
+        configs = [measure_config(name, args, dev) for name in synth.CONFIG_ORDER
+                   if name != w.spec.name]
     ms_separate = timed(lambda st: st.step_separate(), args.steps)
     dense_ms = timed(lambda st: st.dense(), max(10, args.steps // 4)) if not args.no_dense else None
 
@@ -526,6 +491,54 @@ def main():
                "traffic": {k: measured_traffic(k, w.spec.name)
                            for k in ("page_mass_mfma_kernel", "coverage_cut_kernel")}}
         del csteps
+
+    # Per-call averages, each call timed in its own loop with events on the stream the
+    # kernels are launched on (torch's current stream). page_meta_update, select_score and
+    # select_merge are single kernels (select_merge launches none when each scoring
+    # workgroup ranked a whole unit); sparse_decode is the attention kernel, plus the split
+    # merge unless one workgroup attends each unit; decode_step and select_sparse_decode are
+    # one kernel each where one_call_kernel() names it, else the launches of their calls.
+    calls = {"page_meta_update": timed(lambda st: st.refresh_tail(), args.steps),
+             "select_sparse_decode": timed(lambda st: st.select_sparse(), args.steps),
+             "select_score": timed(lambda st: st.select_score(), args.steps),
+             "select_merge": timed(lambda st: st.select_merge(), args.steps),
+             "sparse_decode": timed(lambda st: st.sparse(), args.steps)}
+    # W untimed warmup steps, then the measured region: K whole steps on the rotated
+    # copies; then the same call in its own K-step loop for the roofline.
+    for i in range(args.warmup):
+        steps[i % R].step()
+    torch.cuda.synchronize()
+    ms_step = timed(lambda st: st.step(), args.steps, prime=False)
+    calls["decode_step"] = timed(lambda st: st.step(), args.steps, prime=False)
+
+    graph = None
+    if not args.no_graph:
+        # The same step replayed from a HIP graph (one captured step per rotated copy),
+        # checked bit for bit against the eager outputs.
+        for st in steps:
+            st.step()
+        torch.cuda.synchronize()
+        eager_out = [st.out.clone() for st in steps]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for st in steps:
+                st.step()
+        replays = max(1, args.steps // R)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(st.out, o) for st, o in zip(steps, eager_out))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        same = same and all(torch.equal(st.out, o) for st, o in zip(steps, eager_out))
+        ms_graph = e0.elapsed_time(e1) / (replays * R)
+        graph = {"ms_per_step": round(ms_graph, 5), "steps_per_s": round(1000.0 / ms_graph, 3),
+                 "matches_eager": bool(same)}
+        del g
 
     if args.calibrate_copy:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -605,10 +618,9 @@ def main():
         result["dense"] = {"ms": round(dense_ms, 5),
                            "gbs": round(ab["dense_decode"] / (dense_ms * 1e-3) / 1e9, 1),
                            "step_speedup_vs_dense": round(dense_ms / ms_step, 3)}
-    result["launch_floor"] = launch_floor(max(100, args.steps))
-    if not args.no_configs:
-        result["configs"] = [measure_config(name, args, dev) for name in synth.CONFIG_ORDER
-                             if name != w.spec.name]
+    result["launch_floor"] = launch_fl
+    if configs is not None:
+        result["configs"] = configs
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
