@@ -754,6 +754,12 @@ __device__ __forceinline__ void score_body(const SelArgs& a, int c, int g, int s
     uint64_t P, M;
     int need;
     block_kth_largest<NT>(keys, cnt, kp, sc, P, M, need, true);
+    // the list's sink and tail entries (every staged load has landed: the ranking's
+    // barriers follow each wave's wait for its loads)
+    if (list && tid == 0) {
+      list[0] = 0;
+      list[kp + 1] = n - 1;
+    }
     block_emit_top<NT>(keys, cnt, P, M, need, sc, [&](int pos, int i) {
       row[1 + pos] = 1 + i;
       if (list) list[1 + pos] = 1 + i;
@@ -907,9 +913,10 @@ hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStre
 // writes the selection row and count the same way), keeps the page list in LDS at
 // `list_off`, and then attends over it as the whole-unit attention kernel does, its 16
 // waves being the splits. The list lies past both the ranking keys and the attention's
-// closing combine area, inside the statistics staging area: its winners are written by
-// the emission, which follows the last staged load, and its sink, tail or identity
-// entries after the barrier that follows the scoring.
+// closing combine area, inside the statistics staging area: a ranking unit's entries
+// (winners, sink and tail) are written by the emission, which follows the last staged
+// load; a unit that needs no ranking writes its entries after the barrier that follows
+// the scoring.
 //
 // With `meta_w` (decode step) the workgroup also refreshes the statistics of its
 // sequence's tail page for its KV head, as the statistics kernel does for the tail page.
@@ -937,8 +944,14 @@ void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, void* meta_w, int6
 #endif
   score_body<BF16, D, HB, true, 1024, 1, 1>(a, 0, g, s, list);
   __syncthreads();  // every staged load has landed; the ranking keys are no longer read
-  const int count = write_list_header<1024>(list, unit_info(a, s), a.b_max);
-  __syncthreads();
+  // A ranking unit's list is complete (its emission wrote the sink and tail too); a unit
+  // that needs no ranking writes its list now.
+  const UnitInfo ui = unit_info(a, s);
+  int count = ui.b;
+  if (ui.trivial) {
+    count = write_list_header<1024>(list, ui, a.b_max);
+    __syncthreads();
+  }
   auto refresh_tail = [&]() {
     if constexpr (REFRESH) {
       if ((threadIdx.x >> 6) == 15)  // all 16 rows at once: the attention's registers are free
