@@ -30,6 +30,10 @@ Prints one JSON line. Besides the contract fields it carries:
   coverage_select  the adaptive coverage selection (--coverage, default 0.95) on the
                 same inputs: selection alone and selection plus sparse attention, with
                 the algorithmic GB/s of the dense K read the page masses need
+  value_tier    V in pinned host memory with a resident hot buffer of 1.5x one step's
+                kept slices, over 8 steps of drifting queries: hit rate, host-link bytes
+                per step (against reading every kept V row from host memory) and the
+                step time (--no-tier skips it)
 """
 from __future__ import annotations
 
@@ -316,6 +320,69 @@ def launch_floor(iters: int) -> dict:
             "kernel": "torch.cuda._sleep(0), back to back on one stream"}
 
 
+def value_tier_leg(w, base, dev, steps: int = 8) -> dict:
+    """The value tier over consecutive decode steps: V in pinned host memory, a resident hot
+    buffer of 1.5x one step's kept (block, KV head) slices, queries on a random walk (about
+    5 % per step). Per step: hits, slices copied over the host link and their bytes, the
+    step time (selection, staging, attention) against the same step reading every kept V
+    row from host memory (zero copy)."""
+    import torch
+
+    from page_selected_sparse_amd import DecodeStep
+
+    sp = w.spec
+    st = DecodeStep(base.q.clone(), base.cache, base.block_table, base.seq_lens, base.budgets,
+                    sp.head_dim_v, sp.latent, b_max=base.b_max, v_host=True)
+    st.build_meta()
+    st.select()
+    kept0 = int(st.sel_count.clamp(min=0).sum())
+    slots = int(1.5 * kept0)
+    st.enable_tier(slots)
+    es = 2 if sp.dtype == "bf16" else 4
+    slice_bytes = 16 * sp.head_dim_v * es
+    gen = torch.Generator(device=dev).manual_seed(11)
+    q = st.q.float()
+    rows = []
+
+    def ev_time(fn):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    for t in range(steps):
+        if t:
+            q = q + 0.05 * torch.randn(q.shape, generator=gen, device=dev)
+        st.q.copy_(q.to(st.q.dtype))
+        ms_tier = ev_time(lambda: (st.select(), st.tier_stage(), st.sparse_tiered()))
+        c = st.tier_counts()
+        kept = int(st.sel_count.clamp(min=0).sum())
+        ms_zero = ev_time(lambda: (st.select(), st.sparse()))
+        rows.append({"step": t, "kept_slices": kept, "hits": c["hits"],
+                     "copied": c["copied"], "from_host": c["from_host"],
+                     "link_bytes": c["copied"] * slice_bytes + c["from_host"] * slice_bytes,
+                     "zero_copy_link_bytes": kept * slice_bytes,
+                     "ms": round(ms_tier, 4), "zero_copy_ms": round(ms_zero, 4)})
+    warm = rows[1:]
+    res = {"slots": slots, "slice_bytes": slice_bytes,
+           "hot_buffer_bytes": slots * slice_bytes,
+           "v_pool_bytes": int(st.v.numel() * st.v.element_size()),
+           "hit_rate": round(sum(r["hits"] for r in warm) / max(1, sum(r["kept_slices"] for r in warm)), 4),
+           "link_bytes_per_step": int(np.mean([r["link_bytes"] for r in warm])),
+           "zero_copy_link_bytes_per_step": int(np.mean([r["zero_copy_link_bytes"] for r in warm])),
+           "ms_per_step": round(float(np.mean([r["ms"] for r in warm])), 4),
+           "zero_copy_ms_per_step": round(float(np.mean([r["zero_copy_ms"] for r in warm])), 4),
+           "first_step": rows[0], "steps": rows,
+           "note": "queries on a random walk of about 5 % per step; steps after the first "
+                   "averaged; each step timed alone (selection, staging, attention)"}
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_config(name: str, args, dev) -> dict:
     """One decode step (psd_decode_step) and the dense decode (psd_dense_decode) of
     another measured workload, on rotated resident copies as for the headline."""
@@ -370,6 +437,8 @@ def main():
                     help="target mass of the adaptive coverage selection leg (0: skip it)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the step / dense pairs of the other measured workloads")
+    ap.add_argument("--no-tier", action="store_true",
+                    help="skip the value-tier leg (V in pinned host memory, hot buffer)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -614,6 +683,8 @@ def main():
         result["coverage_select"] = cov
     if graph is not None:
         result["graph_replay"] = graph
+    if not args.no_tier and not w.spec.latent and w.spec.head_dim == w.spec.head_dim_v:
+        result["value_tier"] = value_tier_leg(w, steps[0], dev)
     if dense_ms is not None:
         result["dense"] = {"ms": round(dense_ms, 5),
                            "gbs": round(ab["dense_decode"] / (dense_ms * 1e-3) / 1e9, 1),

@@ -293,6 +293,57 @@ psd_status psd_decode_step(const psd_shape* shape, const void* q, void* meta, co
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Value tier with a resident hot buffer (AMASS page, "What is in the box", item 2: the
+ * DRAM value tier keeps a bounded resident hot buffer plus a staging pool in VRAM; LOCKS
+ * README, "How it works", the optional DRAM tier keeps only the pages called each step
+ * resident). V lives in pinned host memory (v_host: its device address, the V layout of
+ * the shape); a device buffer `hot` of `slots` slices, each the 16 token rows of one
+ * (block, KV head) ([slots][16][D_v] elements of dtype), keeps the slices that steps
+ * call. Each step:
+ *
+ *   psd_value_tier_stage     - for every kept page of every unit (sel_pages / sel_count
+ *                              of psd_select_pages), the slot of its V slice: a slice
+ *                              already resident is a hit; a missed slice gets a slot that
+ *                              this step does not use (evicting what it held) and its 16
+ *                              rows are copied from v_host over the host link. When the
+ *                              slots run out, the remaining entries read V from v_host.
+ *                              Writes vslot[s][g][e] (slot of entry e, -1: from host) and
+ *                              stats[0..3] = hits, misses (entries), slices copied,
+ *                              entries read from host (device, uint64).
+ *   psd_sparse_decode_tiered - psd_sparse_decode with each entry's V read from its slot
+ *                              (or from v_host), the same arithmetic: the same bits as
+ *                              psd_sparse_decode over the same V.
+ *
+ *   state       device, psd_value_tier_state_bytes: the page map and the slots' owners
+ *               and last steps, kept between steps; psd_value_tier_reset empties it
+ *               (call it once before the first stage, and after any change of v_host's
+ *               contents that the hot buffer holds).
+ *   step        any value that differs from the previous stage call's since the reset
+ *               (a step counter); the slots this call uses are stamped with it.
+ *   workspace   psd_value_tier_workspace_bytes(shape, b_max, slots) (scratch).
+ * GQA shapes only: D == D_v in {64, 128}, up to 16 query heads per KV head (otherwise
+ * PSD_ERR_UNSUPPORTED). The stage enqueues four launches; stats are final once they
+ * have run. Calls that share a state or a hot buffer run in stream order.
+ */
+size_t psd_value_tier_state_bytes(const psd_shape* shape, int32_t slots);
+size_t psd_value_tier_workspace_bytes(const psd_shape* shape, int32_t b_max, int32_t slots);
+psd_status psd_value_tier_reset(const psd_shape* shape, int32_t slots, void* state,
+                                hipStream_t stream);
+psd_status psd_value_tier_stage(const psd_shape* shape, const void* v_host, void* hot,
+                                void* state, int32_t slots, int32_t step,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* sel_pages, const int32_t* sel_count,
+                                int32_t b_max, int32_t* vslot, uint64_t* stats, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+/* workspace: psd_decode_workspace_bytes(shape, b_max), as for psd_sparse_decode. */
+psd_status psd_sparse_decode_tiered(const psd_shape* shape, const void* q, const void* k_cache,
+                                    const void* v_host, const void* hot, const int32_t* vslot,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* sel_pages, const int32_t* sel_count,
+                                    int32_t b_max, float scale, float* out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
  * psd_dense_decode - the same attention over every page of each sequence (baseline).
  *
  * workspace >= psd_decode_workspace_bytes(shape, shape->max_pages_per_seq) bytes.

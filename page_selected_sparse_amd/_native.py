@@ -50,6 +50,15 @@ SIGNATURES = {
                                           c_size, c_void_p]),
     "psd_status_string": (ctypes.c_char_p, [c_i32]),
     "psd_version": (c_i32, []),
+    "psd_value_tier_state_bytes": (c_size, [c_void_p, c_i32]),
+    "psd_value_tier_workspace_bytes": (c_size, [c_void_p, c_i32, c_i32]),
+    "psd_value_tier_reset": (c_i32, [c_void_p, c_i32, c_void_p, c_void_p]),
+    "psd_value_tier_stage": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_i32,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_void_p,
+                                     c_void_p, c_void_p, c_size, c_void_p]),
+    "psd_sparse_decode_tiered": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_i32, c_float, c_void_p, c_void_p, c_size, c_void_p]),
 }
 
 

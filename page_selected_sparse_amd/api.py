@@ -132,6 +132,42 @@ def sparse_decode(shape: PsdShape, q, k_cache, v_cache, block_table, seq_lens, s
                                         _stream(stream)), "psd_sparse_decode")
 
 
+def value_tier_state_bytes(shape: PsdShape, slots: int) -> int:
+    return int(_native.lib().psd_value_tier_state_bytes(ctypes.byref(shape), slots))
+
+
+def value_tier_workspace_bytes(shape: PsdShape, b_max: int, slots: int) -> int:
+    return int(_native.lib().psd_value_tier_workspace_bytes(ctypes.byref(shape), b_max, slots))
+
+
+def value_tier_reset(shape: PsdShape, slots: int, state, stream=None):
+    _ok(_native.lib().psd_value_tier_reset(ctypes.byref(shape), slots, _ptr(state),
+                                           _stream(stream)), "psd_value_tier_reset")
+
+
+def value_tier_stage(shape: PsdShape, v_host, hot, state, slots: int, step: int, block_table,
+                     seq_lens, sel_pages, sel_count, b_max: int, vslot, stats, workspace,
+                     stream=None):
+    _ok(_native.lib().psd_value_tier_stage(ctypes.byref(shape), _ptr(v_host), _ptr(hot),
+                                           _ptr(state), slots, step, _ptr(block_table),
+                                           _ptr(seq_lens), _ptr(sel_pages), _ptr(sel_count),
+                                           b_max, _ptr(vslot), _ptr(stats), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(stream)), "psd_value_tier_stage")
+
+
+def sparse_decode_tiered(shape: PsdShape, q, k_cache, v_host, hot, vslot, block_table, seq_lens,
+                         sel_pages, sel_count, b_max: int, scale: float, out, workspace,
+                         stream=None):
+    _ok(_native.lib().psd_sparse_decode_tiered(ctypes.byref(shape), _ptr(q), _ptr(k_cache),
+                                               _ptr(v_host), _ptr(hot), _ptr(vslot),
+                                               _ptr(block_table), _ptr(seq_lens), _ptr(sel_pages),
+                                               _ptr(sel_count), b_max, scale, _ptr(out),
+                                               _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(),
+                                               _stream(stream)), "psd_sparse_decode_tiered")
+
+
 def select_sparse_decode_workspace_bytes(shape: PsdShape, b_max: int) -> int:
     return int(_native.lib().psd_select_sparse_decode_workspace_bytes(ctypes.byref(shape), b_max))
 

@@ -638,11 +638,16 @@ __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a) {
     reinterpret_cast<float4*>(out)[tid] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }
 
-template <bool BF16, int DQK, int DV>
+template <bool BF16, int DQK, int DV, bool TIER = false>
 hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) {
   // occupancy target per variant: the smallest register budget that does not spill
   constexpr int W1 = DQK > 128 ? 1 : (BF16 ? PSD_ATTN_W1 : 2);
   constexpr int W2 = DQK > 128 ? 1 : 2;
+  if constexpr (TIER) {  // value tier: groups of up to 16 heads (one wave)
+    if (waves != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 1, W1, 0, true>), grid, dim3(64), 0, st, a);
+    return hipGetLastError();
+  }
   if (waves == 1) {
     hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 1, W1>), grid, dim3(64), 0, st, a);
   } else if (waves == 2) {
@@ -653,9 +658,9 @@ hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) 
   return hipGetLastError();
 }
 
-template <bool BF16, int D, int NW = PSD_ATTN_UNIT_WAVES>
+template <bool BF16, int D, int NW = PSD_ATTN_UNIT_WAVES, bool TIER = false>
 hipError_t launch_unit(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  auto kern = &attn_kernel<BF16, D, D, 1, (NW + 3) / 4, NW>;
+  auto kern = &attn_kernel<BF16, D, D, 1, (NW + 3) / 4, NW, TIER>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -684,6 +689,32 @@ hipError_t launch_latent(const AttnArgs& a, dim3 grid, int waves, hipStream_t st
     case 6: hipLaunchKernelGGL(attn_latent_kernel<6>, grid, dim3(384), 0, st, a); break;
     case 7: hipLaunchKernelGGL(attn_latent_kernel<7>, grid, dim3(448), 0, st, a); break;
     default: hipLaunchKernelGGL(attn_latent_kernel<8>, grid, dim3(512), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+// The split-K partials' merge (log-sum-exp weights), one workgroup per (sequence, query
+// head); `cnt` nullptr for the dense walk.
+hipError_t launch_split_merge(const Geo& g, const DecodePlan& p, const AttnArgs& a,
+                              const int32_t* lens, const int32_t* cnt, int b_max, float* out,
+                              hipStream_t st) {
+  MergeArgs m{lens, cnt, a.pacc, a.pml, out, g.Hq, g.Hkv, g.G, p.pps, p.nsplit, g.Dv, b_max};
+  // wider workgroups when there are many splits to combine
+  const int nt = p.nsplit > 32 ? 1024 : 256;
+  const size_t lds = ((p.nsplit + 3) & ~3) * sizeof(float) + (size_t)nt * 4 * sizeof(float);
+  hipError_t e;
+  if (nt == 1024) {
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lse_merge_kernel<1024>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
+        hipSuccess)
+      return e;
+    hipLaunchKernelGGL(lse_merge_kernel<1024>, dim3(g.Hq, g.B), dim3(1024), lds, st, m);
+  } else {
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lse_merge_kernel<256>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
+        hipSuccess)
+      return e;
+    hipLaunchKernelGGL(lse_merge_kernel<256>, dim3(g.Hq, g.B), dim3(256), lds, st, m);
   }
   return hipGetLastError();
 }
@@ -772,25 +803,39 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
     e = bf ? launch_attn<true, 576, 512>(a, grid, p.waves, st)
            : launch_attn<false, 576, 512>(a, grid, p.waves, st);
   if (e != hipSuccess) return e;
-  MergeArgs m{lens, sel ? cnt : nullptr, a.pacc, a.pml, out, g.Hq, g.Hkv, g.G, p.pps,
-              p.nsplit, g.Dv, b_max};
-  // wider workgroups when there are many splits to combine
-  const int nt = p.nsplit > 32 ? 1024 : 256;
-  const size_t lds = ((p.nsplit + 3) & ~3) * sizeof(float) + (size_t)nt * 4 * sizeof(float);
-  if (nt == 1024) {
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lse_merge_kernel<1024>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
-        hipSuccess)
-      return e;
-    hipLaunchKernelGGL(lse_merge_kernel<1024>, dim3(g.Hq, g.B), dim3(1024), lds, st, m);
-  } else {
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lse_merge_kernel<256>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
-        hipSuccess)
-      return e;
-    hipLaunchKernelGGL(lse_merge_kernel<256>, dim3(g.Hq, g.B), dim3(256), lds, st, m);
+  return launch_split_merge(g, p, a, lens, sel ? cnt : nullptr, b_max, out, st);
+}
+
+hipError_t launch_decode_tiered(const Geo& g, const DecodePlan& p, const void* q, const void* k,
+                                const void* v, const void* hot, const int32_t* vslot,
+                                const int32_t* bt, const int32_t* lens, const int32_t* sel,
+                                const int32_t* cnt, int b_max, float scale, float* out, void* ws,
+                                hipStream_t st) {
+  if (p.latent_tiles || g.D != g.Dv || (g.D != 64 && g.D != 128) || g.G > 16)
+    return hipErrorInvalidValue;
+  AttnArgs a = make_attn_args(g, p, q, k, v, bt, lens, sel, cnt, b_max, scale, out, ws);
+  a.vslot = vslot;
+  a.hot = hot;
+  const bool bf = g.dtype == 1;
+  hipError_t e;
+  if (p.unit) {
+    const size_t lds = unit_combine_lds(g);
+    const dim3 ugrid(g.Hkv, g.B);
+    if (g.D == 64)
+      return bf ? launch_unit<true, 64, PSD_ATTN_UNIT_WAVES, true>(a, ugrid, lds, st)
+                : launch_unit<false, 64, PSD_ATTN_UNIT_WAVES, true>(a, ugrid, lds, st);
+    if (bf) return launch_unit<true, 128, PSD_ATTN_UNIT_WAVES, true>(a, ugrid, lds, st);
+    return p.unit == 8 ? launch_unit<false, 128, 8, true>(a, ugrid, lds, st) : hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  const dim3 grid(p.nsplit, g.Hkv, g.B);
+  if (g.D == 64)
+    e = bf ? launch_attn<true, 64, 64, true>(a, grid, p.waves, st)
+           : launch_attn<false, 64, 64, true>(a, grid, p.waves, st);
+  else
+    e = bf ? launch_attn<true, 128, 128, true>(a, grid, p.waves, st)
+           : launch_attn<false, 128, 128, true>(a, grid, p.waves, st);
+  if (e != hipSuccess) return e;
+  return launch_split_merge(g, p, a, lens, sel ? cnt : nullptr, b_max, out, st);
 }
 
 }  // namespace psd

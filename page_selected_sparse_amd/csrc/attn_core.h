@@ -55,6 +55,10 @@ struct AttnArgs {
   int Hq, Hkv, G, max_pages, b_max, pps, nsplit, num_blocks;
   int64_t kbs, kts, khs, vbs, vts, vhs;
   float sl2;  // scale * log2(e)
+  // Value tier (TIER builds): entry e of unit u reads V from hot slice vslot[u][e] when
+  // it is >= 0 ([slots][16][Dv] elements), else from v through the block table.
+  const int32_t* vslot = nullptr;
+  const void* hot = nullptr;
 };
 
 constexpr int kMaxSplits = 16384;
@@ -154,11 +158,13 @@ struct NoHook {
   __device__ void operator()() const {}
 };
 
-template <bool BF16, int DQK, int DV, int WAVES, int NWS, typename Hook = NoHook>
+template <bool BF16, int DQK, int DV, int WAVES, int NWS, typename Hook = NoHook,
+          bool TIER = false>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g, int s,
                                           const int32_t* list, int list_count,
                                           const Hook& before_combine = Hook()) {
   constexpr bool UNIT = NWS > 0;
+  static_assert(!TIER || DQK <= 128, "value tier: D <= 128");
   static_assert(!UNIT || (WAVES == 1 && DQK <= 128), "unit workgroups: one head tile");
   constexpr bool PIPE = PSD_ATTN_PIPE != 0 && BF16;
   constexpr int NQ = DQK / 32;   // QK MFMAs per page (K = 32 dims each)
@@ -193,13 +199,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
   // Page list of a batch of up to 64 entries: lane i holds entry first + stride * (b0 + i).
   // Entries are clamped to the sequence's pages so that a malformed list can never
   // address outside the table.
-  int my_lp = 0, my_blk = 0;
-  auto set_batch = [&](int np) {
+  int my_lp = 0, my_blk = 0, my_vs = -1;
+  auto set_batch = [&](int np, int e) {  // e: this lane's list entry
     my_lp = my_blk = 0;
+    my_vs = -1;
     if (lane < np) {
       my_lp = min(max(sel_lp, 0), n - 1);
       my_blk = a.bt[(int64_t)s * a.max_pages + my_lp];
       my_blk = min(max(my_blk, 0), a.num_blocks - 1);
+      if constexpr (TIER) my_vs = a.vslot[srow + min(e, a.b_max - 1)];
     }
   };
 
@@ -261,10 +269,28 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
       const int blk = __builtin_amdgcn_readlane(my_blk, i);
 #pragma unroll
       for (int c = 0; c < NQ; ++c) load_k(blk, c, R.kr[c][0], R.kr[c][1]);
+      const int vs = TIER ? __builtin_amdgcn_readlane(my_vs, i) : -1;
+      if (TIER && vs >= 0) {  // the page's V slice is resident: [16][Dv] at slice vs
 #pragma unroll
-      for (int w = 0; w < NG; ++w)
+        for (int w = 0; w < NG; ++w)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) R.vr[w][j] = load_v(blk, w, j);
+          for (int j = 0; j < 4; ++j) {
+            const int64_t off = ((int64_t)vs * kPage + 4 * grp + j) * DV + (int64_t)r * NC + w * CW;
+            if constexpr (BF16 && CW == 8) {
+              R.vr[w][j] = load16(static_cast<const uint16_t*>(a.hot) + off);
+            } else if constexpr (BF16) {
+              const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.hot) + off);
+              R.vr[w][j] = make_uint4(x.x, x.y, 0u, 0u);
+            } else {
+              R.vr[w][j] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.hot) + off);
+            }
+          }
+      } else {
+#pragma unroll
+        for (int w = 0; w < NG; ++w)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) R.vr[w][j] = load_v(blk, w, j);
+      }
     }
   };
   auto compute = [&](int i, const PageRegs& R) {
@@ -396,11 +422,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
 
   for (int b0 = 0; b0 < total; b0 += 64) {
     const int np = min(64, total - b0);
-    if (b0 > 0) {
-      const int e = first + stride * (b0 + lane);
+    const int e = first + stride * (b0 + lane);
+    if (b0 > 0)
       sel_lp = list ? list[min(e, count - 1)] : (a.sel ? a.sel[srow + min(e, a.b_max - 1)] : e);
-    }
-    set_batch(np);
+    set_batch(np, e);
     if constexpr (EARLY && PIPE) {
       // Two register sets: page i + 1's loads are in flight while page i is computed.
       PageRegs A, B;
@@ -486,13 +511,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
   if (grp == 0 && hvalid) a.pml[(ubase + head) * a.nsplit + split] = make_float2(m_run, l_run);
 }
 
-template <bool BF16, int DQK, int DV, int WAVES, int MIN_WAVES_PER_SIMD, int NWS = 0>
+template <bool BF16, int DQK, int DV, int WAVES, int MIN_WAVES_PER_SIMD, int NWS = 0,
+          bool TIER = false>
 __global__ __launch_bounds__(64 * (NWS > 0 ? NWS : WAVES))
 __attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnArgs a) {
   if constexpr (NWS > 0)
-    attn_body<BF16, DQK, DV, WAVES, NWS>(a, 0, blockIdx.x, blockIdx.y, nullptr, 0);
+    attn_body<BF16, DQK, DV, WAVES, NWS, NoHook, TIER>(a, 0, blockIdx.x, blockIdx.y, nullptr, 0);
   else
-    attn_body<BF16, DQK, DV, WAVES, NWS>(a, blockIdx.x, blockIdx.y, blockIdx.z, nullptr, 0);
+    attn_body<BF16, DQK, DV, WAVES, NWS, NoHook, TIER>(a, blockIdx.x, blockIdx.y, blockIdx.z,
+                                                       nullptr, 0);
 }
 
 }  // namespace

@@ -212,6 +212,81 @@ psd_status psd_dense_decode(const psd_shape* shape, const void* q, const void* k
                        stream);
 }
 
+// ---- value tier ----------------------------------------------------------------------------
+static bool tier_shape(const psd_shape* shape, psd::Geo* g) {
+  if (check_shape(shape, g) != PSD_OK) return false;
+  return g->D == g->Dv && (g->D == 64 || g->D == 128) && g->G <= 16 &&
+         check_strides(*g, true) == PSD_OK;
+}
+
+size_t psd_value_tier_state_bytes(const psd_shape* shape, int32_t slots) {
+  psd::Geo g;
+  if (slots < 0 || !tier_shape(shape, &g)) return 0;
+  return psd::tier_layout(g, slots, 1).state_bytes;
+}
+
+size_t psd_value_tier_workspace_bytes(const psd_shape* shape, int32_t b_max, int32_t slots) {
+  psd::Geo g;
+  if (slots < 0 || b_max < 1 || !tier_shape(shape, &g)) return 0;
+  return psd::tier_layout(g, slots, b_max).work_bytes;
+}
+
+psd_status psd_value_tier_reset(const psd_shape* shape, int32_t slots, void* state,
+                                hipStream_t stream) {
+  psd::Geo g;
+  if (check_shape(shape, &g) != PSD_OK) return PSD_ERR_INVALID_ARG;
+  if (!tier_shape(shape, &g)) return PSD_ERR_UNSUPPORTED;
+  if (slots < 0 || !state || !aligned16(state)) return PSD_ERR_INVALID_ARG;
+  return launched(psd::launch_tier_reset(g, slots, state, stream));
+}
+
+psd_status psd_value_tier_stage(const psd_shape* shape, const void* v_host, void* hot,
+                                void* state, int32_t slots, int32_t step,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* sel_pages, const int32_t* sel_count,
+                                int32_t b_max, int32_t* vslot, uint64_t* stats, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  psd::Geo g;
+  if (check_shape(shape, &g) != PSD_OK) return PSD_ERR_INVALID_ARG;
+  if (!tier_shape(shape, &g)) return PSD_ERR_UNSUPPORTED;
+  if (slots < 0 || b_max < 1 || !v_host || !state || !block_table || !seq_lens || !sel_pages ||
+      !sel_count || !vslot || !stats || (slots > 0 && !hot))
+    return PSD_ERR_INVALID_ARG;
+  if (!aligned16(v_host) || (hot && !aligned16(hot)) || !aligned16(state))
+    return PSD_ERR_INVALID_ARG;
+  const psd::TierLayout t = psd::tier_layout(g, slots, b_max);
+  if (!workspace || workspace_bytes < t.work_bytes || !aligned16(workspace))
+    return PSD_ERR_WORKSPACE;
+  return launched(psd::launch_tier_stage(g, slots, step, v_host, hot, state, block_table, seq_lens,
+                                         sel_pages, sel_count, b_max, vslot,
+                                         reinterpret_cast<unsigned long long*>(stats), workspace,
+                                         stream));
+}
+
+psd_status psd_sparse_decode_tiered(const psd_shape* shape, const void* q, const void* k_cache,
+                                    const void* v_host, const void* hot, const int32_t* vslot,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* sel_pages, const int32_t* sel_count,
+                                    int32_t b_max, float scale, float* out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  psd::Geo g;
+  if (check_shape(shape, &g) != PSD_OK) return PSD_ERR_INVALID_ARG;
+  if (!tier_shape(shape, &g)) return PSD_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_host || !vslot || !block_table || !seq_lens || !sel_pages ||
+      !sel_count || !out || b_max < 1)
+    return PSD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_host) || (hot && !aligned16(hot)) ||
+      !aligned16(out))
+    return PSD_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == __builtin_inff()) return PSD_ERR_INVALID_ARG;
+  psd::DecodePlan p;
+  if (!psd::plan_decode(g, b_max, false, &p)) return PSD_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < p.bytes || !aligned16(workspace)) return PSD_ERR_WORKSPACE;
+  return launched(psd::launch_decode_tiered(g, p, q, k_cache, v_host, hot, vslot, block_table,
+                                            seq_lens, sel_pages, sel_count, b_max, scale, out,
+                                            workspace, stream));
+}
+
 // select_pages then sparse_decode, as one launch when the plans allow; with `refresh`,
 // the tail-page statistics refresh of page_meta_update (no first_page) comes first.
 static psd_status step_common(const psd_shape* shape, const void* q, const void* meta,

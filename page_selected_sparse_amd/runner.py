@@ -148,6 +148,56 @@ class DecodeStep:
                                 self.seq_lens, self.budgets, self.b_max, self.scale,
                                 self.sel_pages, self.sel_count, self.out, stream)
 
+    # -- value tier: V in (pinned host) memory, a resident hot buffer in device memory ------
+    def enable_tier(self, slots: int):
+        """Keep up to ``slots`` (block, KV head) V slices resident in a device hot buffer;
+        each tiered step copies only the kept slices that are not resident (from ``v``,
+        pinned host memory when the step was built with ``v_host``)."""
+        dev = self.q.device
+        B, Hkv = self.sel_count.shape
+        dv = self.v.shape[-1]
+        st_bytes = api.value_tier_state_bytes(self.shape, slots)
+        ws_bytes = api.value_tier_workspace_bytes(self.shape, self.b_max, slots)
+        if st_bytes == 0 or ws_bytes == 0:
+            raise api.PsdError(-2, "value tier (GQA shapes with D == D_v in {64, 128})")
+        self.tier_slots = int(slots)
+        self.tier_hot = (torch.empty((slots, 16, dv), dtype=self.q.dtype, device=dev)
+                         if slots > 0 else None)
+        self.tier_state = torch.empty(st_bytes, dtype=torch.uint8, device=dev)
+        self.tier_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.tier_vslot = torch.empty((B, Hkv, self.b_max), dtype=torch.int32, device=dev)
+        self.tier_stats = torch.zeros(4, dtype=torch.int64, device=dev)
+        self.tier_step = 0
+        api.value_tier_reset(self.shape, self.tier_slots, self.tier_state)
+
+    def tier_stage(self, stream=None):
+        """Slots for this step's kept V slices (after ``select``); copies the missed ones."""
+        self.tier_step += 1
+        api.value_tier_stage(self.shape, self.v, self.tier_hot, self.tier_state, self.tier_slots,
+                             self.tier_step, self.block_table, self.seq_lens, self.sel_pages,
+                             self.sel_count, self.b_max, self.tier_vslot, self.tier_stats,
+                             self.tier_ws, stream)
+
+    def sparse_tiered(self, stream=None):
+        api.sparse_decode_tiered(self.shape, self.q, self.k, self.v, self.tier_hot,
+                                 self.tier_vslot, self.block_table, self.seq_lens,
+                                 self.sel_pages, self.sel_count, self.b_max, self.scale,
+                                 self.out, self.ws_decode, stream)
+
+    def step_tiered(self, stream=None):
+        """One decode step with V in the value tier: tail refresh, selection, staging of the
+        kept slices, attention."""
+        self.refresh_tail(stream)
+        self.select(stream)
+        self.tier_stage(stream)
+        self.sparse_tiered(stream)
+
+    def tier_counts(self) -> dict:
+        """The last stage's counts (synchronises): hits, misses (entries), slices copied,
+        entries read from the host pool."""
+        h, m, c, o = (int(x) for x in self.tier_stats.cpu().tolist())
+        return {"hits": h, "misses": m, "copied": c, "from_host": o}
+
     def step_separate(self, stream=None):
         """The same step as three calls: tail refresh, selection, attention."""
         self.refresh_tail(stream)

@@ -255,3 +255,41 @@ def test_noalloc_step_rejects_oversize_before_touching_the_device(native):
                                        None) == -1
     assert lib.psd_decode_step_noalloc(ctypes.byref(_shape(native)), f, f, f, f, f, f, f, 1,
                                        0.1, f, f, f, None) == -1
+
+
+def test_value_tier_queries_and_checks(native):
+    """Value tier: state and workspace sizes follow the layout the calls document (page map
+    of num_blocks x H_kv words, owner and last-step words per slot; per-entry miss and copy
+    lists, a free list per slot); unsupported shapes and bad arguments are refused on the
+    host."""
+    lib = native.lib()
+    al = lambda x: (x + 255) // 256 * 256
+    sh = _shape(native, batch=2, num_blocks=100)
+    keys = 100 * 8
+    assert lib.psd_value_tier_state_bytes(ctypes.byref(sh), 10) == al(keys * 4) + 2 * al(40)
+    assert lib.psd_value_tier_state_bytes(ctypes.byref(sh), 0) == al(keys * 4)
+    assert lib.psd_value_tier_state_bytes(ctypes.byref(sh), -1) == 0
+    entries = 2 * 8 * 12
+    assert (lib.psd_value_tier_workspace_bytes(ctypes.byref(sh), 12, 10)
+            == 2 * al(entries * 4) + al(40) + 256)
+    assert lib.psd_value_tier_workspace_bytes(ctypes.byref(sh), 0, 10) == 0
+    latent = _shape(native, num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512,
+                    k_block_stride=16 * 576, k_token_stride=576, k_head_stride=576,
+                    v_block_stride=16 * 576, v_token_stride=576, v_head_stride=576)
+    assert lib.psd_value_tier_state_bytes(ctypes.byref(latent), 10) == 0
+    f = ctypes.c_void_p(4096)
+    assert lib.psd_value_tier_reset(ctypes.byref(latent), 10, f, None) == -2
+    assert lib.psd_value_tier_reset(ctypes.byref(sh), -1, f, None) == -1
+    assert lib.psd_value_tier_reset(ctypes.byref(sh), 10, None, None) == -1
+    stage = lambda hot, slots, ws, nbytes: lib.psd_value_tier_stage(
+        ctypes.byref(sh), f, hot, f, slots, 1, f, f, f, f, 12, f, f, ws, nbytes, None)
+    need = lib.psd_value_tier_workspace_bytes(ctypes.byref(sh), 12, 10)
+    assert stage(None, 10, f, need) == -1  # slots without a hot buffer
+    assert stage(f, 10, None, need) == -3
+    assert stage(f, 10, f, need - 1) == -3
+    assert lib.psd_value_tier_stage(ctypes.byref(latent), f, f, f, 10, 1, f, f, f, f, 12, f, f,
+                                    f, 1 << 30, None) == -2
+    dec = lambda vslot, nbytes: lib.psd_sparse_decode_tiered(
+        ctypes.byref(sh), f, f, f, f, vslot, f, f, f, f, 12, 0.1, f, f, nbytes, None)
+    assert dec(None, 1 << 30) == -1
+    assert dec(f, 8) == -3
