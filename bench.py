@@ -50,6 +50,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PREHEAT_CALLS = 160  # step + dense pairs run untimed first (about 0.1 s on the ragged batch)
 METRIC = "sparse decode attn steps/s + effective HBM GB/s (% peak), B=32 @32K ctx"
 
 
@@ -402,7 +403,7 @@ def measure_config(name: str, args, dev) -> dict:
     for i in range(max(args.warmup, 2 * len(sts))):
         sts[i % len(sts)].step()
         sts[i % len(sts)].dense()
-    iters = max(20, args.steps)
+    iters = max(100, args.steps)
     ms_step = timed_over(sts, lambda st: st.step(), iters)
     ms_dense = timed_over(sts, lambda st: st.dense(), max(10, iters // 4))
     ab = algorithmic_bytes(w, sts[0].sel_count.cpu().numpy())
@@ -499,7 +500,12 @@ def main():
 
     # The other legs run before the measured region, the other workloads first, so that
     # the measured region runs at steady clocks on inputs the legs just before it have
-    # touched (a 20-step region right after the GPU wakes runs about 8 % slower).
+    # touched (a 20-step region right after the GPU wakes runs about 8 % slower). First,
+    # untimed, about 0.1 s of steps and dense walks brings the GPU to its steady clocks.
+    for i in range(PREHEAT_CALLS):
+        steps[i % R].step()
+        steps[i % R].dense()
+    torch.cuda.synchronize()
     launch_fl = launch_floor(max(100, args.steps))
     configs = None
     if not args.no_configs:
