@@ -369,7 +369,9 @@ psd_status psd_dense_decode(const psd_shape* shape, const void* q, const void* k
  * page.
  *
  *   q            [B, H_q, D] dtype, 16-byte aligned
- *   k_cache      paged K cache (shape strides), 16-byte aligned; only valid rows are read
+ *   k_cache      paged K cache (shape strides), 16-byte aligned; every row of each page's
+ *                block is read (the tail block's rows at or past the length too, which
+ *                must be readable), and rows at or past the length are ignored
  *   block_table  [B, max_pages_per_seq] int32 physical block ids
  *   seq_lens     [B] int32 token counts
  *   coverage     target kept mass, in (0, 1]; larger values act as 1
