@@ -643,28 +643,39 @@ hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) 
   // occupancy target per variant: the smallest register budget that does not spill
   constexpr int W1 = DQK > 128 ? 1 : (BF16 ? PSD_ATTN_W1 : 2);
   constexpr int W2 = DQK > 128 ? 1 : 2;
+  constexpr bool KT = BF16 && DQK == 128;  // K through a 4 KB LDS tile per wave
+  constexpr size_t T = KT ? kKTileBytes : 0;
   if constexpr (TIER) {  // value tier: groups of up to 16 heads (one wave)
     if (waves != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 1, W1, 0, true>), grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 1, W1, 0, true, KT>), grid, dim3(64), T, st,
+                       a, 0, (int)T);
     return hipGetLastError();
   }
   if (waves == 1) {
-    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 1, W1>), grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 1, W1, 0, false, KT>), grid, dim3(64), T, st,
+                       a, 0, (int)T);
   } else if (waves == 2) {
-    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 2, W2>), grid, dim3(128), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 2, W2, 0, false, KT>), grid, dim3(128), 2 * T,
+                       st, a, 0, (int)T);
   } else {
-    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 8, 1>), grid, dim3(64 * waves), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<BF16, DQK, DV, 8, 1, 0, false, KT>), grid, dim3(64 * waves),
+                       waves * T, st, a, 0, (int)T);
   }
   return hipGetLastError();
 }
 
+// `lds`: the closing combine's bytes; at bf16, D = 128 the waves' K tiles are placed by
+// ktile_place.
 template <bool BF16, int D, int NW = PSD_ATTN_UNIT_WAVES, bool TIER = false>
-hipError_t launch_unit(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  auto kern = &attn_kernel<BF16, D, D, 1, (NW + 3) / 4, NW, TIER>;
+hipError_t launch_unit(const Geo& g, const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr bool KT = BF16 && D == 128;
+  auto kern = &attn_kernel<BF16, D, D, 1, (NW + 3) / 4, NW, TIER, KT>;
+  KTilePlace kp{0, 0, lds};
+  if (KT) kp = ktile_place(g, NW, lds);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kp.end);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, st, a);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), kp.end, st, a, (int)kp.off, (int)kp.stride);
   return hipGetLastError();
 }
 
@@ -784,10 +795,11 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
     const size_t lds = unit_combine_lds(g);
     const dim3 ugrid(g.Hkv, g.B);
     if (g.D == 64)
-      return bf ? launch_unit<true, 64>(a, ugrid, lds, st) : launch_unit<false, 64>(a, ugrid, lds, st);
-    if (bf) return launch_unit<true, 128>(a, ugrid, lds, st);
+      return bf ? launch_unit<true, 64>(g, a, ugrid, lds, st)
+                : launch_unit<false, 64>(g, a, ugrid, lds, st);
+    if (bf) return launch_unit<true, 128>(g, a, ugrid, lds, st);
     // fp32 D = 128 is built for 8-wave workgroups only (plan_decode)
-    return p.unit == 8 ? launch_unit<false, 128, 8>(a, ugrid, lds, st) : hipErrorInvalidValue;
+    return p.unit == 8 ? launch_unit<false, 128, 8>(g, a, ugrid, lds, st) : hipErrorInvalidValue;
   }
   if (g.D == 64)
     e = bf ? launch_attn<true, 64, 64>(a, grid, p.waves, st)
@@ -822,10 +834,11 @@ hipError_t launch_decode_tiered(const Geo& g, const DecodePlan& p, const void* q
     const size_t lds = unit_combine_lds(g);
     const dim3 ugrid(g.Hkv, g.B);
     if (g.D == 64)
-      return bf ? launch_unit<true, 64, PSD_ATTN_UNIT_WAVES, true>(a, ugrid, lds, st)
-                : launch_unit<false, 64, PSD_ATTN_UNIT_WAVES, true>(a, ugrid, lds, st);
-    if (bf) return launch_unit<true, 128, PSD_ATTN_UNIT_WAVES, true>(a, ugrid, lds, st);
-    return p.unit == 8 ? launch_unit<false, 128, 8, true>(a, ugrid, lds, st) : hipErrorInvalidValue;
+      return bf ? launch_unit<true, 64, PSD_ATTN_UNIT_WAVES, true>(g, a, ugrid, lds, st)
+                : launch_unit<false, 64, PSD_ATTN_UNIT_WAVES, true>(g, a, ugrid, lds, st);
+    if (bf) return launch_unit<true, 128, PSD_ATTN_UNIT_WAVES, true>(g, a, ugrid, lds, st);
+    return p.unit == 8 ? launch_unit<false, 128, 8, true>(g, a, ugrid, lds, st)
+                       : hipErrorInvalidValue;
   }
   const dim3 grid(p.nsplit, g.Hkv, g.B);
   if (g.D == 64)

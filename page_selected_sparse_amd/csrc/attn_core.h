@@ -62,6 +62,20 @@ struct AttnArgs {
 };
 
 constexpr int kMaxSplits = 16384;
+constexpr int kKTileBytes = 16 * 17 * 16;  // a wave's K tile: 16 rows of 256 B, 16 B of pad
+
+// Where the K tiles of a whole-unit workgroup go: inside each wave's own part of the
+// closing combine's area when that part is big enough (a wave writes it only once its own
+// pages are done, and reads the others' only after a barrier), else past `used` bytes.
+struct KTilePlace {
+  size_t off, stride, end;  // first tile, distance between tiles, end of the LDS used
+};
+inline KTilePlace ktile_place(const Geo& g, int waves, size_t used) {
+  const size_t part = (size_t)g.G * g.Dv * sizeof(float);
+  if (part >= (size_t)kKTileBytes) return KTilePlace{0, part, used};
+  const size_t off = (used + 255) / 256 * 256;
+  return KTilePlace{off, (size_t)kKTileBytes, off + (size_t)waves * kKTileBytes};
+}
 
 // LDS of a whole-unit workgroup's closing combine: acc [waves][G][Dv] and (m, l) [waves][16].
 inline size_t unit_combine_lds(const Geo& g) {
@@ -158,13 +172,21 @@ struct NoHook {
   __device__ void operator()() const {}
 };
 
+// KT (bf16, D = 128): each page's K rows are loaded whole (4 rows of 256 bytes per load
+// instruction, as V is) and pass through an LDS tile of the wave (kKTileBytes at `ktile` +
+// wave * kt_stride) to reach the matrix cores' operand layout (16 rows of 64 bytes per
+// fragment): loads of that layout straight from memory touch 16 rows per instruction and
+// make the gather about 40 % slower per byte than whole rows.
 template <bool BF16, int DQK, int DV, int WAVES, int NWS, typename Hook = NoHook,
-          bool TIER = false>
+          bool TIER = false, bool KT = false>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g, int s,
                                           const int32_t* list, int list_count,
-                                          const Hook& before_combine = Hook()) {
+                                          const Hook& before_combine = Hook(),
+                                          unsigned char* ktile = nullptr,
+                                          int kt_stride = kKTileBytes) {
   constexpr bool UNIT = NWS > 0;
   static_assert(!TIER || DQK <= 128, "value tier: D <= 128");
+  static_assert(!KT || (BF16 && DQK == 128), "K through LDS: bf16, D = 128");
   static_assert(!UNIT || (WAVES == 1 && DQK <= 128), "unit workgroups: one head tile");
   constexpr bool PIPE = PSD_ATTN_PIPE != 0 && BF16;
   constexpr int NQ = DQK / 32;   // QK MFMAs per page (K = 32 dims each)
@@ -267,8 +289,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
   auto issue = [&](int i, PageRegs& R) {
     if constexpr (EARLY) {
       const int blk = __builtin_amdgcn_readlane(my_blk, i);
+      if constexpr (KT) {  // instruction c: rows 4c + grp, 16 bytes at dims 8r
 #pragma unroll
-      for (int c = 0; c < NQ; ++c) load_k(blk, c, R.kr[c][0], R.kr[c][1]);
+        for (int c = 0; c < NQ; ++c)
+          R.kr[c][0] = load16(static_cast<const uint16_t*>(a.k) + (int64_t)blk * a.kbs +
+                              (int64_t)(4 * c + grp) * a.kts + (int64_t)g * a.khs + 8 * r);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) load_k(blk, c, R.kr[c][0], R.kr[c][1]);
+      }
       const int vs = TIER ? __builtin_amdgcn_readlane(my_vs, i) : -1;
       if (TIER && vs >= 0) {  // the page's V slice is resident: [16][Dv] at slice vs
 #pragma unroll
@@ -300,10 +329,33 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
 
     // ---- S^T = K Q^T -------------------------------------------------------------------
     float4v sacc = {0.f, 0.f, 0.f, 0.f};
+    uint4 kt[KT ? NQ : 1];
+    if constexpr (KT) {
+      // Row t, 16-byte piece k of the page sits at slot 17 t + k of the wave's tile: the
+      // padding puts the 16 lanes that write one row, and the 16 lanes that read one piece
+      // of 16 rows, on 16 different 4-bank groups; each lane's slots differ by constants.
+      // The wave's LDS operations run in order; the fences keep the compiler from moving
+      // one lane's accesses across another lane's (the last page's reads, these writes).
+      uint4* tile = reinterpret_cast<uint4*>(ktile + (threadIdx.x >> 6) * kt_stride);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint4* wr = tile + 17 * grp + r;  // row 4c + grp, piece r
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) wr[68 * c] = R.kr[c][0];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint4* rd = tile + 17 * r + grp;  // row r, piece 4c + grp
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) kt[c] = rd[4 * c];
+    }
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
       uint4 x0, x1, khi, klo, qh, ql;
-      if constexpr (EARLY) {
+      if constexpr (KT) {
+        x0 = kt[c];
+      } else if constexpr (EARLY) {
         x0 = R.kr[c][0];
         x1 = R.kr[c][1];
       } else {
@@ -511,15 +563,23 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
   if (grp == 0 && hvalid) a.pml[(ubase + head) * a.nsplit + split] = make_float2(m_run, l_run);
 }
 
+// KT: wave w's K tile is at byte kt_off + w * kt_stride of the dynamic LDS.
 template <bool BF16, int DQK, int DV, int WAVES, int MIN_WAVES_PER_SIMD, int NWS = 0,
-          bool TIER = false>
+          bool TIER = false, bool KT = false>
 __global__ __launch_bounds__(64 * (NWS > 0 ? NWS : WAVES))
-__attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnArgs a) {
+__attribute__((amdgpu_waves_per_eu(MIN_WAVES_PER_SIMD))) void attn_kernel(AttnArgs a,
+                                                                           int kt_off,
+                                                                           int kt_stride) {
+  extern __shared__ unsigned char kdyn[];
+  unsigned char* ktile = KT ? kdyn + kt_off : nullptr;
   if constexpr (NWS > 0)
-    attn_body<BF16, DQK, DV, WAVES, NWS, NoHook, TIER>(a, 0, blockIdx.x, blockIdx.y, nullptr, 0);
+    attn_body<BF16, DQK, DV, WAVES, NWS, NoHook, TIER, KT>(a, 0, blockIdx.x, blockIdx.y,
+                                                           nullptr, 0, NoHook(), ktile,
+                                                           kt_stride);
   else
-    attn_body<BF16, DQK, DV, WAVES, NWS, NoHook, TIER>(a, blockIdx.x, blockIdx.y, blockIdx.z,
-                                                       nullptr, 0);
+    attn_body<BF16, DQK, DV, WAVES, NWS, NoHook, TIER, KT>(a, blockIdx.x, blockIdx.y,
+                                                           blockIdx.z, nullptr, 0, NoHook(),
+                                                           ktile, kt_stride);
 }
 
 }  // namespace

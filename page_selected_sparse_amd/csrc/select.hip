@@ -923,10 +923,10 @@ hipError_t dispatch_hb(const SelArgs& a, const SelectPlan& p, dim3 grid, hipStre
 // The tail page is never a ranking candidate, so the refresh is independent of the
 // ranking; the last wave, which has the fewest pages to attend, does it before the waves
 // are combined.
-template <bool BF16, int D, int HB, bool REFRESH>
+template <bool BF16, int D, int HB, bool REFRESH, bool KT>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
-void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, void* meta_w, int64_t kbs,
-                        int64_t kts, int64_t khs) {
+void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, int kt_off, int kt_stride,
+                        void* meta_w, int64_t kbs, int64_t kts, int64_t khs) {
   static_assert(PSD_ATTN_UNIT_WAVES == 16, "one attention split per wave of the workgroup");
   // Built only where it fits the 128 VGPRs of 16 waves per CU without spilling: 4-head
   // groups, and fp32 only at D = 64 (8-head groups and fp32 at D = 128 spill).
@@ -959,35 +959,70 @@ void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, void* meta_w, int6
                                        kbs, kts, khs, threadIdx.x & 63, 64);
     }
   };
-  attn_body<BF16, D, D, 1, 16>(aa, 0, g, s, list, count, refresh_tail);
+  attn_body<BF16, D, D, 1, 16, decltype(refresh_tail), false, KT>(aa, 0, g, s, list, count,
+                                                                   refresh_tail, lds + kt_off,
+                                                                   kt_stride);
 }
 
-template <bool BF16, int D, bool REFRESH>
+struct FusedLayout {
+  size_t list_off, lds;        // byte offset of the page list; dynamic LDS
+  bool kt;                     // K through the waves' LDS tiles
+  size_t kt_off, kt_stride;    // first tile, distance between tiles
+};
+
+template <bool BF16, int D, bool REFRESH, bool KT>
 hipError_t launch_fused(const SelArgs& a, const AttnArgs& aa, int head_block, dim3 grid,
-                        size_t lds, int list_off, void* meta_w, const Geo& g, hipStream_t st) {
+                        const FusedLayout& L, void* meta_w, const Geo& g, hipStream_t st) {
   if (head_block != 4) return hipErrorInvalidValue;  // fused_applies admits 4-head groups only
-  auto kern = &select_attn_kernel<BF16, D, 4, REFRESH>;
-  hipError_t e = set_lds(kern, lds);
+  auto kern = &select_attn_kernel<BF16, D, 4, REFRESH, KT>;
+  hipError_t e = set_lds(kern, L.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(1024), lds, st, a, aa, list_off, meta_w, g.kbs, g.kts,
-                     g.khs);
+  hipLaunchKernelGGL(kern, grid, dim3(1024), L.lds, st, a, aa, (int)L.list_off, (int)L.kt_off,
+                     (int)L.kt_stride, meta_w, g.kbs, g.kts, g.khs);
   return hipGetLastError();
 }
 
 template <bool BF16, int D>
 hipError_t launch_fused_r(const SelArgs& a, const AttnArgs& aa, int head_block, dim3 grid,
-                          size_t lds, int list_off, void* meta_w, const Geo& g, hipStream_t st) {
-  return meta_w ? launch_fused<BF16, D, true>(a, aa, head_block, grid, lds, list_off, meta_w, g, st)
-                : launch_fused<BF16, D, false>(a, aa, head_block, grid, lds, list_off, meta_w, g, st);
+                          const FusedLayout& L, void* meta_w, const Geo& g, hipStream_t st) {
+  if constexpr (BF16 && D == 128) {
+    if (L.kt)
+      return meta_w ? launch_fused<BF16, D, true, true>(a, aa, head_block, grid, L, meta_w, g, st)
+                    : launch_fused<BF16, D, false, true>(a, aa, head_block, grid, L, meta_w, g, st);
+  }
+  return meta_w ? launch_fused<BF16, D, true, false>(a, aa, head_block, grid, L, meta_w, g, st)
+                : launch_fused<BF16, D, false, false>(a, aa, head_block, grid, L, meta_w, g, st);
 }
 
-// Byte offset of the page list and dynamic LDS of the fused launch.
-void fused_layout(const Geo& g, const SelectPlan& sp, int b_max, size_t* list_off, size_t* lds) {
+// Static LDS of the fused kernel (the scoring's query copies and scratch).
+size_t fused_static_lds(const Geo& g, const SelectPlan& sp) {
+  return (size_t)g.D * sp.head_block * 2 * sizeof(float) + sizeof(double2) + sizeof(SelScratch);
+}
+
+// Dynamic LDS of the fused launch. The scoring's keys and staging come first; once the
+// ranking is done, the closing combine's area reuses the start and the page list follows
+// it. At bf16, D = 128 the waves' K tiles sit inside their combine parts, or past the
+// list where those are too small and the total still fits (else no tiles).
+FusedLayout fused_layout(const Geo& g, const SelectPlan& sp, int b_max) {
+  FusedLayout L;
   const size_t keys = (size_t)sp.threads * sp.ppt * sizeof(uint64_t);
   const size_t combine = unit_combine_lds(g);
-  *list_off = ((keys > combine ? keys : combine) + 255) / 256 * 256;
-  const size_t end = *list_off + (size_t)b_max * sizeof(int32_t);
-  *lds = end > sp.score_lds ? end : sp.score_lds;
+  L.list_off = ((keys > combine ? keys : combine) + 255) / 256 * 256;
+  const size_t end = L.list_off + (size_t)b_max * sizeof(int32_t);
+  L.lds = end > sp.score_lds ? end : sp.score_lds;
+  L.kt = false;
+  L.kt_off = L.kt_stride = 0;
+  if (g.dtype == 1 && g.D == 128) {
+    const KTilePlace kp = ktile_place(g, PSD_ATTN_UNIT_WAVES, end);
+    const size_t lds = kp.end > L.lds ? kp.end : L.lds;
+    if (fused_static_lds(g, sp) + lds <= 160 * 1024) {
+      L.kt = true;
+      L.kt_off = kp.off;
+      L.kt_stride = kp.stride;
+      L.lds = lds;
+    }
+  }
+  return L;
 }
 
 }  // namespace
@@ -1191,11 +1226,7 @@ bool fused_applies(const Geo& g, const SelectPlan& sp, const DecodePlan& dp, int
   if (sp.head_block != 4 || (g.dtype != 1 && g.D > 64)) return false;  // spill-free builds
   if (sp.cpl != 1 || sp.stages != 1) return false;
   if (dp.unit != 16 || g.D > 128 || g.Dv != g.D) return false;
-  size_t list_off, lds;
-  fused_layout(g, sp, b_max, &list_off, &lds);
-  const size_t static_lds = (size_t)g.D * sp.head_block * 2 * sizeof(float) + sizeof(double2) +
-                            sizeof(SelScratch);
-  return static_lds + lds <= 160 * 1024;
+  return fused_static_lds(g, sp) + fused_layout(g, sp, b_max).lds <= 160 * 1024;
 }
 
 hipError_t launch_select_decode(const Geo& g, const SelectPlan& sp, const DecodePlan& dp,
@@ -1205,16 +1236,14 @@ hipError_t launch_select_decode(const Geo& g, const SelectPlan& sp, const Decode
                                 void* ws, void* meta_tail, hipStream_t st) {
   const SelArgs a = make_args(g, sp, q, meta, bt, lens, budgets, b_max, sel, cnt, ws);
   const AttnArgs aa = make_attn_args(g, dp, q, k, v, bt, lens, sel, cnt, b_max, scale, out, ws);
-  size_t list_off, lds;
-  fused_layout(g, sp, b_max, &list_off, &lds);
+  const FusedLayout L = fused_layout(g, sp, b_max);
   const dim3 grid(g.Hkv, g.B);
   const bool bf = g.dtype == 1;
-  const int lo = (int)list_off;
   if (g.D == 64)
-    return bf ? launch_fused_r<true, 64>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st)
-              : launch_fused_r<false, 64>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st);
+    return bf ? launch_fused_r<true, 64>(a, aa, sp.head_block, grid, L, meta_tail, g, st)
+              : launch_fused_r<false, 64>(a, aa, sp.head_block, grid, L, meta_tail, g, st);
   if (!bf) return hipErrorInvalidValue;  // fp32 at D = 128: no fused build (fused_applies)
-  return launch_fused_r<true, 128>(a, aa, sp.head_block, grid, lds, lo, meta_tail, g, st);
+  return launch_fused_r<true, 128>(a, aa, sp.head_block, grid, L, meta_tail, g, st);
 }
 
 }  // namespace psd
