@@ -643,7 +643,7 @@ hipError_t launch_attn(const AttnArgs& a, dim3 grid, int waves, hipStream_t st) 
   // occupancy target per variant: the smallest register budget that does not spill
   constexpr int W1 = DQK > 128 ? 1 : (BF16 ? PSD_ATTN_W1 : 2);
   constexpr int W2 = DQK > 128 ? 1 : 2;
-  constexpr bool KT = BF16 && DQK == 128;  // K through a 4 KB LDS tile per wave
+  constexpr bool KT = BF16 && DQK == 128;  // K through an LDS tile per wave
   constexpr size_t T = KT ? kKTileBytes : 0;
   if constexpr (TIER) {  // value tier: groups of up to 16 heads (one wave)
     if (waves != 1) return hipErrorInvalidValue;

@@ -982,16 +982,14 @@ hipError_t launch_fused(const SelArgs& a, const AttnArgs& aa, int head_block, di
   return hipGetLastError();
 }
 
+// bf16 at D = 128 is built with the K tiles only (fused_applies admits no other layout).
 template <bool BF16, int D>
 hipError_t launch_fused_r(const SelArgs& a, const AttnArgs& aa, int head_block, dim3 grid,
                           const FusedLayout& L, void* meta_w, const Geo& g, hipStream_t st) {
-  if constexpr (BF16 && D == 128) {
-    if (L.kt)
-      return meta_w ? launch_fused<BF16, D, true, true>(a, aa, head_block, grid, L, meta_w, g, st)
-                    : launch_fused<BF16, D, false, true>(a, aa, head_block, grid, L, meta_w, g, st);
-  }
-  return meta_w ? launch_fused<BF16, D, true, false>(a, aa, head_block, grid, L, meta_w, g, st)
-                : launch_fused<BF16, D, false, false>(a, aa, head_block, grid, L, meta_w, g, st);
+  constexpr bool KT = BF16 && D == 128;
+  if (L.kt != KT) return hipErrorInvalidValue;
+  return meta_w ? launch_fused<BF16, D, true, KT>(a, aa, head_block, grid, L, meta_w, g, st)
+                : launch_fused<BF16, D, false, KT>(a, aa, head_block, grid, L, meta_w, g, st);
 }
 
 // Static LDS of the fused kernel (the scoring's query copies and scratch).
@@ -1002,7 +1000,8 @@ size_t fused_static_lds(const Geo& g, const SelectPlan& sp) {
 // Dynamic LDS of the fused launch. The scoring's keys and staging come first; once the
 // ranking is done, the closing combine's area reuses the start and the page list follows
 // it. At bf16, D = 128 the waves' K tiles sit inside their combine parts, or past the
-// list where those are too small and the total still fits (else no tiles).
+// list where those are too small; `kt` is false where they would not fit, and
+// fused_applies then turns the launch down.
 FusedLayout fused_layout(const Geo& g, const SelectPlan& sp, int b_max) {
   FusedLayout L;
   const size_t keys = (size_t)sp.threads * sp.ppt * sizeof(uint64_t);
@@ -1226,7 +1225,9 @@ bool fused_applies(const Geo& g, const SelectPlan& sp, const DecodePlan& dp, int
   if (sp.head_block != 4 || (g.dtype != 1 && g.D > 64)) return false;  // spill-free builds
   if (sp.cpl != 1 || sp.stages != 1) return false;
   if (dp.unit != 16 || g.D > 128 || g.Dv != g.D) return false;
-  return fused_static_lds(g, sp) + fused_layout(g, sp, b_max).lds <= 160 * 1024;
+  const FusedLayout L = fused_layout(g, sp, b_max);
+  if (L.kt != (g.dtype == 1 && g.D == 128)) return false;  // the build takes K tiles there
+  return fused_static_lds(g, sp) + L.lds <= 160 * 1024;
 }
 
 hipError_t launch_select_decode(const Geo& g, const SelectPlan& sp, const DecodePlan& dp,
