@@ -34,6 +34,8 @@ Prints one JSON line. Besides the contract fields it carries:
                 kept slices, over 8 steps of drifting queries: hit rate, host-link bytes
                 per step (against reading every kept V row from host memory) and the
                 step time (--no-tier skips it)
+  kv_tier       the same with K in pinned host memory too (the KV tier: each resident
+                slice holds its K and V rows)
 """
 from __future__ import annotations
 
@@ -321,26 +323,26 @@ def launch_floor(iters: int) -> dict:
             "kernel": "torch.cuda._sleep(0), back to back on one stream"}
 
 
-def value_tier_leg(w, base, dev, steps: int = 8) -> dict:
-    """The value tier over consecutive decode steps: V in pinned host memory, a resident hot
-    buffer of 1.5x one step's kept (block, KV head) slices, queries on a random walk (about
-    5 % per step). Per step: hits, slices copied over the host link and their bytes, the
-    step time (selection, staging, attention) against the same step reading every kept V
-    row from host memory (zero copy)."""
+def value_tier_leg(w, base, dev, steps: int = 8, kv: bool = False) -> dict:
+    """The value tier over consecutive decode steps: V (with ``kv``, K and V: the KV tier)
+    in pinned host memory, a resident hot buffer of 1.5x one step's kept (block, KV head)
+    slices, queries on a random walk (about 5 % per step). Per step: hits, slices copied
+    over the host link and their bytes, the step time (selection, staging, attention)
+    against the same step reading every kept row from host memory (zero copy)."""
     import torch
 
     from page_selected_sparse_amd import DecodeStep
 
     sp = w.spec
     st = DecodeStep(base.q.clone(), base.cache, base.block_table, base.seq_lens, base.budgets,
-                    sp.head_dim_v, sp.latent, b_max=base.b_max, v_host=True)
+                    sp.head_dim_v, sp.latent, b_max=base.b_max, v_host=True, kv_host=kv)
     st.build_meta()
     st.select()
     kept0 = int(st.sel_count.clamp(min=0).sum())
     slots = int(1.5 * kept0)
-    st.enable_tier(slots)
+    st.enable_tier(slots, kv=kv)
     es = 2 if sp.dtype == "bf16" else 4
-    slice_bytes = 16 * sp.head_dim_v * es
+    slice_bytes = 16 * (sp.head_dim_v + (sp.head_dim if kv else 0)) * es
     gen = torch.Generator(device=dev).manual_seed(11)
     q = st.q.float()
     rows = []
@@ -370,7 +372,8 @@ def value_tier_leg(w, base, dev, steps: int = 8) -> dict:
     warm = rows[1:]
     res = {"slots": slots, "slice_bytes": slice_bytes,
            "hot_buffer_bytes": slots * slice_bytes,
-           "v_pool_bytes": int(st.v.numel() * st.v.element_size()),
+           "host_pool_bytes": int(st.v.numel() * st.v.element_size() +
+                                  (st.k.numel() * st.k.element_size() if kv else 0)),
            "hit_rate": round(sum(r["hits"] for r in warm) / max(1, sum(r["kept_slices"] for r in warm)), 4),
            "link_bytes_per_step": int(np.mean([r["link_bytes"] for r in warm])),
            "zero_copy_link_bytes_per_step": int(np.mean([r["zero_copy_link_bytes"] for r in warm])),
@@ -691,6 +694,7 @@ def main():
         result["graph_replay"] = graph
     if not args.no_tier and not w.spec.latent and w.spec.head_dim == w.spec.head_dim_v:
         result["value_tier"] = value_tier_leg(w, steps[0], dev)
+        result["kv_tier"] = value_tier_leg(w, steps[0], dev, kv=True)
     if dense_ms is not None:
         result["dense"] = {"ms": round(dense_ms, 5),
                            "gbs": round(ab["dense_decode"] / (dense_ms * 1e-3) / 1e9, 1),

@@ -344,6 +344,42 @@ psd_status psd_sparse_decode_tiered(const psd_shape* shape, const void* q, const
                                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * KV tier: the same with K in host memory too (AMASS page, "Two variants, one algorithm":
+ * the mem-kv residency, K and V offloaded to DRAM with only the page summaries and the
+ * called pages resident; LOCKS README, "How it works", the optional DRAM tier's mem-kv).
+ * k_host is the device address of the K cache in pinned host memory (the K layout of the
+ * shape); hot_k, [slots][16][D] elements of dtype, holds the K rows of each resident slice
+ * in the slot that holds its V in hot_v. The page statistics stay in device memory, so
+ * the selection reads no K; psd_page_meta_update refreshes the tail pages from k_host.
+ *
+ *   psd_kv_tier_stage          - psd_value_tier_stage, with each copied slice's K rows
+ *                                brought to hot_k as well; slot[s][g][e] is the slot of
+ *                                both (-1: entry e reads K and V from host memory).
+ *   psd_sparse_decode_kv_tiered - psd_sparse_decode with each entry's K and V read from
+ *                                its slot (or from host memory): the same bits as
+ *                                psd_sparse_decode over the same K and V.
+ *
+ * State, workspace sizes and reset are the value tier's (psd_value_tier_state_bytes,
+ * psd_value_tier_workspace_bytes, psd_value_tier_reset); a state serves one tier kind
+ * from its reset on. hot_k and hot_v may be null only when slots == 0 (both or neither
+ * in the attention). Errors and limits as for the value tier.
+ */
+psd_status psd_kv_tier_stage(const psd_shape* shape, const void* k_host, const void* v_host,
+                             void* hot_k, void* hot_v, void* state, int32_t slots, int32_t step,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* sel_pages, const int32_t* sel_count, int32_t b_max,
+                             int32_t* slot, uint64_t* stats, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+/* workspace: psd_decode_workspace_bytes(shape, b_max), as for psd_sparse_decode. */
+psd_status psd_sparse_decode_kv_tiered(const psd_shape* shape, const void* q, const void* k_host,
+                                       const void* v_host, const void* hot_k, const void* hot_v,
+                                       const int32_t* slot, const int32_t* block_table,
+                                       const int32_t* seq_lens, const int32_t* sel_pages,
+                                       const int32_t* sel_count, int32_t b_max, float scale,
+                                       float* out, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
  * psd_dense_decode - the same attention over every page of each sequence (baseline).
  *
  * workspace >= psd_decode_workspace_bytes(shape, shape->max_pages_per_seq) bytes.

@@ -168,6 +168,28 @@ def sparse_decode_tiered(shape: PsdShape, q, k_cache, v_host, hot, vslot, block_
                                                _stream(stream)), "psd_sparse_decode_tiered")
 
 
+def kv_tier_stage(shape: PsdShape, k_host, v_host, hot_k, hot_v, state, slots: int, step: int,
+                  block_table, seq_lens, sel_pages, sel_count, b_max: int, slot, stats,
+                  workspace, stream=None):
+    _ok(_native.lib().psd_kv_tier_stage(ctypes.byref(shape), _ptr(k_host), _ptr(v_host),
+                                        _ptr(hot_k), _ptr(hot_v), _ptr(state), slots, step,
+                                        _ptr(block_table), _ptr(seq_lens), _ptr(sel_pages),
+                                        _ptr(sel_count), b_max, _ptr(slot), _ptr(stats),
+                                        _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)), "psd_kv_tier_stage")
+
+
+def sparse_decode_kv_tiered(shape: PsdShape, q, k_host, v_host, hot_k, hot_v, slot, block_table,
+                            seq_lens, sel_pages, sel_count, b_max: int, scale: float, out,
+                            workspace, stream=None):
+    _ok(_native.lib().psd_sparse_decode_kv_tiered(
+        ctypes.byref(shape), _ptr(q), _ptr(k_host), _ptr(v_host), _ptr(hot_k), _ptr(hot_v),
+        _ptr(slot), _ptr(block_table), _ptr(seq_lens), _ptr(sel_pages), _ptr(sel_count), b_max,
+        scale, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "psd_sparse_decode_kv_tiered")
+
+
 def select_sparse_decode_workspace_bytes(shape: PsdShape, b_max: int) -> int:
     return int(_native.lib().psd_select_sparse_decode_workspace_bytes(ctypes.byref(shape), b_max))
 

@@ -819,15 +819,16 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& p, const void* q, const
 }
 
 hipError_t launch_decode_tiered(const Geo& g, const DecodePlan& p, const void* q, const void* k,
-                                const void* v, const void* hot, const int32_t* vslot,
-                                const int32_t* bt, const int32_t* lens, const int32_t* sel,
-                                const int32_t* cnt, int b_max, float scale, float* out, void* ws,
-                                hipStream_t st) {
+                                const void* v, const void* hot_k, const void* hot,
+                                const int32_t* vslot, const int32_t* bt, const int32_t* lens,
+                                const int32_t* sel, const int32_t* cnt, int b_max, float scale,
+                                float* out, void* ws, hipStream_t st) {
   if (p.latent_tiles || g.D != g.Dv || (g.D != 64 && g.D != 128) || g.G > 16)
     return hipErrorInvalidValue;
   AttnArgs a = make_attn_args(g, p, q, k, v, bt, lens, sel, cnt, b_max, scale, out, ws);
   a.vslot = vslot;
   a.hot = hot;
+  a.hot_k = hot_k;
   const bool bf = g.dtype == 1;
   hipError_t e;
   if (p.unit) {

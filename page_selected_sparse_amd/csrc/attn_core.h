@@ -59,6 +59,7 @@ struct AttnArgs {
   // it is >= 0 ([slots][16][Dv] elements), else from v through the block table.
   const int32_t* vslot = nullptr;
   const void* hot = nullptr;
+  const void* hot_k = nullptr;  // KV tier: [slices][16][D], K of the resident slices
 };
 
 constexpr int kMaxSplits = 16384;
@@ -289,7 +290,29 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
   auto issue = [&](int i, PageRegs& R) {
     if constexpr (EARLY) {
       const int blk = __builtin_amdgcn_readlane(my_blk, i);
-      if constexpr (KT) {  // instruction c: rows 4c + grp, 16 bytes at dims 8r
+      const int vs = TIER ? __builtin_amdgcn_readlane(my_vs, i) : -1;
+      if (TIER && vs >= 0 && a.hot_k) {
+        // KV tier, resident slice: K rows at [16][D] of slice vs, the same fragments
+        const int64_t row0 = (int64_t)vs * kPage;
+        if constexpr (KT) {
+#pragma unroll
+          for (int c = 0; c < NQ; ++c)
+            R.kr[c][0] = load16(static_cast<const uint16_t*>(a.hot_k) +
+                                (row0 + 4 * c + grp) * DQK + 8 * r);
+        } else {
+#pragma unroll
+          for (int c = 0; c < NQ; ++c) {
+            const int64_t off = (row0 + r) * DQK + 32 * c + 8 * grp;
+            if constexpr (BF16) {
+              R.kr[c][0] = load16(static_cast<const uint16_t*>(a.hot_k) + off);
+            } else {
+              const float* src = static_cast<const float*>(a.hot_k) + off;
+              R.kr[c][0] = *reinterpret_cast<const uint4*>(src);
+              R.kr[c][1] = *reinterpret_cast<const uint4*>(src + 4);
+            }
+          }
+        }
+      } else if constexpr (KT) {  // instruction c: rows 4c + grp, 16 bytes at dims 8r
 #pragma unroll
         for (int c = 0; c < NQ; ++c)
           R.kr[c][0] = load16(static_cast<const uint16_t*>(a.k) + (int64_t)blk * a.kbs +
@@ -298,7 +321,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int split_x, int g,
 #pragma unroll
         for (int c = 0; c < NQ; ++c) load_k(blk, c, R.kr[c][0], R.kr[c][1]);
       }
-      const int vs = TIER ? __builtin_amdgcn_readlane(my_vs, i) : -1;
       if (TIER && vs >= 0) {  // the page's V slice is resident: [16][Dv] at slice vs
 #pragma unroll
         for (int w = 0; w < NG; ++w)

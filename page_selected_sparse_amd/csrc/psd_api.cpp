@@ -240,27 +240,78 @@ psd_status psd_value_tier_reset(const psd_shape* shape, int32_t slots, void* sta
   return launched(psd::launch_tier_reset(g, slots, state, stream));
 }
 
+// The value tier (k_host and hot_k null) and the KV tier share the stage and the attention.
+static psd_status tier_stage_common(const psd_shape* shape, const void* k_host,
+                                    const void* v_host, void* hot_k, void* hot, void* state,
+                                    int32_t slots, int32_t step, const int32_t* block_table,
+                                    const int32_t* seq_lens, const int32_t* sel_pages,
+                                    const int32_t* sel_count, int32_t b_max, int32_t* slot,
+                                    uint64_t* stats, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  psd::Geo g;
+  if (check_shape(shape, &g) != PSD_OK) return PSD_ERR_INVALID_ARG;
+  if (!tier_shape(shape, &g)) return PSD_ERR_UNSUPPORTED;
+  if (slots < 0 || b_max < 1 || !v_host || !state || !block_table || !seq_lens || !sel_pages ||
+      !sel_count || !slot || !stats || (slots > 0 && !hot))
+    return PSD_ERR_INVALID_ARG;
+  if (k_host && slots > 0 && !hot_k) return PSD_ERR_INVALID_ARG;
+  if (!aligned16(v_host) || (hot && !aligned16(hot)) || !aligned16(state))
+    return PSD_ERR_INVALID_ARG;
+  if ((k_host && !aligned16(k_host)) || (hot_k && !aligned16(hot_k))) return PSD_ERR_INVALID_ARG;
+  const psd::TierLayout t = psd::tier_layout(g, slots, b_max);
+  if (!workspace || workspace_bytes < t.work_bytes || !aligned16(workspace))
+    return PSD_ERR_WORKSPACE;
+  return launched(psd::launch_tier_stage(g, slots, step, k_host, v_host, k_host ? hot_k : nullptr,
+                                         hot, state, block_table, seq_lens, sel_pages, sel_count,
+                                         b_max, slot, reinterpret_cast<unsigned long long*>(stats),
+                                         workspace, stream));
+}
+
 psd_status psd_value_tier_stage(const psd_shape* shape, const void* v_host, void* hot,
                                 void* state, int32_t slots, int32_t step,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 const int32_t* sel_pages, const int32_t* sel_count,
                                 int32_t b_max, int32_t* vslot, uint64_t* stats, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
+  return tier_stage_common(shape, nullptr, v_host, nullptr, hot, state, slots, step, block_table,
+                           seq_lens, sel_pages, sel_count, b_max, vslot, stats, workspace,
+                           workspace_bytes, stream);
+}
+
+psd_status psd_kv_tier_stage(const psd_shape* shape, const void* k_host, const void* v_host,
+                             void* hot_k, void* hot_v, void* state, int32_t slots, int32_t step,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* sel_pages, const int32_t* sel_count, int32_t b_max,
+                             int32_t* slot, uint64_t* stats, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (!k_host) return PSD_ERR_INVALID_ARG;
+  return tier_stage_common(shape, k_host, v_host, hot_k, hot_v, state, slots, step, block_table,
+                           seq_lens, sel_pages, sel_count, b_max, slot, stats, workspace,
+                           workspace_bytes, stream);
+}
+
+static psd_status tiered_common(const psd_shape* shape, const void* q, const void* k_cache,
+                                const void* v_host, const void* hot_k, const void* hot,
+                                const int32_t* slot, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* sel_pages,
+                                const int32_t* sel_count, int32_t b_max, float scale, float* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   psd::Geo g;
   if (check_shape(shape, &g) != PSD_OK) return PSD_ERR_INVALID_ARG;
   if (!tier_shape(shape, &g)) return PSD_ERR_UNSUPPORTED;
-  if (slots < 0 || b_max < 1 || !v_host || !state || !block_table || !seq_lens || !sel_pages ||
-      !sel_count || !vslot || !stats || (slots > 0 && !hot))
+  if (!q || !k_cache || !v_host || !slot || !block_table || !seq_lens || !sel_pages ||
+      !sel_count || !out || b_max < 1)
     return PSD_ERR_INVALID_ARG;
-  if (!aligned16(v_host) || (hot && !aligned16(hot)) || !aligned16(state))
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_host) || (hot && !aligned16(hot)) ||
+      (hot_k && !aligned16(hot_k)) || !aligned16(out))
     return PSD_ERR_INVALID_ARG;
-  const psd::TierLayout t = psd::tier_layout(g, slots, b_max);
-  if (!workspace || workspace_bytes < t.work_bytes || !aligned16(workspace))
-    return PSD_ERR_WORKSPACE;
-  return launched(psd::launch_tier_stage(g, slots, step, v_host, hot, state, block_table, seq_lens,
-                                         sel_pages, sel_count, b_max, vslot,
-                                         reinterpret_cast<unsigned long long*>(stats), workspace,
-                                         stream));
+  if (!(scale > 0.f) || scale == __builtin_inff()) return PSD_ERR_INVALID_ARG;
+  psd::DecodePlan p;
+  if (!psd::plan_decode(g, b_max, false, &p)) return PSD_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < p.bytes || !aligned16(workspace)) return PSD_ERR_WORKSPACE;
+  return launched(psd::launch_decode_tiered(g, p, q, k_cache, v_host, hot_k, hot, slot,
+                                            block_table, seq_lens, sel_pages, sel_count, b_max,
+                                            scale, out, workspace, stream));
 }
 
 psd_status psd_sparse_decode_tiered(const psd_shape* shape, const void* q, const void* k_cache,
@@ -269,22 +320,22 @@ psd_status psd_sparse_decode_tiered(const psd_shape* shape, const void* q, const
                                     const int32_t* sel_pages, const int32_t* sel_count,
                                     int32_t b_max, float scale, float* out, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
-  psd::Geo g;
-  if (check_shape(shape, &g) != PSD_OK) return PSD_ERR_INVALID_ARG;
-  if (!tier_shape(shape, &g)) return PSD_ERR_UNSUPPORTED;
-  if (!q || !k_cache || !v_host || !vslot || !block_table || !seq_lens || !sel_pages ||
-      !sel_count || !out || b_max < 1)
-    return PSD_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_host) || (hot && !aligned16(hot)) ||
-      !aligned16(out))
-    return PSD_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || scale == __builtin_inff()) return PSD_ERR_INVALID_ARG;
-  psd::DecodePlan p;
-  if (!psd::plan_decode(g, b_max, false, &p)) return PSD_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < p.bytes || !aligned16(workspace)) return PSD_ERR_WORKSPACE;
-  return launched(psd::launch_decode_tiered(g, p, q, k_cache, v_host, hot, vslot, block_table,
-                                            seq_lens, sel_pages, sel_count, b_max, scale, out,
-                                            workspace, stream));
+  return tiered_common(shape, q, k_cache, v_host, nullptr, hot, vslot, block_table, seq_lens,
+                       sel_pages, sel_count, b_max, scale, out, workspace, workspace_bytes,
+                       stream);
+}
+
+psd_status psd_sparse_decode_kv_tiered(const psd_shape* shape, const void* q, const void* k_host,
+                                       const void* v_host, const void* hot_k, const void* hot_v,
+                                       const int32_t* slot, const int32_t* block_table,
+                                       const int32_t* seq_lens, const int32_t* sel_pages,
+                                       const int32_t* sel_count, int32_t b_max, float scale,
+                                       float* out, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  if ((hot_k == nullptr) != (hot_v == nullptr)) return PSD_ERR_INVALID_ARG;
+  return tiered_common(shape, q, k_host, v_host, hot_k, hot_v, slot, block_table, seq_lens,
+                       sel_pages, sel_count, b_max, scale, out, workspace, workspace_bytes,
+                       stream);
 }
 
 // select_pages then sparse_decode, as one launch when the plans allow; with `refresh`,

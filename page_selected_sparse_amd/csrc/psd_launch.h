@@ -94,11 +94,12 @@ hipError_t launch_decode(const Geo& g, const DecodePlan& plan, const void* q, co
 // The same attention with V from the value tier: entry e of unit u reads its V from hot
 // slice vslot[u][e] ([slots][16][Dv]) when >= 0, else from v (host pool) by the block
 // table. GQA shapes with D == Dv in {64, 128} and groups of up to 16 heads.
+// hot_k: the KV tier's K hot buffer (K of a resident entry read from its slot), else null.
 hipError_t launch_decode_tiered(const Geo& g, const DecodePlan& plan, const void* q,
-                                const void* k, const void* v, const void* hot,
-                                const int32_t* vslot, const int32_t* bt, const int32_t* lens,
-                                const int32_t* sel, const int32_t* cnt, int b_max, float scale,
-                                float* out, void* ws, hipStream_t st);
+                                const void* k, const void* v, const void* hot_k,
+                                const void* hot, const int32_t* vslot, const int32_t* bt,
+                                const int32_t* lens, const int32_t* sel, const int32_t* cnt,
+                                int b_max, float scale, float* out, void* ws, hipStream_t st);
 
 // ---- value tier (V in host memory, resident hot buffer) ----------------------------------
 struct TierLayout {
@@ -109,10 +110,12 @@ struct TierLayout {
 };
 TierLayout tier_layout(const Geo& g, int slots, int b_max);
 hipError_t launch_tier_reset(const Geo& g, int slots, void* state, hipStream_t st);
-hipError_t launch_tier_stage(const Geo& g, int slots, int step, const void* v, void* hot,
-                             void* state, const int32_t* bt, const int32_t* lens,
-                             const int32_t* sel, const int32_t* cnt, int b_max, int32_t* vslot,
-                             unsigned long long* stats, void* ws, hipStream_t st);
+// k / hot_k: the KV tier's host K pool and K hot buffer, or null for the value tier.
+hipError_t launch_tier_stage(const Geo& g, int slots, int step, const void* k, const void* v,
+                             void* hot_k, void* hot, void* state, const int32_t* bt,
+                             const int32_t* lens, const int32_t* sel, const int32_t* cnt,
+                             int b_max, int32_t* vslot, unsigned long long* stats, void* ws,
+                             hipStream_t st);
 
 // ---- selection and attention in one launch -------------------------------------------------
 // Applies when both plans take one workgroup per unit (DPP scoring of groups of up to 8

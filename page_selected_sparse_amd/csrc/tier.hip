@@ -1,4 +1,5 @@
-// Value tier: V in pinned host memory, with a bounded resident buffer in device memory.
+// Value tier: V in pinned host memory, with a bounded resident buffer in device memory;
+// and the KV tier, the same with K in host memory too (each resident slice holds both).
 //
 // The value cache can live in host DRAM, mapped for the device, while a bounded hot
 // buffer in HBM holds the V slices that decode steps keep calling, and only the slices a
@@ -20,7 +21,9 @@
 //      their old slices, and lists the copies; a slice missed by several entries gets one
 //      slot; when the slots run out, the remaining entries read V from host memory;
 //   4. the copies: each listed slice's 16 rows go from the host pool to its slot.
-// The attention then reads each entry's V from its slot (psd_sparse_decode_tiered).
+// The attention then reads each entry's V from its slot (psd_sparse_decode_tiered); in the
+// KV tier the copies also bring the slice's K rows into a K hot buffer with the same slots,
+// and the attention reads K from there too (psd_sparse_decode_kv_tiered).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,6 +36,8 @@ namespace {
 struct TierArgs {
   const void* v;  // host pool (device-mapped), the V layout of the shape
   void* hot;      // [slots][16][Dv]
+  const void* k;  // KV tier: host K pool (device-mapped), the K layout of the shape; else null
+  void* hot_k;    // KV tier: [slots][16][D]
   const int32_t* bt;
   const int32_t* lens;
   const int32_t* sel;
@@ -46,8 +51,8 @@ struct TierArgs {
   int32_t* freelist;  // [slots]
   int32_t* ctl;       // [8]: 0 misses, 1 copies, 2 hits, 3 overflow
   unsigned long long* stats;  // [4] out: hits, misses, copies, entries read from host
-  int64_t vbs, vts, vhs;
-  int B, Hkv, max_pages, b_max, num_blocks, Dv, es, slots, step;
+  int64_t vbs, vts, vhs, kbs, kts, khs;
+  int B, Hkv, max_pages, b_max, num_blocks, D, Dv, es, slots, step;
 };
 
 __global__ __launch_bounds__(64) void tier_begin_kernel(TierArgs a) {
@@ -177,24 +182,33 @@ __global__ __launch_bounds__(1024) void tier_alloc_kernel(TierArgs a) {
   }
 }
 
-// The copies: one wave per listed slot at a time, 16 bytes per lane per row piece.
+// The 16 rows of one slice, from a pool with strides (bs, ts, hs) to a slot of `cols`
+// elements per row: 16 bytes per lane per row piece.
+__device__ __forceinline__ void copy_slice(const void* pool, void* hot, int f, int blk, int g,
+                                           int64_t bs, int64_t ts, int64_t hs, int cols, int es,
+                                           int lane) {
+  const int row_bytes = cols * es, chunks = row_bytes / 16;
+  const unsigned char* src =
+      static_cast<const unsigned char*>(pool) + ((int64_t)blk * bs + (int64_t)g * hs) * es;
+  unsigned char* dst = static_cast<unsigned char*>(hot) + (int64_t)f * kPage * row_bytes;
+  for (int piece = lane; piece < kPage * chunks; piece += 64) {
+    const int t = piece / chunks, c = piece - t * chunks;
+    const uint4 x = *reinterpret_cast<const uint4*>(src + (int64_t)t * ts * es + c * 16);
+    *reinterpret_cast<uint4*>(dst + (int64_t)t * row_bytes + c * 16) = x;
+  }
+}
+
+// The copies: one wave per listed slot at a time (V, and K in the KV tier).
 __global__ __launch_bounds__(256) void tier_copy_kernel(TierArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), waves = gridDim.x * 4;
   const int njobs = a.ctl[1];
-  const int row_bytes = a.Dv * a.es, chunks = row_bytes / 16;  // 16-byte pieces per row
   for (int j = wave; j < njobs; j += waves) {
     const int f = a.jobs[j];
     const int key = a.owner[f];
     const int blk = key / a.Hkv, g = key - blk * a.Hkv;
-    const unsigned char* src = static_cast<const unsigned char*>(a.v) +
-                               ((int64_t)blk * a.vbs + (int64_t)g * a.vhs) * a.es;
-    unsigned char* dst = static_cast<unsigned char*>(a.hot) + (int64_t)f * kPage * row_bytes;
-    for (int piece = lane; piece < kPage * chunks; piece += 64) {
-      const int t = piece / chunks, c = piece - t * chunks;
-      const uint4 x = *reinterpret_cast<const uint4*>(src + (int64_t)t * a.vts * a.es + c * 16);
-      *reinterpret_cast<uint4*>(dst + (int64_t)t * row_bytes + c * 16) = x;
-    }
+    copy_slice(a.v, a.hot, f, blk, g, a.vbs, a.vts, a.vhs, a.Dv, a.es, lane);
+    if (a.k) copy_slice(a.k, a.hot_k, f, blk, g, a.kbs, a.kts, a.khs, a.D, a.es, lane);
   }
 }
 
@@ -239,16 +253,19 @@ hipError_t launch_tier_reset(const Geo& g, int slots, void* state, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_tier_stage(const Geo& g, int slots, int step, const void* v, void* hot,
-                             void* state, const int32_t* bt, const int32_t* lens,
-                             const int32_t* sel, const int32_t* cnt, int b_max, int32_t* vslot,
-                             unsigned long long* stats, void* ws, hipStream_t st) {
+hipError_t launch_tier_stage(const Geo& g, int slots, int step, const void* k, const void* v,
+                             void* hot_k, void* hot, void* state, const int32_t* bt,
+                             const int32_t* lens, const int32_t* sel, const int32_t* cnt,
+                             int b_max, int32_t* vslot, unsigned long long* stats, void* ws,
+                             hipStream_t st) {
   const TierLayout t = tier_layout(g, slots, b_max);
   unsigned char* p = static_cast<unsigned char*>(state);
   unsigned char* w = static_cast<unsigned char*>(ws);
   TierArgs a;
   a.v = v;
   a.hot = hot;
+  a.k = k;
+  a.hot_k = hot_k;
   a.bt = bt;
   a.lens = lens;
   a.sel = sel;
@@ -265,6 +282,10 @@ hipError_t launch_tier_stage(const Geo& g, int slots, int step, const void* v, v
   a.vbs = g.vbs;
   a.vts = g.vts;
   a.vhs = g.vhs;
+  a.kbs = g.kbs;
+  a.kts = g.kts;
+  a.khs = g.khs;
+  a.D = g.D;
   a.B = g.B;
   a.Hkv = g.Hkv;
   a.max_pages = g.max_pages;

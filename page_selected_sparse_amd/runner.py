@@ -26,22 +26,28 @@ def _to_device_bits(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
 class DecodeStep:
     def __init__(self, q: torch.Tensor, cache: torch.Tensor, block_table: torch.Tensor,
                  seq_lens: torch.Tensor, budgets: torch.Tensor, head_dim_v: int,
-                 latent: bool, b_max: int | None = None, v_host: bool = False):
+                 latent: bool, b_max: int | None = None, v_host: bool = False,
+                 kv_host: bool = False):
         """q [B, H_q, D]; cache [2, NB, 16, H_kv, D] (or [1, ...] when ``latent``: V is the
         first ``head_dim_v`` dims of K); block_table [B, max_pages] int32; seq_lens and
         budgets [B] int32. All on the same HIP device. ``v_host`` moves V to pinned host
         memory (the value tier in host DRAM): the attention then reads only the kept
-        pages' V rows over the host link."""
+        pages' V rows over the host link. ``kv_host`` moves K as well (the page statistics
+        stay in device memory)."""
         self.q, self.cache = q, cache
         self.block_table, self.seq_lens, self.budgets = block_table, seq_lens, budgets
         self.k = cache[0]
         self.v = cache[0][..., :head_dim_v] if latent else cache[1]
-        if v_host:
+        if v_host or kv_host:
             if latent:
                 raise ValueError("a latent cache holds V inside K: V cannot move alone")
             host = torch.empty(self.v.shape, dtype=self.v.dtype, pin_memory=True)
             host.copy_(self.v)
             self.v = host
+        if kv_host:
+            host = torch.empty(self.k.shape, dtype=self.k.dtype, pin_memory=True)
+            host.copy_(self.k)
+            self.k = host
         self.shape = api.make_shape(q, self.k, self.v, block_table, head_dim_v)
         B, Hq, D = q.shape
         NB, _, Hkv, _ = self.k.shape
@@ -74,13 +80,14 @@ class DecodeStep:
     @classmethod
     def from_arrays(cls, q: np.ndarray, cache: np.ndarray, block_table: np.ndarray,
                     seq_lens: np.ndarray, budgets: np.ndarray, dtype: str, head_dim_v: int,
-                    latent: bool, device="cuda", b_max: int | None = None, v_host: bool = False):
+                    latent: bool, device="cuda", b_max: int | None = None, v_host: bool = False,
+                    kv_host: bool = False):
         dev = torch.device(device)
         return cls(_to_device_bits(q, dtype, dev), _to_device_bits(cache, dtype, dev),
                    torch.from_numpy(np.ascontiguousarray(block_table, dtype=np.int32)).to(dev),
                    torch.from_numpy(np.ascontiguousarray(seq_lens, dtype=np.int32)).to(dev),
                    torch.from_numpy(np.ascontiguousarray(budgets, dtype=np.int32)).to(dev),
-                   head_dim_v, latent, b_max, v_host)
+                   head_dim_v, latent, b_max, v_host, kv_host)
 
     # -- the calls ------------------------------------------------------------------------
     def build_meta(self, stream=None):
@@ -149,13 +156,17 @@ class DecodeStep:
                                 self.sel_pages, self.sel_count, self.out, stream)
 
     # -- value tier: V in (pinned host) memory, a resident hot buffer in device memory ------
-    def enable_tier(self, slots: int):
+    def enable_tier(self, slots: int, kv: bool = False):
         """Keep up to ``slots`` (block, KV head) V slices resident in a device hot buffer;
         each tiered step copies only the kept slices that are not resident (from ``v``,
-        pinned host memory when the step was built with ``v_host``)."""
+        pinned host memory when the step was built with ``v_host``). With ``kv`` (the KV
+        tier) each resident slice holds its K rows too, in ``tier_hot_k``."""
         dev = self.q.device
         B, Hkv = self.sel_count.shape
         dv = self.v.shape[-1]
+        self.tier_kv = bool(kv)
+        self.tier_hot_k = (torch.empty((slots, 16, self.k.shape[-1]), dtype=self.q.dtype,
+                                       device=dev) if kv and slots > 0 else None)
         st_bytes = api.value_tier_state_bytes(self.shape, slots)
         ws_bytes = api.value_tier_workspace_bytes(self.shape, self.b_max, slots)
         if st_bytes == 0 or ws_bytes == 0:
@@ -173,12 +184,24 @@ class DecodeStep:
     def tier_stage(self, stream=None):
         """Slots for this step's kept V slices (after ``select``); copies the missed ones."""
         self.tier_step += 1
+        if self.tier_kv:
+            api.kv_tier_stage(self.shape, self.k, self.v, self.tier_hot_k, self.tier_hot,
+                              self.tier_state, self.tier_slots, self.tier_step, self.block_table,
+                              self.seq_lens, self.sel_pages, self.sel_count, self.b_max,
+                              self.tier_vslot, self.tier_stats, self.tier_ws, stream)
+            return
         api.value_tier_stage(self.shape, self.v, self.tier_hot, self.tier_state, self.tier_slots,
                              self.tier_step, self.block_table, self.seq_lens, self.sel_pages,
                              self.sel_count, self.b_max, self.tier_vslot, self.tier_stats,
                              self.tier_ws, stream)
 
     def sparse_tiered(self, stream=None):
+        if self.tier_kv:
+            api.sparse_decode_kv_tiered(self.shape, self.q, self.k, self.v, self.tier_hot_k,
+                                        self.tier_hot, self.tier_vslot, self.block_table,
+                                        self.seq_lens, self.sel_pages, self.sel_count,
+                                        self.b_max, self.scale, self.out, self.ws_decode, stream)
+            return
         api.sparse_decode_tiered(self.shape, self.q, self.k, self.v, self.tier_hot,
                                  self.tier_vslot, self.block_table, self.seq_lens,
                                  self.sel_pages, self.sel_count, self.b_max, self.scale,

@@ -70,10 +70,11 @@ def meta_f64(step: DecodeStep, dtype: str) -> np.ndarray:
     return meta.transpose(0, 1, 3, 2, 4).reshape(nb, hkv, 2, nc * cd)
 
 
-def make_step(w: synth.Workload, b_max=None, cache=None, v_host=False, guard=True):
+def make_step(w: synth.Workload, b_max=None, cache=None, v_host=False, guard=True,
+              kv_host=False):
     step = DecodeStep.from_arrays(w.q, w.cache if cache is None else cache, w.block_table,
                                   w.seq_lens, w.budgets, w.spec.dtype, w.spec.head_dim_v,
-                                  w.spec.latent, b_max=b_max, v_host=v_host)
+                                  w.spec.latent, b_max=b_max, v_host=v_host, kv_host=kv_host)
     bands = guard_buffers(step) if guard else {}
     return step, bands
 

@@ -293,3 +293,20 @@ def test_value_tier_queries_and_checks(native):
         ctypes.byref(sh), f, f, f, f, vslot, f, f, f, f, 12, 0.1, f, f, nbytes, None)
     assert dec(None, 1 << 30) == -1
     assert dec(f, 8) == -3
+    # the KV tier: K pool required, a K hot buffer beside the V one whenever slots exist
+    kvstage = lambda k, hot_k, hot_v, slots, ws, nbytes: lib.psd_kv_tier_stage(
+        ctypes.byref(sh), k, f, hot_k, hot_v, f, slots, 1, f, f, f, f, 12, f, f, ws, nbytes,
+        None)
+    assert kvstage(None, f, f, 10, f, need) == -1
+    assert kvstage(f, None, f, 10, f, need) == -1
+    assert kvstage(f, f, None, 10, f, need) == -1
+    assert kvstage(f, f, f, 10, None, need) == -3
+    assert kvstage(f, f, f, 10, f, need - 1) == -3
+    assert lib.psd_kv_tier_stage(ctypes.byref(latent), f, f, f, f, f, 10, 1, f, f, f, f, 12, f,
+                                 f, f, 1 << 30, None) == -2
+    kvdec = lambda k, hot_k, hot_v, nbytes: lib.psd_sparse_decode_kv_tiered(
+        ctypes.byref(sh), f, k, f, hot_k, hot_v, f, f, f, f, f, 12, 0.1, f, f, nbytes, None)
+    assert kvdec(None, f, f, 1 << 30) == -1
+    assert kvdec(f, f, None, 1 << 30) == -1  # both hot buffers or neither
+    assert kvdec(f, None, f, 1 << 30) == -1
+    assert kvdec(f, f, f, 8) == -3

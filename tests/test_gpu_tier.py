@@ -1,8 +1,10 @@
 """Value tier with a resident hot buffer (psd_value_tier_stage + psd_sparse_decode_tiered),
-V in pinned host memory, over consecutive decode steps whose queries drift: outputs are the
-same bits as the attention reading V straight from host memory, and the oracle's; every
-resident slot holds its slice's rows; the counts add up; with no slots every entry reads
-from host, with few slots the overflow reads from host."""
+V in pinned host memory, and the KV tier (psd_kv_tier_stage + psd_sparse_decode_kv_tiered),
+K and V in pinned host memory, over consecutive decode steps whose queries drift: outputs
+are the same bits as the attention reading K and V straight from where they live, and the
+oracle's; every resident slot holds its slice's rows (K and V for the KV tier); the counts
+add up; with no slots every entry reads from host, with few slots the overflow reads from
+host."""
 import dataclasses
 
 import numpy as np
@@ -51,18 +53,21 @@ def _q_tensor(raw: np.ndarray, dtype: str, dev) -> torch.Tensor:
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("tier", ["v", "kv"])
 @pytest.mark.parametrize("mode", ["ample", "tight", "none"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_value_tier_over_steps(name, mode):
+def test_value_tier_over_steps(name, mode, tier):
     w = synth.make_workload(CASES[name])
-    print(f"[gpu] value tier {name} {mode}", flush=True)
-    step, bands = make_step(w, v_host=True, guard=False)
+    kv = tier == "kv"
+    print(f"[gpu] {tier} tier {name} {mode}", flush=True)
+    step, bands = make_step(w, v_host=True, guard=False, kv_host=kv)
     step.build_meta()
     step.select()
     kept = int(step.sel_count.clamp(min=0).sum())
     slots = {"ample": 2 * kept, "tight": max(1, kept // 3), "none": 0}[mode]
-    step.enable_tier(slots)
+    step.enable_tier(slots, kv=kv)
     v_host = step.v  # pinned host V pool [NB, 16, H_kv, D_v]
+    k_host = step.k  # the K pool: pinned host memory for the KV tier
     Hkv = w.spec.num_kv_heads
     for t in range(3):
         q_raw = _drifted_q(w, t)
@@ -73,7 +78,7 @@ def test_value_tier_over_steps(name, mode):
         torch.cuda.synchronize()
         out_tier = step.out.clone()
         step.out.fill_(123.0)
-        step.sparse()  # V straight from host memory
+        step.sparse()  # V (and K for the KV tier) straight from host memory
         torch.cuda.synchronize()
         assert torch.equal(out_tier.view(torch.int32), step.out.view(torch.int32)), f"step {t}"
         cnt = step.sel_count.cpu().numpy().clip(min=0)
@@ -98,6 +103,7 @@ def test_value_tier_over_steps(name, mode):
         # every slot an entry reads holds that entry's slice (its block's rows of head g)
         if slots:
             hot = step.tier_hot.cpu()
+            hot_k = step.tier_hot_k.cpu() if kv else None
             used = {}
             for s, g, e in entries:
                 slot = int(vslot[s, g, e])
@@ -108,6 +114,9 @@ def test_value_tier_over_steps(name, mode):
                 bits = torch.int16 if w.spec.dtype == "bf16" else torch.int32  # NaN rows too
                 assert torch.equal(hot[slot].view(bits), v_host[blk, :, g, :].view(bits)), \
                     (s, g, e, slot)
+                if kv:
+                    assert torch.equal(hot_k[slot].view(bits), k_host[blk, :, g, :].view(bits)), \
+                        ("K", s, g, e, slot)
         if t in (0, 2):  # the oracle on the drifted queries
             wt = dataclasses.replace(w, q=q_raw)
             seqs = range(w.spec.batch) if w.spec.batch <= 8 else range(0, w.spec.batch, 5)
