@@ -952,11 +952,25 @@ void select_attn_kernel(SelArgs a, AttnArgs aa, int list_off, int kt_off, int kt
     count = write_list_header<1024>(list, ui, a.b_max);
     __syncthreads();
   }
+  // The tail refresh feeds only later steps (a tail page is always kept, never scored),
+  // so of each pair of sequences (s, s ^ 1) the shorter one's workgroup refreshes both
+  // tails of head g and the longer one's none: the longest units end without it.
   auto refresh_tail = [&]() {
     if constexpr (REFRESH) {
-      if ((threadIdx.x >> 6) == 15)  // all 16 rows at once: the attention's registers are free
-        refresh_tail_page<BF16, kPage>(aa.k, meta_w, a.bt, a.lens, a.max_pages, s, g, a.Hkv, D,
-                                       kbs, kts, khs, threadIdx.x & 63, 64);
+      if ((threadIdx.x >> 6) == 15) {  // all 16 rows at once: the attention's registers are free
+        const int ps = s ^ 1;
+        bool own = true, pair = false;
+        if (ps < (int)gridDim.y) {
+          const int ls = a.lens[s], lp = a.lens[ps];
+          own = pair = ls < lp || (ls == lp && (s & 1) == 0);
+        }
+        if (own)
+          refresh_tail_page<BF16, kPage>(aa.k, meta_w, a.bt, a.lens, a.max_pages, s, g, a.Hkv,
+                                         D, kbs, kts, khs, threadIdx.x & 63, 64);
+        if (pair)
+          refresh_tail_page<BF16, kPage>(aa.k, meta_w, a.bt, a.lens, a.max_pages, ps, g, a.Hkv,
+                                         D, kbs, kts, khs, threadIdx.x & 63, 64);
+      }
     }
   };
   attn_body<BF16, D, D, 1, 16, decltype(refresh_tail), false, KT>(aa, 0, g, s, list, count,
