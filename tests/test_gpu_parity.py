@@ -37,6 +37,11 @@ SMALL = {
     "group8": synth.small_spec(num_q_heads=16, num_kv_heads=2),
     "group16": synth.small_spec(num_q_heads=16, num_kv_heads=1),
     "group32": synth.small_spec(num_q_heads=64, num_kv_heads=2),
+    # split-K attention workgroups of 3 and 8 waves (48- and 128-head groups), each wave
+    # with its own K tile
+    "group48": synth.small_spec(num_q_heads=96, num_kv_heads=2),
+    "group128": synth.small_spec(batch=2, num_q_heads=128, num_kv_heads=1,
+                                 seq_lens=(2000, 301), max_len=2000),
     "d64_bf16": synth.small_spec(head_dim=64, head_dim_v=64),
     "d64_f32": synth.small_spec(head_dim=64, head_dim_v=64, dtype="f32"),
     "d128_f32": synth.small_spec(dtype="f32", seq_lens=(500, 37, 1200), max_len=1200),
