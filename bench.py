@@ -36,6 +36,9 @@ Prints one JSON line. Besides the contract fields it carries:
                 step time (--no-tier skips it)
   kv_tier       the same with K in pinned host memory too (the KV tier: each resident
                 slice holds its K and V rows)
+  walks         the step's reads with no arithmetic (psd_diag_walk), on the same rotated
+                copies: the kept pages' K and V rows and the candidate statistics
+                records, with their GB/s (--no-walk skips them)
 """
 from __future__ import annotations
 
@@ -424,6 +427,8 @@ def measure_config(name: str, args, dev) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--no-walk", action="store_true",
+                    help="skip the memory walks (the step's reads with no arithmetic)")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="ragged_b32_32k")
@@ -618,6 +623,12 @@ def main():
                  "matches_eager": bool(same)}
         del g
 
+    # The step's reads with no arithmetic (psd_diag_walk): the kept pages' K and V rows,
+    # and the candidate pages' statistics records, on the same rotated copies.
+    walk_ms = None
+    if not args.no_walk:
+        walk_ms = (timed(lambda st: st.walk(0), args.steps), timed(lambda st: st.walk(1), args.steps))
+
     if args.calibrate_copy:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)
@@ -688,6 +699,21 @@ def main():
         v_bytes = v_tok * w.spec.head_dim_v * es
         result["host_link"] = {"v_bytes_per_step": v_bytes,
                                "gbs": round(v_bytes / (ms_step * 1e-3) / 1e9, 2)}
+    if walk_ms is not None:
+        es = 2 if w.spec.dtype == "bf16" else 4
+        n = (w.seq_lens.astype(np.int64) + 15) // 16
+        kept = int(np.clip(sel_counts, 0, None).sum())
+        row = w.spec.head_dim + (0 if w.spec.latent else w.spec.head_dim_v)
+        kv_bytes = kept * 16 * row * es
+        st_bytes = int(np.maximum(n - 2, 0).sum()) * w.spec.num_kv_heads * 2 * w.spec.head_dim * es
+        result["walks"] = {
+            "kv_ms": round(walk_ms[0], 5), "kv_bytes": kv_bytes,
+            "kv_gbs": round(kv_bytes / (walk_ms[0] * 1e-3) / 1e9, 1),
+            "stats_ms": round(walk_ms[1], 5), "stats_bytes": st_bytes,
+            "stats_gbs": round(st_bytes / (walk_ms[1] * 1e-3) / 1e9, 1),
+            "note": "the step's reads with no arithmetic (psd_diag_walk): kv = the kept "
+                    "pages' K and V rows (what sparse_decode reads), stats = every candidate "
+                    "page's statistics record (what the scoring reads)"}
     if cov is not None:
         result["coverage_select"] = cov
     if graph is not None:

@@ -380,6 +380,29 @@ psd_status psd_sparse_decode_kv_tiered(const psd_shape* shape, const void* q, co
                                        hipStream_t stream);
 
 /*
+ * psd_diag_walk - diagnostic: the decode step's memory reads with no arithmetic, to
+ * measure what the memory system gives their access patterns on this GPU (the practical
+ * ceiling of the kernels that make them). Not part of the method.
+ *
+ *   kind 0: every kept page's K and V rows of every (sequence, KV head) unit
+ *           (sel_pages / sel_count as psd_sparse_decode takes them), one 1024-thread
+ *           workgroup per unit, 16 bytes per lane per load (whole 256-byte rows at
+ *           D = 128 bf16); a latent cache (v_cache = k_cache, same strides) walks K only.
+ *   kind 1: the statistics record of every candidate page 1 .. n - 2 of every unit (meta
+ *           as psd_page_meta_update writes it), 128-byte lines of 8 pages per load.
+ * Every 32-bit word a unit reads is folded by XOR into checksum[s * H_kv + g] (device,
+ * B * H_kv uint32, all written), so a test can check that exactly those bytes were read.
+ * Shapes:
+ * 16-byte pieces per K row of 8, 16, 32 (with V rows of the same size) or 72 (latent);
+ * others give PSD_ERR_UNSUPPORTED. Pointers not needed by the kind may be null.
+ */
+psd_status psd_diag_walk(const psd_shape* shape, int32_t kind, const void* k_cache,
+                         const void* v_cache, const void* meta, const int32_t* block_table,
+                         const int32_t* seq_lens, const int32_t* sel_pages,
+                         const int32_t* sel_count, int32_t b_max, uint32_t* checksum,
+                         hipStream_t stream);
+
+/*
  * psd_dense_decode - the same attention over every page of each sequence (baseline).
  *
  * workspace >= psd_decode_workspace_bytes(shape, shape->max_pages_per_seq) bytes.

@@ -59,6 +59,8 @@ SIGNATURES = {
     "psd_sparse_decode_tiered": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_i32, c_float, c_void_p, c_void_p, c_size, c_void_p]),
+    "psd_diag_walk": (c_i32, [c_void_p, c_i32, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p]),
     "psd_kv_tier_stage": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_i32, c_i32, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
                                   c_void_p, c_void_p, c_void_p, c_size, c_void_p]),

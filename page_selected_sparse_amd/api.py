@@ -190,6 +190,17 @@ def sparse_decode_kv_tiered(shape: PsdShape, q, k_host, v_host, hot_k, hot_v, sl
         _stream(stream)), "psd_sparse_decode_kv_tiered")
 
 
+def diag_walk(shape: PsdShape, kind: int, k_cache, v_cache, meta, block_table, seq_lens,
+              sel_pages, sel_count, b_max: int, checksum, stream=None):
+    """Diagnostic: the step's reads with no arithmetic (kind 0: kept K/V rows; kind 1:
+    candidate statistics records), XOR-folded per unit into ``checksum`` ([B * H_kv]
+    uint32 on the device)."""
+    _ok(_native.lib().psd_diag_walk(ctypes.byref(shape), int(kind), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(meta), _ptr(block_table), _ptr(seq_lens),
+                                    _ptr(sel_pages), _ptr(sel_count), int(b_max), _ptr(checksum),
+                                    _stream(stream)), "psd_diag_walk")
+
+
 def select_sparse_decode_workspace_bytes(shape: PsdShape, b_max: int) -> int:
     return int(_native.lib().psd_select_sparse_decode_workspace_bytes(ctypes.byref(shape), b_max))
 

@@ -212,6 +212,31 @@ psd_status psd_dense_decode(const psd_shape* shape, const void* q, const void* k
                        stream);
 }
 
+// ---- diagnostic memory walks ----------------------------------------------------------------
+psd_status psd_diag_walk(const psd_shape* shape, int32_t kind, const void* k_cache,
+                         const void* v_cache, const void* meta, const int32_t* block_table,
+                         const int32_t* seq_lens, const int32_t* sel_pages,
+                         const int32_t* sel_count, int32_t b_max, uint32_t* checksum,
+                         hipStream_t stream) {
+  psd::Geo g;
+  psd_status st = check_shape(shape, &g);
+  if (st != PSD_OK) return st;
+  if ((kind != 0 && kind != 1) || !block_table || !seq_lens || !checksum)
+    return PSD_ERR_INVALID_ARG;
+  if (kind == 0 && (!k_cache || !v_cache || !sel_pages || !sel_count || b_max < 1))
+    return PSD_ERR_INVALID_ARG;
+  if (kind == 1 && !meta) return PSD_ERR_INVALID_ARG;
+  if ((k_cache && !aligned16(k_cache)) || (v_cache && !aligned16(v_cache)) ||
+      (meta && !aligned16(meta)))
+    return PSD_ERR_INVALID_ARG;
+  if (kind == 0 && (st = check_strides(g, true)) != PSD_OK) return st;
+  const bool latent = k_cache == v_cache && g.kbs == g.vbs && g.kts == g.vts && g.khs == g.vhs &&
+                      g.Dv <= g.D;
+  if (!psd::walk_supported(g, latent)) return PSD_ERR_UNSUPPORTED;
+  return launched(psd::launch_walk(g, kind, latent, k_cache, v_cache, meta, block_table,
+                                   seq_lens, sel_pages, sel_count, b_max, checksum, stream));
+}
+
 // ---- value tier ----------------------------------------------------------------------------
 static bool tier_shape(const psd_shape* shape, psd::Geo* g) {
   if (check_shape(shape, g) != PSD_OK) return false;

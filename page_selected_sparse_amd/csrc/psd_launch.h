@@ -101,6 +101,15 @@ hipError_t launch_decode_tiered(const Geo& g, const DecodePlan& plan, const void
                                 const int32_t* lens, const int32_t* sel, const int32_t* cnt,
                                 int b_max, float scale, float* out, void* ws, hipStream_t st);
 
+// ---- diagnostic memory walks (walk.hip) --------------------------------------------------
+// kind 0: the kept pages' K and V rows; kind 1: the candidate pages' statistics records.
+// latent: V is the leading part of each K row and is not walked again.
+bool walk_supported(const Geo& g, bool latent);
+hipError_t launch_walk(const Geo& g, int kind, bool latent, const void* k, const void* v,
+                       const void* meta, const int32_t* bt, const int32_t* lens,
+                       const int32_t* sel, const int32_t* cnt, int b_max, uint32_t* checksum,
+                       hipStream_t st);
+
 // ---- value tier (V in host memory, resident hot buffer) ----------------------------------
 struct TierLayout {
   // state: slot_of [num_blocks * H_kv] at 0, owner [slots], stamp [slots]

@@ -155,6 +155,17 @@ class DecodeStep:
                                 self.seq_lens, self.budgets, self.b_max, self.scale,
                                 self.sel_pages, self.sel_count, self.out, stream)
 
+    def walk(self, kind: int, stream=None):
+        """Diagnostic: the step's reads with no arithmetic (0: the kept pages' K and V rows
+        of the last selection; 1: every candidate page's statistics record); the XOR of
+        each unit's words lands in ``walk_checksum`` [B * H_kv]."""
+        if getattr(self, "walk_checksum", None) is None:
+            self.walk_checksum = torch.zeros(self.sel_count.numel(), dtype=torch.int32,
+                                             device=self.q.device)
+        api.diag_walk(self.shape, kind, self.k, self.v, self.meta, self.block_table,
+                      self.seq_lens, self.sel_pages, self.sel_count, self.b_max,
+                      self.walk_checksum, stream)
+
     # -- value tier: V in (pinned host) memory, a resident hot buffer in device memory ------
     def enable_tier(self, slots: int, kv: bool = False):
         """Keep up to ``slots`` (block, KV head) V slices resident in a device hot buffer;

@@ -257,6 +257,25 @@ def test_noalloc_step_rejects_oversize_before_touching_the_device(native):
                                        0.1, f, f, f, None) == -1
 
 
+def test_diag_walk_checks(native):
+    """The diagnostic walk refuses bad kinds, missing pointers and shapes it has no build
+    for on the host."""
+    lib = native.lib()
+    sh = _shape(native, batch=2, num_blocks=100)
+    f = ctypes.c_void_p(4096)
+    walk = lambda shape, kind, k, v, meta, sel, cnt, checksum: lib.psd_diag_walk(
+        ctypes.byref(shape), kind, k, v, meta, f, f, sel, cnt, 12, checksum, None)
+    assert walk(sh, 2, f, f, f, f, f, f) == -1
+    assert walk(sh, 0, f, f, f, f, f, None) == -1
+    assert walk(sh, 0, None, f, f, f, f, f) == -1
+    assert walk(sh, 0, f, f, f, None, f, f) == -1
+    assert walk(sh, 1, f, f, None, f, f, f) == -1
+    odd = _shape(native, head_dim=96, head_dim_v=96, k_block_stride=16 * 8 * 96,
+                 k_token_stride=8 * 96, k_head_stride=96, v_block_stride=16 * 8 * 96,
+                 v_token_stride=8 * 96, v_head_stride=96)
+    assert walk(odd, 0, f, f, f, f, f, f) in (-1, -2)
+
+
 def test_value_tier_queries_and_checks(native):
     """Value tier: state and workspace sizes follow the layout the calls document (page map
     of num_blocks x H_kv words, owner and last-step words per slot; per-entry miss and copy
