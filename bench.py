@@ -104,15 +104,17 @@ KERNEL_SOURCES = {"score_kernel": ("select.hip",), "merge_kernel": ("select.hip"
 def one_call_kernel(w):
     """The kernel behind decode_step and select_sparse_decode when each is a single launch,
     else None.
-    Follows the library's planning rule: at least 128 (sequence, KV head) units, at most
-    2048 candidate pages per unit, groups of up to 4 query heads, D = D_v <= 128 (bf16) or
-    D = D_v = 64 (fp32), and no certified pre-score."""
+    Follows the library's planning rule: at least 128 (sequence, KV head) units of at
+    most 2048 candidate pages, or block-table rows of at most 256 pages at any batch size;
+    groups of up to 4 query heads, D = D_v <= 128 (bf16) or D = D_v = 64 (fp32), and no
+    certified pre-score."""
     sp = w.spec
     G = sp.num_q_heads // sp.num_kv_heads
     units = sp.batch * sp.num_kv_heads
+    width = w.block_table.shape[1]
     d_ok = sp.head_dim <= 128 if sp.dtype == "bf16" else sp.head_dim == 64
-    if (G <= 4 and d_ok and sp.head_dim_v == sp.head_dim and units >= 128 and
-            w.block_table.shape[1] - 2 <= 2048):
+    if (G <= 4 and d_ok and sp.head_dim_v == sp.head_dim and
+            ((units >= 128 and width - 2 <= 2048) or width <= 256)):
         return "select_attn_kernel"
     return None
 

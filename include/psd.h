@@ -172,7 +172,8 @@ psd_status psd_select_pages(const psd_shape* shape, const void* q, const void* m
  * psd_select_score scores the pages. It writes sel_count and every sel_pages entry except
  * the ranked winners: the sink, the tail and the -1 padding, and the whole row of a unit
  * that keeps every page or exceeds b_max. When one workgroup scores a whole unit (batches
- * of at least 128 units of at most 2050 pages, groups of up to 8 heads) it also writes
+ * of at least 128 units of at most 2050 pages, or rows of at most 256 pages at any batch
+ * size; groups of up to 8 heads) it also writes
  * the winners, and psd_select_merge then launches nothing. Otherwise it leaves
  * candidates in the workspace: either each chunk's top pages by exact score or, for
  * groups of 16 or more bf16 heads, approximate scores with a proven error bound.
@@ -205,7 +206,8 @@ size_t psd_decode_workspace_bytes(const psd_shape* shape, int32_t max_pages_atte
  * out[s, h, :] = sum_t softmax_t(scale * q[s,h] . K_t) V_t[:D_v] over the valid tokens t
  * of the pages sel_pages[s, h / G, 0 .. sel_count - 1]. Accumulation is fp32; the page
  * splits of a unit are combined by log-sum-exp, inside the workgroup when one workgroup
- * holds a whole unit (batches of at least 128 units, groups of up to 16 heads, D <= 128),
+ * holds a whole unit (batches of at least 128 units, or rows of at most 256 pages at any
+ * batch size; groups of up to 16 heads, D <= 128),
  * else by a second launch over partials in the workspace. Units whose sel_count is
  * negative get NaN.
  *
@@ -242,12 +244,13 @@ size_t psd_select_sparse_decode_workspace_bytes(const psd_shape* shape, int32_t 
  * b_max, sel_pages, sel_count, ...) and then psd_sparse_decode(shape, q, k_cache, v_cache,
  * block_table, seq_lens, sel_pages, sel_count, b_max, scale, out, ...) write, bit for bit.
  * When one workgroup can both rank and attend a whole unit (batches of at least 128
- * units of at most 2050 pages, groups of up to 8 heads, D <= 128 in bf16 or D = 64 in
- * fp32) it is a single launch: each workgroup scores and ranks its unit's pages, keeps
- * the page list on chip and attends over it, so that no unit waits for the slowest
- * ranking of the batch before its attention starts. Otherwise the call enqueues the two
- * calls' launches in turn, sharing the workspace. sel_pages and sel_count are still
- * written in full.
+ * units of at most 2050 pages, or rows of at most 256 pages at any batch size; groups of
+ * up to 4 heads, D <= 128 in bf16 or D = 64 in fp32) it is a single launch: each
+ * workgroup scores and ranks its unit's pages, keeps the page list on chip and attends
+ * over it, so that no unit waits for the slowest ranking of the batch before its
+ * attention starts, and a short batch-1 step is one launch. Otherwise the call
+ * enqueues the two calls' launches in turn, sharing the workspace. sel_pages and
+ * sel_count are still written in full.
  *
  *   arguments   as for psd_select_pages and psd_sparse_decode
  *   workspace   >= psd_select_sparse_decode_workspace_bytes(shape, b_max) bytes (scratch)

@@ -738,7 +738,8 @@ bool plan_decode(const Geo& g, int max_pages_attended, bool dense, DecodePlan* p
   const int64_t units = (int64_t)g.B * g.Hkv;
   p->unit = 0;
   p->latent_tiles = 0;
-  if (g.G <= 16 && g.D <= 128 && units >= PSD_ATTN_UNIT_MIN && (!dense || PSD_ATTN_UNIT_DENSE)) {
+  if (g.G <= 16 && g.D <= 128 && (units >= PSD_ATTN_UNIT_MIN || small_units(g)) &&
+      (!dense || PSD_ATTN_UNIT_DENSE)) {
     // one workgroup per unit, its waves the splits, combined in LDS: no partials. fp32 at
     // D = 128 takes 8 waves: its 16-wave build spills at the 128-VGPR budget and was
     // measured to give wrong outputs for two of every four heads, while the 8-wave build

@@ -13,6 +13,14 @@ struct Geo {
   int64_t kbs, kts, khs, vbs, vts, vhs;
 };
 
+// A step over few pages per unit: one workgroup per unit scores and attends them in
+// about a launch time, so the whole-unit plans (and with them the one-launch step) pay
+// even when there are too few units to fill the GPU.
+#ifndef PSD_SMALL_PAGES
+#define PSD_SMALL_PAGES 256
+#endif
+inline bool small_units(const Geo& g) { return g.max_pages <= PSD_SMALL_PAGES; }
+
 // ---- page statistics ------------------------------------------------------------------
 hipError_t launch_meta_update(const Geo& g, const void* k, void* meta, const int32_t* bt,
                               const int32_t* lens, const int32_t* first_page, hipStream_t st);

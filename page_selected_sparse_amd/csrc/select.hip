@@ -1102,7 +1102,7 @@ bool plan_select(const Geo& g, int b_max, SelectPlan* p) {
     }
   };
   bool ok = false;
-  if (dpp && inner <= 2048 && units >= PSD_UNIT_MIN_UNITS) {
+  if (dpp && inner <= 2048 && (units >= PSD_UNIT_MIN_UNITS || small_units(g))) {
     // one workgroup per unit: scores every page and ranks them, no merge
     p->threads = p->head_block == 4 ? PSD_UNIT_THREADS : 512;
     p->ppt = (inner + p->threads - 1) / p->threads;

@@ -121,7 +121,12 @@ def test_one_call_step_checks(native):
     f = ctypes.c_void_p(16)
     ws = lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(sh), 10)
     assert ws >= lib.psd_select_workspace_bytes(ctypes.byref(sh), 10)
-    assert ws >= lib.psd_decode_workspace_bytes(ctypes.byref(sh), 10)
+    # past 256 pages per sequence the attention of a two-unit batch takes split partials
+    # (whose size both decode plans share at 10 pages): the workspace holds them too
+    mid = _shape(native, max_pages_per_seq=512, num_blocks=1100)
+    ws_mid = lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(mid), 10)
+    assert ws_mid >= lib.psd_select_workspace_bytes(ctypes.byref(mid), 10)
+    assert ws_mid >= lib.psd_decode_workspace_bytes(ctypes.byref(mid), 10)
     assert lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(sh), 1) == 0
     long = _shape(native, batch=1, max_pages_per_seq=65536, num_blocks=65536)
     assert lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(long), 60000) == 0
@@ -174,8 +179,9 @@ def test_plans_follow_the_batch_shape(native):
 
 
 def test_whole_unit_attention_needs_no_partials(native):
-    """With 256 units, whole-unit attention (bf16 and fp32, D = 64 and 128) keeps no split
-    partials, so the one-call workspace stays small; at 64 units split-K holds them."""
+    """With 256 units, or rows of at most 256 pages, whole-unit attention (bf16 and fp32,
+    D = 64 and 128) keeps no split partials, so the one-call workspace stays small; at 64
+    units of longer rows split-K holds them."""
     lib = native.lib()
     one_call = lambda sh: lib.psd_select_sparse_decode_workspace_bytes(ctypes.byref(sh), 102)
     d64 = dict(head_dim=64, head_dim_v=64, k_block_stride=16 * 8 * 64, k_token_stride=8 * 64,
@@ -188,6 +194,15 @@ def test_whole_unit_attention_needs_no_partials(native):
             assert 0 < one_call(sh) < 64 * 1024
         few = _shape(native, batch=8, max_pages_per_seq=2048, num_blocks=65536, dtype=dtype)
         assert one_call(few) >= 8 * 32 * 2 * 128 * 4  # B x H_q x (2+ splits) x D_v fp32
+        # rows of at most 256 pages take the whole-unit plans at any batch size; one
+        # page more and the small batch is back on chunks and split partials
+        for b in (1, 8):
+            short = _shape(native, batch=b, max_pages_per_seq=256, num_blocks=65536,
+                           dtype=dtype)
+            assert 0 < one_call(short) < 64 * 1024
+            longer = _shape(native, batch=b, max_pages_per_seq=257, num_blocks=65536,
+                            dtype=dtype)
+            assert one_call(longer) >= b * 32 * 2 * 128 * 4
 
 
 def test_bench_refuses_more_than_one_gpu():

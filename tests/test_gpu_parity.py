@@ -87,6 +87,27 @@ def test_small_parity(name):
     check_workload(w, res)
 
 
+def _table_pages(spec) -> int:
+    width = spec.max_len or (max(spec.seq_lens) if spec.seq_lens else spec.len_range[1])
+    return -(-width // 16)
+
+
+# Rows of at most 256 pages take one workgroup per unit at any batch size. The same
+# workloads with a block table 300 pages wide (same sequences) keep the plans of few
+# units over long rows: chunked scoring with a merge or in-launch refresh, split-K
+# attention and its log-sum-exp merge.
+CHUNKED = {n: dataclasses.replace(sp, max_len=16 * 300) for n, sp in SMALL.items()
+           if _table_pages(sp) <= 256 and sp.batch * sp.num_kv_heads < 128
+           and sp.group <= 16 and sp.head_dim <= 128}
+
+
+@pytest.mark.parametrize("name", list(CHUNKED))
+def test_small_parity_wide_table(name):
+    w = synth.make_workload(CHUNKED[name])
+    res = run_gpu(w)
+    check_workload(w, res)
+
+
 def test_full_budget_sparse_equals_dense_on_gpu():
     w = synth.make_workload(SMALL["full_budget"])
     res = run_gpu(w)
@@ -188,16 +209,19 @@ def test_measured_workloads(name):
 
 
 # Where the decode step refreshes the tail page's statistics, by the planning rules of
-# the library: inside the one-launch step (its last wave); as an extra workgroup per
-# unit of the exact scoring launch (at most one workgroup per CU); as an extra
+# the library: inside the one-launch step (its last wave; many units, or rows of at most
+# 256 pages); as an extra workgroup per unit of the exact scoring launch (at most one
+# workgroup per CU); as an extra
 # workgroup per unit of the chunk merge launch or of the certify launch; or as a launch
 # of its own (whole-unit scoring that is not the one-launch step, over more units than
 # CUs).
 REFRESH_SITES = {
     "fused_bf16": "wide_batch",
     "fused_f32_d64": "wide_f32_d64",
-    "in_score": "ragged_default",
-    "in_score_edge_lengths": "edge_lengths",
+    "fused_short_rows": "ragged_default",
+    "fused_short_rows_f32_d64": "tiny_cfg_seed1",
+    "in_score": dataclasses.replace(SMALL["ragged_default"], max_len=16 * 300),
+    "in_score_edge_lengths": dataclasses.replace(SMALL["edge_lengths"], max_len=16 * 300),
     "in_merge": synth.small_spec(batch=8, num_q_heads=32, num_kv_heads=8, seq_lens=(),
                                  len_range=(16 * 2500, 16 * 3000), budget_pages=50,
                                  max_len=16 * 3000),
