@@ -102,7 +102,11 @@ typedef struct psd_shape {
  * into chunks of CD dims; the minima and maxima of one chunk form one 128-byte line and
  * the lines of one (block, head) are one contiguous record of 2 * head_dim elements.
  * Total size: 2 * num_blocks * num_kv_heads * head_dim elements. Values are exact
- * (copied key values).
+ * (copied key values). Statistics held as two planes P[2][num_blocks][num_kv_heads]
+ * [head_dim] (P[0] the minima, P[1] the maxima) map to this layout element by element:
+ * meta[b][h][c][t][i] = P[t][b][h][c * CD + i], a permutation of the same elements.
+ * psd_page_meta_update builds the records from the cache, so a caller need not hold
+ * statistics of its own.
  */
 /*
  * psd_page_meta_update - recompute page statistics from the cached keys.
