@@ -205,7 +205,7 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
   __shared__ uint4 stage[kPreStages * STG];
   __shared__ int32_t blk_of[16 * 64];  // physical block of each page of the workgroup
   __shared__ float wmax[2][HT][16];
-  __shared__ uint32_t wabs[2][KS][16];
+  __shared__ uint32_t wabs[2][WAVES][16];
   __shared__ float4 psum[KS > 1 ? HT : 1][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
   float* second = a.second + (int64_t)unit * a.max_inner;
   int32_t* best = a.best + (int64_t)unit * a.max_inner;
   auto finish = [&](int t) {
-    if (tid < 16) {  // wave 0 (the record maxima come from the last head tile's waves)
+    if (tid < 16) {  // wave 0 (every wave contributed its share of the record maxima)
       const int i = 16 * (t0 + t) + tid;  // inner page index
       if (i < inner) {
         // the leading 16-head tile and the best of the other tiles
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
         best[i] = arg;
         uint32_t bits = wabs[t & 1][0][tid];
 #pragma unroll
-        for (int h = 1; h < KS; ++h) bits = max(bits, wabs[t & 1][h][tid]);
+        for (int w = 1; w < WAVES; ++w) bits = max(bits, wabs[t & 1][w][tid]);
         pmax[i] = bits > 0x7f80u ? __builtin_inff() : __uint_as_float(bits << 16);
       }
     }
@@ -359,7 +359,6 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
         sbase + (uint32_t)((t % NST) * STG + r * SLP + grp) * 16 + 64 * kb0;
     float sum[4] = {0.f, 0.f, 0.f, 0.f};
     float4v chain = {0.f, 0.f, 0.f, 0.f}, chain2 = {0.f, 0.f, 0.f, 0.f};
-    u16x2 amax = {0, 0};
     // the reads of step kb + 2 are in flight while step kb's MFMAs run
     u32x4p ra[2][2];
     lds2i_issue<0, 64>(row, ra[0][0], ra[0][1]);
@@ -389,26 +388,29 @@ __global__ __launch_bounds__(64 * HT * KS) void prescore_kernel(PreArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sum[i] += chain2[i];
       }
-      // every wave tracks it (no branch in the MFMA stream); the last head tile reports
-      // it (wave 0 already finishes the previous tile). The
-      // empty asm pins the running max each step, so that the max is not reassociated
-      // into a tree that would keep every fragment alive to the end.
-      const uint32_t ws[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        amax = __builtin_elementwise_max(amax, __builtin_bit_cast(u16x2, ws[i] & 0x7fff7fffu));
-      uint32_t pin = __builtin_bit_cast(uint32_t, amax);
-      asm volatile("" : "+v"(pin));
-      amax = __builtin_bit_cast(u16x2, pin);
       // keep each step's reads, MFMAs and adds together (short register live ranges)
       __builtin_amdgcn_sched_barrier(0);
     });
-    if (ht == HT - 1) {
-      // page r's record (this wave's k blocks) spans the four grp lanes of row r
+    {
+      // The largest |statistic| of each page's record, shared out: wave w takes the k
+      // blocks [w per, (w + 1) per) of the staged tile (lane (r, grp) holds 16 bytes of
+      // page r's block), after its MFMA stream, whose LDS reads have all completed.
+      constexpr int PER = (NKB + WAVES - 1) / WAVES;
+      const unsigned char* tb = reinterpret_cast<const unsigned char*>(stage) +
+                                ((t % NST) * STG + r * SLP + grp) * 16;
+      const int kb0w = __builtin_amdgcn_readfirstlane(wave) * PER;
+      u16x2 amax = {0, 0};
+      for (int kb = kb0w; kb < NKB && kb < kb0w + PER; ++kb) {
+        const uint4 x = *reinterpret_cast<const uint4*>(tb + 64 * kb);
+        const uint32_t ws[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          amax = __builtin_elementwise_max(amax, __builtin_bit_cast(u16x2, ws[i] & 0x7fff7fffu));
+      }
       uint32_t m = amax.x > amax.y ? amax.x : amax.y;
       m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
       m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
-      if (grp == 0) wabs[t & 1][kh][r] = m;
+      if (grp == 0) wabs[t & 1][wave][r] = m;
     }
     if constexpr (KS > 1) {
       if (kh == 1) psum[ht][lane] = make_float4(sum[0], sum[1], sum[2], sum[3]);
