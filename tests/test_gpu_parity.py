@@ -172,6 +172,32 @@ def test_tie_break_across_chunks():
     check_workload(w, res, dense_seqs=[])
 
 
+# Ties on the certified path (bf16 groups of 16+ heads): n_tied identical pages beat every
+# other page and `slots` of them fit the budget, so all of them are left undecided and
+# rescored exactly; the lowest pages win (more undecided pages than one wave ranks
+# directly, and fewer; the latent 576-dim record).
+@pytest.mark.parametrize("n_tied,slots,latent", [(20, 10, False), (80, 25, False),
+                                                 (24, 12, True)])
+def test_certified_ties(n_tied, slots, latent):
+    kw = dict(num_q_heads=128, num_kv_heads=1, head_dim=576, head_dim_v=512,
+              latent=True) if latent else dict(num_q_heads=16, num_kv_heads=1)
+    spec = synth.small_spec(batch=1, seq_lens=(16 * 3000,), budget_pages=slots + 2,
+                            needles=0, max_len=16 * 3000, **kw)
+    w = synth.make_workload(spec)
+    rng = np.random.default_rng(7 + n_tied)
+    pages = np.sort(rng.choice(np.arange(1, 2999), size=n_tied, replace=False))
+    q = synth.to_f64(w.q, "bf16")[0]
+    vec = np.where(q[0] >= 0, 4.0, -4.0).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(vec)
+    for p in pages:
+        w.cache[0, w.block_table[0, p], :, 0, :] = bits
+    print(f"[gpu] certified ties n_tied={n_tied} slots={slots} latent={latent}", flush=True)
+    res = run_gpu(w, dense=False)
+    expect = [0] + sorted(pages[:slots].tolist()) + [2999]
+    check_selection_row(res["sel"][0, 0], int(res["cnt"][0, 0]), expect, res["b_max"])
+    check_workload(w, res, dense_seqs=[])
+
+
 def test_all_pages_tie():
     spec = synth.small_spec(batch=1, seq_lens=(16 * 1200,), budget_pages=30, needles=0,
                             num_q_heads=8, num_kv_heads=2, max_len=16 * 1200)
