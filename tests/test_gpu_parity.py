@@ -198,16 +198,19 @@ def test_certified_ties(n_tied, slots, latent):
     check_workload(w, res, dense_seqs=[])
 
 
-def test_all_pages_tie():
-    spec = synth.small_spec(batch=1, seq_lens=(16 * 1200,), budget_pages=30, needles=0,
-                            num_q_heads=8, num_kv_heads=2, max_len=16 * 1200)
+# Every page identical: the lowest pages win, over 1,198 candidates and over 58 (one
+# workgroup per unit at both sizes).
+@pytest.mark.parametrize("pages,budget", [(1200, 30), (60, 10)])
+def test_all_pages_tie(pages, budget):
+    spec = synth.small_spec(batch=1, seq_lens=(16 * pages,), budget_pages=budget, needles=0,
+                            num_q_heads=8, num_kv_heads=2, max_len=16 * pages)
     w = synth.make_workload(spec)
     src = w.cache[0, w.block_table[0, 0]].copy()
     w.cache[0] = src[None]
     res = run_gpu(w, dense=False)
     for g in range(2):
         check_selection_row(res["sel"][0, g], int(res["cnt"][0, g]),
-                            list(range(29)) + [1199], res["b_max"])
+                            list(range(budget - 1)) + [pages - 1], res["b_max"])
     check_workload(w, res, dense_seqs=[])
 
 
