@@ -85,6 +85,106 @@ __device__ __forceinline__ void lds_read2(uint32_t a0, uint32_t a1, uint4& x0, u
   x1 = make_uint4(r1.x, r1.y, r1.z, r1.w);
 }
 
+// A page's K fragments (18) or V fragments (16) of the latent tile kernel: every read of
+// the group in one asm block with one wait, so that the reads overlap one another and the
+// compiler does not make them wait for the loads still streaming into the other slot.
+__device__ __forceinline__ void lds_read18(const uint32_t (&ad)[18], uint4 (&x)[18]) {
+  u32x4l r0, r1, r2, r3, r4, r5, r6, r7;
+  u32x4l r8, r9, r10, r11, r12, r13, r14, r15;
+  u32x4l r16, r17;
+  asm volatile(
+      "ds_read_b128 %0, %18\n\t"
+      "ds_read_b128 %1, %19\n\t"
+      "ds_read_b128 %2, %20\n\t"
+      "ds_read_b128 %3, %21\n\t"
+      "ds_read_b128 %4, %22\n\t"
+      "ds_read_b128 %5, %23\n\t"
+      "ds_read_b128 %6, %24\n\t"
+      "ds_read_b128 %7, %25\n\t"
+      "ds_read_b128 %8, %26\n\t"
+      "ds_read_b128 %9, %27\n\t"
+      "ds_read_b128 %10, %28\n\t"
+      "ds_read_b128 %11, %29\n\t"
+      "ds_read_b128 %12, %30\n\t"
+      "ds_read_b128 %13, %31\n\t"
+      "ds_read_b128 %14, %32\n\t"
+      "ds_read_b128 %15, %33\n\t"
+      "ds_read_b128 %16, %34\n\t"
+      "ds_read_b128 %17, %35\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+        "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13),
+        "=&v"(r14), "=&v"(r15), "=&v"(r16), "=&v"(r17)
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+        "v"(ad[7]), "v"(ad[8]), "v"(ad[9]), "v"(ad[10]), "v"(ad[11]), "v"(ad[12]),
+        "v"(ad[13]), "v"(ad[14]), "v"(ad[15]), "v"(ad[16]), "v"(ad[17])
+      : "memory");
+  x[0] = make_uint4(r0.x, r0.y, r0.z, r0.w);
+  x[1] = make_uint4(r1.x, r1.y, r1.z, r1.w);
+  x[2] = make_uint4(r2.x, r2.y, r2.z, r2.w);
+  x[3] = make_uint4(r3.x, r3.y, r3.z, r3.w);
+  x[4] = make_uint4(r4.x, r4.y, r4.z, r4.w);
+  x[5] = make_uint4(r5.x, r5.y, r5.z, r5.w);
+  x[6] = make_uint4(r6.x, r6.y, r6.z, r6.w);
+  x[7] = make_uint4(r7.x, r7.y, r7.z, r7.w);
+  x[8] = make_uint4(r8.x, r8.y, r8.z, r8.w);
+  x[9] = make_uint4(r9.x, r9.y, r9.z, r9.w);
+  x[10] = make_uint4(r10.x, r10.y, r10.z, r10.w);
+  x[11] = make_uint4(r11.x, r11.y, r11.z, r11.w);
+  x[12] = make_uint4(r12.x, r12.y, r12.z, r12.w);
+  x[13] = make_uint4(r13.x, r13.y, r13.z, r13.w);
+  x[14] = make_uint4(r14.x, r14.y, r14.z, r14.w);
+  x[15] = make_uint4(r15.x, r15.y, r15.z, r15.w);
+  x[16] = make_uint4(r16.x, r16.y, r16.z, r16.w);
+  x[17] = make_uint4(r17.x, r17.y, r17.z, r17.w);
+}
+
+__device__ __forceinline__ void lds_read16(const uint32_t (&ad)[16], uint4 (&x)[16]) {
+  u32x4l r0, r1, r2, r3, r4, r5, r6, r7;
+  u32x4l r8, r9, r10, r11, r12, r13, r14, r15;
+  asm volatile(
+      "ds_read_b128 %0, %16\n\t"
+      "ds_read_b128 %1, %17\n\t"
+      "ds_read_b128 %2, %18\n\t"
+      "ds_read_b128 %3, %19\n\t"
+      "ds_read_b128 %4, %20\n\t"
+      "ds_read_b128 %5, %21\n\t"
+      "ds_read_b128 %6, %22\n\t"
+      "ds_read_b128 %7, %23\n\t"
+      "ds_read_b128 %8, %24\n\t"
+      "ds_read_b128 %9, %25\n\t"
+      "ds_read_b128 %10, %26\n\t"
+      "ds_read_b128 %11, %27\n\t"
+      "ds_read_b128 %12, %28\n\t"
+      "ds_read_b128 %13, %29\n\t"
+      "ds_read_b128 %14, %30\n\t"
+      "ds_read_b128 %15, %31\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+        "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13),
+        "=&v"(r14), "=&v"(r15)
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+        "v"(ad[7]), "v"(ad[8]), "v"(ad[9]), "v"(ad[10]), "v"(ad[11]), "v"(ad[12]),
+        "v"(ad[13]), "v"(ad[14]), "v"(ad[15])
+      : "memory");
+  x[0] = make_uint4(r0.x, r0.y, r0.z, r0.w);
+  x[1] = make_uint4(r1.x, r1.y, r1.z, r1.w);
+  x[2] = make_uint4(r2.x, r2.y, r2.z, r2.w);
+  x[3] = make_uint4(r3.x, r3.y, r3.z, r3.w);
+  x[4] = make_uint4(r4.x, r4.y, r4.z, r4.w);
+  x[5] = make_uint4(r5.x, r5.y, r5.z, r5.w);
+  x[6] = make_uint4(r6.x, r6.y, r6.z, r6.w);
+  x[7] = make_uint4(r7.x, r7.y, r7.z, r7.w);
+  x[8] = make_uint4(r8.x, r8.y, r8.z, r8.w);
+  x[9] = make_uint4(r9.x, r9.y, r9.z, r9.w);
+  x[10] = make_uint4(r10.x, r10.y, r10.z, r10.w);
+  x[11] = make_uint4(r11.x, r11.y, r11.z, r11.w);
+  x[12] = make_uint4(r12.x, r12.y, r12.z, r12.w);
+  x[13] = make_uint4(r13.x, r13.y, r13.z, r13.w);
+  x[14] = make_uint4(r14.x, r14.y, r14.z, r14.w);
+  x[15] = make_uint4(r15.x, r15.y, r15.z, r15.w);
+}
+
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void attn_latent_kernel(AttnArgs a) {
   constexpr int DQK = 576, DV = 512, NQ = DQK / 32, NC = DV / 16;  // 18 and 32
@@ -263,8 +363,9 @@ __global__ __launch_bounds__(64 * WAVES) void attn_latent_kernel(AttnArgs a) {
 // Each wave streams its own pages through a private two-slot LDS ring with direct-to-LDS
 // loads (page i + 1 in flight while page i is computed; no registers held by loads in
 // flight), in the padded row layout of the staged kernel above, and reads its K and V
-// fragments from there: S^T = K Q^T (18 MFMAs 16x16x32 bf16, q of its 16 heads in
-// registers) and O += P V (32 MFMAs; V rows 4grp + j at piece 16w + r serve tiles 8w + cc).
+// fragments from there, each set in one read group with one wait: S^T = K Q^T (18 MFMAs
+// 16x16x32 bf16, q of its 16 heads in registers) and O += P V (32 MFMAs; V rows 4grp + j
+// at piece 16w + r serve tiles 8w + cc).
 // Two fp32 values rounded to bf16 (nearest even) and packed, the first in bits 15:0.
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   typedef __attribute__((ext_vector_type(2))) float f32x2;
@@ -388,21 +489,20 @@ void attn_latent_tile_kernel(AttnArgs a) {
     wait_vm_n<kLatLoads>();  // page i has landed: only page i + 1's loads are in flight
     const uint32_t st = rbase + (uint32_t)((i & 1) * kLatStage * 16);
     const int valid = min(kPage, L - __builtin_amdgcn_readlane(my_lp, i) * kPage);
-    // three independent accumulation chains over the 18 steps, summed at the end
+    // all 18 K fragments in one read group, then three independent accumulation chains
+    // over the 18 steps, summed at the end
     float4v s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0;
     const uint32_t krow = st + (uint32_t)(r * kLatRowPieces + grp) * 16;
+    uint32_t kad[NQ];
+    uint4 k[NQ];
 #pragma unroll
-    for (int c0 = 0; c0 < NQ; c0 += 6) {
-      uint4 k[6];
-      lds_read2(krow + 64 * c0, krow + 64 * (c0 + 1), k[0], k[1]);
-      lds_read4(krow + 64 * (c0 + 2), krow + 64 * (c0 + 3), krow + 64 * (c0 + 4),
-                krow + 64 * (c0 + 5), k[2], k[3], k[4], k[5]);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[0]), as_bf16x8(qf[c0]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[1]), as_bf16x8(qf[c0 + 1]), s1, 0, 0, 0);
-      s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[2]), as_bf16x8(qf[c0 + 2]), s2, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[3]), as_bf16x8(qf[c0 + 3]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[4]), as_bf16x8(qf[c0 + 4]), s1, 0, 0, 0);
-      s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[5]), as_bf16x8(qf[c0 + 5]), s2, 0, 0, 0);
+    for (int c = 0; c < NQ; ++c) kad[c] = krow + 64 * c;
+    lds_read18(kad, k);
+#pragma unroll
+    for (int c = 0; c < NQ; c += 3) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[c]), as_bf16x8(qf[c]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[c + 1]), as_bf16x8(qf[c + 1]), s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[c + 2]), as_bf16x8(qf[c + 2]), s2, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -423,13 +523,18 @@ void attn_latent_tile_kernel(AttnArgs a) {
     const uint32_t l01 = pk_bf16(p[0] - bf_lo(h01), p[1] - bf_hi(h01));
     const uint32_t l23 = pk_bf16(p[2] - bf_lo(h23), p[3] - bf_hi(h23));
     const bf16x8 PP = as_bf16x8(make_uint4(h01, h23, l01, l23));
+    // all 16 V fragments of the page in one read group: V rows 4grp + j, piece 16w + r
     const uint32_t vrow = st + (uint32_t)((4 * grp) * kLatRowPieces + r) * 16;
+    uint32_t vad[16];
+    uint4 vx[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vad[4 * w + j] = vrow + 16 * (j * kLatRowPieces + 16 * w);
+    lds_read16(vad, vx);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint4 x[4];
-      lds_read4(vrow + 16 * (0 * kLatRowPieces + 16 * w), vrow + 16 * (1 * kLatRowPieces + 16 * w),
-                vrow + 16 * (2 * kLatRowPieces + 16 * w), vrow + 16 * (3 * kLatRowPieces + 16 * w),
-                x[0], x[1], x[2], x[3]);
+      uint4 x[4] = {vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3]};
       uint32_t vh[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
