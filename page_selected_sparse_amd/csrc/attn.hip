@@ -536,9 +536,13 @@ void attn_latent_tile_kernel(AttnArgs a) {
     for (int w = 0; w < 4; ++w) {
       uint4 x[4] = {vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3]};
       uint32_t vh[4][4];
+      if (valid < kPage) {  // uniform: only a sequence's last page has unwritten slots
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * grp + j >= valid) x[j] = make_uint4(0u, 0u, 0u, 0u);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (4 * grp + j >= valid) x[j] = make_uint4(0u, 0u, 0u, 0u);  // unwritten slots
         vh[j][0] = x[j].x; vh[j][1] = x[j].y; vh[j][2] = x[j].z; vh[j][3] = x[j].w;
       }
 #pragma unroll
