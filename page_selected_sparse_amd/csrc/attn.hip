@@ -85,9 +85,9 @@ __device__ __forceinline__ void lds_read2(uint32_t a0, uint32_t a1, uint4& x0, u
   x1 = make_uint4(r1.x, r1.y, r1.z, r1.w);
 }
 
-// A page's K fragments (18) or V fragments (16) of the latent tile kernel: every read of
-// the group in one asm block with one wait, so that the reads overlap one another and the
-// compiler does not make them wait for the loads still streaming into the other slot.
+// A page's 18 K fragments of the latent tile kernel: every read in one asm block with one
+// wait, so that the reads overlap one another and the compiler does not make them wait for
+// the loads still streaming into the other slot.
 __device__ __forceinline__ void lds_read18(const uint32_t (&ad)[18], uint4 (&x)[18]) {
   u32x4l r0, r1, r2, r3, r4, r5, r6, r7;
   u32x4l r8, r9, r10, r11, r12, r13, r14, r15;
@@ -139,50 +139,85 @@ __device__ __forceinline__ void lds_read18(const uint32_t (&ad)[18], uint4 (&x)[
   x[17] = make_uint4(r17.x, r17.y, r17.z, r17.w);
 }
 
-__device__ __forceinline__ void lds_read16(const uint32_t (&ad)[16], uint4 (&x)[16]) {
-  u32x4l r0, r1, r2, r3, r4, r5, r6, r7;
-  u32x4l r8, r9, r10, r11, r12, r13, r14, r15;
+// A page's 32 V operands of the latent tile kernel, through gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): in each 16-lane group, lane i receives element i % 4 of the
+// 8-byte reads of lanes 4j + i / 4, j = 0 .. 3. Read k is at byte 32 k from `base`; one
+// asm block with one wait, as above.
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2l;
+__device__ __forceinline__ void lds_read_tr32(uint32_t base, uint2 (&x)[32]) {
+  u32x2l r0, r1, r2, r3, r4, r5, r6, r7;
+  u32x2l r8, r9, r10, r11, r12, r13, r14, r15;
+  u32x2l r16, r17, r18, r19, r20, r21, r22, r23;
+  u32x2l r24, r25, r26, r27, r28, r29, r30, r31;
   asm volatile(
-      "ds_read_b128 %0, %16\n\t"
-      "ds_read_b128 %1, %17\n\t"
-      "ds_read_b128 %2, %18\n\t"
-      "ds_read_b128 %3, %19\n\t"
-      "ds_read_b128 %4, %20\n\t"
-      "ds_read_b128 %5, %21\n\t"
-      "ds_read_b128 %6, %22\n\t"
-      "ds_read_b128 %7, %23\n\t"
-      "ds_read_b128 %8, %24\n\t"
-      "ds_read_b128 %9, %25\n\t"
-      "ds_read_b128 %10, %26\n\t"
-      "ds_read_b128 %11, %27\n\t"
-      "ds_read_b128 %12, %28\n\t"
-      "ds_read_b128 %13, %29\n\t"
-      "ds_read_b128 %14, %30\n\t"
-      "ds_read_b128 %15, %31\n\t"
+      "ds_read_b64_tr_b16 %0, %32 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %32 offset:32\n\t"
+      "ds_read_b64_tr_b16 %2, %32 offset:64\n\t"
+      "ds_read_b64_tr_b16 %3, %32 offset:96\n\t"
+      "ds_read_b64_tr_b16 %4, %32 offset:128\n\t"
+      "ds_read_b64_tr_b16 %5, %32 offset:160\n\t"
+      "ds_read_b64_tr_b16 %6, %32 offset:192\n\t"
+      "ds_read_b64_tr_b16 %7, %32 offset:224\n\t"
+      "ds_read_b64_tr_b16 %8, %32 offset:256\n\t"
+      "ds_read_b64_tr_b16 %9, %32 offset:288\n\t"
+      "ds_read_b64_tr_b16 %10, %32 offset:320\n\t"
+      "ds_read_b64_tr_b16 %11, %32 offset:352\n\t"
+      "ds_read_b64_tr_b16 %12, %32 offset:384\n\t"
+      "ds_read_b64_tr_b16 %13, %32 offset:416\n\t"
+      "ds_read_b64_tr_b16 %14, %32 offset:448\n\t"
+      "ds_read_b64_tr_b16 %15, %32 offset:480\n\t"
+      "ds_read_b64_tr_b16 %16, %32 offset:512\n\t"
+      "ds_read_b64_tr_b16 %17, %32 offset:544\n\t"
+      "ds_read_b64_tr_b16 %18, %32 offset:576\n\t"
+      "ds_read_b64_tr_b16 %19, %32 offset:608\n\t"
+      "ds_read_b64_tr_b16 %20, %32 offset:640\n\t"
+      "ds_read_b64_tr_b16 %21, %32 offset:672\n\t"
+      "ds_read_b64_tr_b16 %22, %32 offset:704\n\t"
+      "ds_read_b64_tr_b16 %23, %32 offset:736\n\t"
+      "ds_read_b64_tr_b16 %24, %32 offset:768\n\t"
+      "ds_read_b64_tr_b16 %25, %32 offset:800\n\t"
+      "ds_read_b64_tr_b16 %26, %32 offset:832\n\t"
+      "ds_read_b64_tr_b16 %27, %32 offset:864\n\t"
+      "ds_read_b64_tr_b16 %28, %32 offset:896\n\t"
+      "ds_read_b64_tr_b16 %29, %32 offset:928\n\t"
+      "ds_read_b64_tr_b16 %30, %32 offset:960\n\t"
+      "ds_read_b64_tr_b16 %31, %32 offset:992\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
-        "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13),
-        "=&v"(r14), "=&v"(r15)
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
-        "v"(ad[7]), "v"(ad[8]), "v"(ad[9]), "v"(ad[10]), "v"(ad[11]), "v"(ad[12]),
-        "v"(ad[13]), "v"(ad[14]), "v"(ad[15])
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13), "=&v"(r14), "=&v"(r15), "=&v"(r16), "=&v"(r17), "=&v"(r18), "=&v"(r19), "=&v"(r20), "=&v"(r21), "=&v"(r22), "=&v"(r23), "=&v"(r24), "=&v"(r25), "=&v"(r26), "=&v"(r27), "=&v"(r28), "=&v"(r29), "=&v"(r30), "=&v"(r31)
+      : "v"(base)
       : "memory");
-  x[0] = make_uint4(r0.x, r0.y, r0.z, r0.w);
-  x[1] = make_uint4(r1.x, r1.y, r1.z, r1.w);
-  x[2] = make_uint4(r2.x, r2.y, r2.z, r2.w);
-  x[3] = make_uint4(r3.x, r3.y, r3.z, r3.w);
-  x[4] = make_uint4(r4.x, r4.y, r4.z, r4.w);
-  x[5] = make_uint4(r5.x, r5.y, r5.z, r5.w);
-  x[6] = make_uint4(r6.x, r6.y, r6.z, r6.w);
-  x[7] = make_uint4(r7.x, r7.y, r7.z, r7.w);
-  x[8] = make_uint4(r8.x, r8.y, r8.z, r8.w);
-  x[9] = make_uint4(r9.x, r9.y, r9.z, r9.w);
-  x[10] = make_uint4(r10.x, r10.y, r10.z, r10.w);
-  x[11] = make_uint4(r11.x, r11.y, r11.z, r11.w);
-  x[12] = make_uint4(r12.x, r12.y, r12.z, r12.w);
-  x[13] = make_uint4(r13.x, r13.y, r13.z, r13.w);
-  x[14] = make_uint4(r14.x, r14.y, r14.z, r14.w);
-  x[15] = make_uint4(r15.x, r15.y, r15.z, r15.w);
+  x[0] = make_uint2(r0.x, r0.y);
+  x[1] = make_uint2(r1.x, r1.y);
+  x[2] = make_uint2(r2.x, r2.y);
+  x[3] = make_uint2(r3.x, r3.y);
+  x[4] = make_uint2(r4.x, r4.y);
+  x[5] = make_uint2(r5.x, r5.y);
+  x[6] = make_uint2(r6.x, r6.y);
+  x[7] = make_uint2(r7.x, r7.y);
+  x[8] = make_uint2(r8.x, r8.y);
+  x[9] = make_uint2(r9.x, r9.y);
+  x[10] = make_uint2(r10.x, r10.y);
+  x[11] = make_uint2(r11.x, r11.y);
+  x[12] = make_uint2(r12.x, r12.y);
+  x[13] = make_uint2(r13.x, r13.y);
+  x[14] = make_uint2(r14.x, r14.y);
+  x[15] = make_uint2(r15.x, r15.y);
+  x[16] = make_uint2(r16.x, r16.y);
+  x[17] = make_uint2(r17.x, r17.y);
+  x[18] = make_uint2(r18.x, r18.y);
+  x[19] = make_uint2(r19.x, r19.y);
+  x[20] = make_uint2(r20.x, r20.y);
+  x[21] = make_uint2(r21.x, r21.y);
+  x[22] = make_uint2(r22.x, r22.y);
+  x[23] = make_uint2(r23.x, r23.y);
+  x[24] = make_uint2(r24.x, r24.y);
+  x[25] = make_uint2(r25.x, r25.y);
+  x[26] = make_uint2(r26.x, r26.y);
+  x[27] = make_uint2(r27.x, r27.y);
+  x[28] = make_uint2(r28.x, r28.y);
+  x[29] = make_uint2(r29.x, r29.y);
+  x[30] = make_uint2(r30.x, r30.y);
+  x[31] = make_uint2(r31.x, r31.y);
 }
 
 template <int WAVES>
@@ -364,8 +399,9 @@ __global__ __launch_bounds__(64 * WAVES) void attn_latent_kernel(AttnArgs a) {
 // loads (page i + 1 in flight while page i is computed; no registers held by loads in
 // flight), in the padded row layout of the staged kernel above, and reads its K and V
 // fragments from there, each set in one read group with one wait: S^T = K Q^T (18 MFMAs
-// 16x16x32 bf16, q of its 16 heads in registers) and O += P V (32 MFMAs; V rows 4grp + j
-// at piece 16w + r serve tiles 8w + cc).
+// 16x16x32 bf16, q of its 16 heads in registers) and O += P V (32 MFMAs; tile c's V
+// operand comes from a transposing read: lane (r, grp) gets tokens 4grp .. 4grp+3 of
+// column 16c + r).
 // Two fp32 values rounded to bf16 (nearest even) and packed, the first in bits 15:0.
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   typedef __attribute__((ext_vector_type(2))) float f32x2;
@@ -523,39 +559,25 @@ void attn_latent_tile_kernel(AttnArgs a) {
     const uint32_t l01 = pk_bf16(p[0] - bf_lo(h01), p[1] - bf_hi(h01));
     const uint32_t l23 = pk_bf16(p[2] - bf_lo(h23), p[3] - bf_hi(h23));
     const bf16x8 PP = as_bf16x8(make_uint4(h01, h23, l01, l23));
-    // all 16 V fragments of the page in one read group: V rows 4grp + j, piece 16w + r
-    const uint32_t vrow = st + (uint32_t)((4 * grp) * kLatRowPieces + r) * 16;
-    uint32_t vad[16];
-    uint4 vx[16];
+    // V as the B operand straight from LDS: the transposing read of tile c gives lane
+    // (r, grp) the tokens 4grp .. 4grp+3 of column 16c + r (lanes s of a 16-lane group
+    // read row 4grp + s/4 at columns 16c + 4(s % 4))
+    const uint32_t vtr = st + (uint32_t)((4 * grp + (r >> 2)) * kLatRowPieces) * 16 + 8 * (r & 3);
+    uint2 vt[NC];
+    lds_read_tr32(vtr, vt);
+    if (valid < kPage) {  // uniform: only a sequence's last page has unwritten slots
+      const uint32_t m01 = (4 * grp + 0 < valid ? 0xffffu : 0u) | (4 * grp + 1 < valid ? 0xffff0000u : 0u);
+      const uint32_t m23 = (4 * grp + 2 < valid ? 0xffffu : 0u) | (4 * grp + 3 < valid ? 0xffff0000u : 0u);
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vad[4 * w + j] = vrow + 16 * (j * kLatRowPieces + 16 * w);
-    lds_read16(vad, vx);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint4 x[4] = {vx[4 * w], vx[4 * w + 1], vx[4 * w + 2], vx[4 * w + 3]};
-      uint32_t vh[4][4];
-      if (valid < kPage) {  // uniform: only a sequence's last page has unwritten slots
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (4 * grp + j >= valid) x[j] = make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vh[j][0] = x[j].x; vh[j][1] = x[j].y; vh[j][2] = x[j].z; vh[j][3] = x[j].w;
-      }
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        // column cc of the four rows: half cc & 1 of word cc / 2, packed by byte permutes
-        const int wd = cc >> 1;
-        const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t v01 = __builtin_amdgcn_perm(vh[1][wd], vh[0][wd], sel);
-        const uint32_t v23 = __builtin_amdgcn_perm(vh[3][wd], vh[2][wd], sel);
-        acc[8 * w + cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            PP, as_bf16x8(make_uint4(v01, v23, v01, v23)), acc[8 * w + cc], 0, 0, 0);
+      for (int c = 0; c < NC; ++c) {
+        vt[c].x &= m01;
+        vt[c].y &= m23;
       }
     }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          PP, as_bf16x8(make_uint4(vt[c].x, vt[c].y, vt[c].x, vt[c].y)), acc[c], 0, 0, 0);
   };
 
   // Online softmax with a lazily moved reference: a head's weights are taken relative to
@@ -601,7 +623,7 @@ void attn_latent_tile_kernel(AttnArgs a) {
   }
 
   // ---- the SUB waves' states -> one partial of 16 heads for this split -----------------
-  // acc rows are heads 4grp + j; tile 8w + cc column r is d = 128w + 8r + cc. The combine
+  // acc rows are heads 4grp + j; tile c column r is d = 16c + r. The combine
   // area overlaps the rings: the trailing repeat of the last page must land, and every
   // wave must be past its pages, first.
   wait_vm_upto20(0);
@@ -610,14 +632,9 @@ void attn_latent_tile_kernel(AttnArgs a) {
   float2* tml = reinterpret_cast<float2*>(tsh + SUB * 16 * DV);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float* dst = tsh + (wave * 16 + 4 * grp + j) * DV + 8 * r;
+    float* dst = tsh + (wave * 16 + 4 * grp + j) * DV + r;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      *reinterpret_cast<float4*>(dst + 128 * w) =
-          make_float4(acc[8 * w][j], acc[8 * w + 1][j], acc[8 * w + 2][j], acc[8 * w + 3][j]);
-      *reinterpret_cast<float4*>(dst + 128 * w + 4) =
-          make_float4(acc[8 * w + 4][j], acc[8 * w + 5][j], acc[8 * w + 6][j], acc[8 * w + 7][j]);
-    }
+    for (int c = 0; c < NC; ++c) dst[16 * c] = acc[c][j];
   }
   if (grp == 0) tml[wave * 16 + r] = make_float2(m_run, l_run);
   __syncthreads();
