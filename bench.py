@@ -11,7 +11,8 @@ K measured ones, so that the measured region runs at steady clocks (a 20-step re
 right after the GPU wakes runs about 8 % slower).
 
 Prints one JSON line. Besides the contract fields it carries:
-  roofline      achieved algorithmic GB/s of the dominant kernel against 8 TB/s
+  roofline      achieved algorithmic GB/s of the dominant kernel against 8 TB/s; a
+                one-launch step is timed over launches 2..K of the measured region
   cpu_baseline  the fp64 oracle's step on the host: all usable cores (the value), one
                 thread, and the oracle's dense step
   calls         per-call average durations (HIP events on the launch stream)
