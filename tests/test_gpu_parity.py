@@ -48,6 +48,11 @@ SMALL = {
     "latent576": synth.small_spec(batch=2, num_q_heads=128, num_kv_heads=1, head_dim=576,
                                   head_dim_v=512, latent=True, seq_lens=(1500, 333),
                                   max_len=1504),
+    # the latent kernels' tail masking at every count of written rows in the last page
+    "latent_tails": synth.small_spec(batch=16, num_q_heads=128, num_kv_heads=1, head_dim=576,
+                                     head_dim_v=512, latent=True,
+                                     seq_lens=tuple(16 * 40 + v for v in range(1, 17)),
+                                     max_len=16 * 41),
     "many_chunks": synth.small_spec(batch=2, seq_lens=(16 * 3000 - 5, 16 * 700), budget_pages=40,
                                     max_len=16 * 3000),
     "tiny_cfg_seed1": dataclasses.replace(synth.SPECS["tiny"], seed=1),
