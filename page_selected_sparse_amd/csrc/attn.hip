@@ -183,7 +183,11 @@ __device__ __forceinline__ void lds_read_tr32(uint32_t base, uint2 (&x)[32]) {
       "ds_read_b64_tr_b16 %30, %32 offset:960\n\t"
       "ds_read_b64_tr_b16 %31, %32 offset:992\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13), "=&v"(r14), "=&v"(r15), "=&v"(r16), "=&v"(r17), "=&v"(r18), "=&v"(r19), "=&v"(r20), "=&v"(r21), "=&v"(r22), "=&v"(r23), "=&v"(r24), "=&v"(r25), "=&v"(r26), "=&v"(r27), "=&v"(r28), "=&v"(r29), "=&v"(r30), "=&v"(r31)
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+        "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13),
+        "=&v"(r14), "=&v"(r15), "=&v"(r16), "=&v"(r17), "=&v"(r18), "=&v"(r19), "=&v"(r20),
+        "=&v"(r21), "=&v"(r22), "=&v"(r23), "=&v"(r24), "=&v"(r25), "=&v"(r26), "=&v"(r27),
+        "=&v"(r28), "=&v"(r29), "=&v"(r30), "=&v"(r31)
       : "v"(base)
       : "memory");
   x[0] = make_uint2(r0.x, r0.y);
